@@ -1,0 +1,172 @@
+/*
+ * gmm.h -- C ABI of the MI355X (gfx950) grouped matrix multiplication library
+ * (libgmm.so).
+ *
+ * The operation is the Megablox grouped matmul (tpu-inference 0.13.2 wheel
+ * diff page, megablox/gmm.py, gmm()): a row-sorted lhs [M,K] is cut into
+ * contiguous row groups by an int32 group_sizes[G]; the rows of group g are
+ * [o[g], o[g+1]) with o[0] = 0 and o[g+1] = o[g] + group_sizes[g]
+ * (make_group_metadata, group offsets).  Groups s .. s+Ga-1 are active, where
+ * s is the group offset and Ga = rhs.shape[0]; each active row r of group g is
+ *
+ *   out[r,n] = sum_b rhs_scale[g-s,b,0,n] * lhs_scale[r,b] *
+ *                    sum_{k in block b} lhs[r,k] * W(g-s,n,k)
+ *              + rhs_bias[g-s,0,n]
+ *
+ * accumulated in fp32 and rounded once, to nearest even, to the output type
+ * (gmm() kernel body: the accumulator is reset per quantisation block and
+ * scaled by that block's rhs_scale; the bias is added once).  An absent scale
+ * is 1, an absent bias 0, and with neither scale the whole of K is one block.
+ * W(h,n,k) = rhs[h,n,k] when transpose_rhs == 0 (rhs [Ga,N,K], an NT product)
+ * and rhs[h,k,n] when transpose_rhs == 1 (rhs [Ga,K,N], an NN product that
+ * reads the forward weight in place -- MaxText PR "Megablox: transposed-RHS
+ * gmm_v2 kernel for the backward dlhs", Context).  lhs_scale is the
+ * per-token activation scale of the block-scaled W8A8 GEMM (metrale
+ * gemm_quant.rs page, fp8_gemm_t_blockscaled).  Every output row outside
+ * [o[s], o[s+Ga]) is written as +0.0 (gmm(), _zero_uninitialized_memory).
+ *
+ * Conventions
+ *  - Every tensor is a dense, row-major view of device memory that the caller
+ *    owns and keeps alive until the work queued on `stream` has finished.
+ *    Pointers must be 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  gmm_run only
+ *    queues work: it never synchronises and never copies group_sizes or the
+ *    group offset to the host.
+ *  - A handle is used by one host thread at a time.
+ *  - No exception crosses this boundary.  Every call returns a gmm_status;
+ *    gmm_last_error() gives the text of the last failure on a handle.
+ */
+#ifndef GMM_MI355X_GMM_H
+#define GMM_MI355X_GMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GMM_F32 = 0,       /* IEEE binary32 */
+  GMM_BF16 = 1,      /* bfloat16 */
+  GMM_F8E4M3FN = 2,  /* OCP e4m3fn: bias 7, max 448, no infinities */
+  GMM_I32 = 3        /* int32 (group_sizes only) */
+} gmm_dtype;
+
+typedef enum {
+  GMM_OK = 0,
+  GMM_E_INVALID = -1,     /* inconsistent shapes, ranks, dtypes or pointers */
+  GMM_E_UNSUPPORTED = -2, /* a valid problem this library does not run */
+  GMM_E_HIP = -3,         /* a HIP runtime call or kernel launch failed */
+  GMM_E_DEVICE_DATA = -4  /* device-resident data was invalid (gmm_device_flags) */
+} gmm_status;
+
+/* A dense row-major device tensor view (caller-owned). */
+typedef struct {
+  const void* data;
+  int32_t dtype;     /* gmm_dtype */
+  int32_t ndim;      /* 1..4 */
+  int64_t shape[4];
+} gmm_tensor;
+
+typedef struct gmm_handle gmm_handle;
+
+/* Bits reported by gmm_device_flags.  The kernels clamp the offending value
+ * so every access stays in bounds, compute with the clamped value and set the
+ * bit. */
+#define GMM_FLAG_NEGATIVE_SIZE 0x1u  /* some group_sizes[g] < 0 (taken as 0) */
+#define GMM_FLAG_SIZES_EXCEED_M 0x2u /* o[G] > M (offsets clamped to M) */
+#define GMM_FLAG_BAD_OFFSET 0x4u     /* group offset < 0 or s + Ga > G (clamped) */
+
+/*
+ * gmm_create: make a handle on HIP device `device` (must be gfx950).
+ * Allocates one 4-byte device word for the data-error flags.
+ * Returns GMM_E_UNSUPPORTED on another architecture, GMM_E_HIP on a HIP
+ * failure, GMM_E_INVALID when h is NULL.
+ */
+gmm_status gmm_create(gmm_handle** h, int device);
+
+/* gmm_destroy: free the handle and its flag word.  NULL is allowed. */
+gmm_status gmm_destroy(gmm_handle* h);
+
+/* gmm_last_error: text of the last failure on h ("" when none; never NULL). */
+const char* gmm_last_error(const gmm_handle* h);
+
+/*
+ * gmm_run: queue out = gmm(lhs, rhs, group_sizes, ...) on `stream`.
+ *
+ *   lhs          [M,K]; F32, BF16 or F8E4M3FN.
+ *   rhs          [Ga,N,K] (transpose_rhs == 0) or [Ga,K,N] (== 1).
+ *                Supported (lhs, rhs) pairs: (F32,F32), (BF16,BF16),
+ *                (BF16,F8E4M3FN: the weight is widened exactly to bf16),
+ *                (F8E4M3FN,F8E4M3FN: fp8 x fp8 products).  F8E4M3FN weights
+ *                need transpose_rhs == 0.
+ *   group_sizes  [G] I32 on the device, 1 <= G <= 1024.
+ *   rhs_scale    NULL or F32 [Ga,nb,1,N]; K % nb == 0.
+ *   rhs_bias     NULL or [Ga,1,N], F32 or BF16.
+ *   lhs_scale    NULL or F32 [M,nb] (its nb must equal rhs_scale's when both
+ *                are given).
+ *   group_offset NULL (s = 0) or a device pointer to one int32 s.
+ *   out          [M,N], F32 or BF16.  All M rows are written.  out must not
+ *                overlap any input.
+ *
+ * Size limits: M < 2^31; N % 8 == 0; K % 64 == 0 for BF16 products,
+ * K % 128 == 0 for fp8 x fp8, K % 32 == 0 for F32, and the block length K/nb
+ * must be a multiple of the same number; Ga <= G.  Outside them the call
+ * returns GMM_E_UNSUPPORTED and queues nothing.  Shape or dtype
+ * inconsistencies return GMM_E_INVALID and queue nothing.  A launch failure
+ * returns GMM_E_HIP.  Invalid device-resident values (negative sizes, a total
+ * beyond M, an offset outside [0, G-Ga]) are clamped and reported through
+ * gmm_device_flags.
+ */
+gmm_status gmm_run(gmm_handle* h,
+                   const gmm_tensor* lhs,
+                   const gmm_tensor* rhs,
+                   const gmm_tensor* group_sizes,
+                   const gmm_tensor* rhs_scale,
+                   const gmm_tensor* rhs_bias,
+                   const gmm_tensor* lhs_scale,
+                   const int32_t* group_offset,
+                   int transpose_rhs,
+                   const gmm_tensor* out,
+                   void* stream);
+
+/*
+ * gmm_device_flags: synchronise `stream`, return the GMM_FLAG_* bits that
+ * runs on this handle have set since the last call, and clear them.
+ * Returns GMM_E_DEVICE_DATA when any bit was set, GMM_OK otherwise.
+ */
+gmm_status gmm_device_flags(gmm_handle* h, void* stream, uint32_t* flags);
+
+/*
+ * gmm_debug_worklist: run the device code that turns group_sizes and the
+ * group offset into group-aligned m-tiles -- the same device functions every
+ * gmm_run kernel starts with -- and write the tiles it finds.
+ *
+ *   group_sizes  [G] I32 on the device.
+ *   group_offset NULL or a device int32 (as in gmm_run).
+ *   num_active   Ga.
+ *   M            number of lhs rows (offsets are clamped to it).
+ *   tm           m-tile height, 1..4096.
+ *   tiles        device int32 [capacity, 3]: (group, first_row, rows) per tile,
+ *                in group order.
+ *   count        device int32 [4]: tile count, first active row, end of the
+ *                active rows, and the flag bits of this call.
+ * Queues one kernel on `stream`.  Tiles beyond `capacity` are counted but not
+ * written.
+ */
+gmm_status gmm_debug_worklist(gmm_handle* h,
+                              const gmm_tensor* group_sizes,
+                              const int32_t* group_offset,
+                              int64_t num_active,
+                              int64_t M,
+                              int32_t tm,
+                              int32_t* tiles,
+                              int64_t capacity,
+                              int32_t* count,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GMM_MI355X_GMM_H */

@@ -1,0 +1,179 @@
+"""Plain CPU oracle for the grouped matmul (gmm).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg use this package; the product library never imports, loads
+or calls it, and it shares no code with the HIP path.
+
+The arithmetic lives in ``gmm_oracle.c`` (plain loops, fp64, k ascending);
+this module builds it with gcc, marshals torch CPU tensors into it, and holds
+the two tile-metadata definitions in ``worklist.py``.  Citations refer to the
+tpu-inference 0.13.2 wheel diff page (megablox/gmm.py), the metrale
+gemm_quant.rs page and the MaxText PR page "Megablox: transposed-RHS gmm_v2
+kernel for the backward dlhs".
+
+Parity pins: every function here is checked by ``tests/test_oracle_pins.py``
+against closed forms, library routines and hand-worked fixtures.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from .worklist import group_offsets, megablox_metadata, tile_worklist  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gmm_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32, BF16, E4M3FN = 0, 1, 2
+_DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: E4M3FN}
+
+OK, E_ARG, E_DATA, E_NOMEM = 0, -1, -4, -5
+
+
+class OracleError(ValueError):
+    pass
+
+
+def build(force: bool = True) -> str:
+    """Compile gmm_oracle.c into liboracle.so with gcc (no fast-math: the
+    k-ascending fp64 summation order is kept)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+                               _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.oracle_decode_bf16.restype = ctypes.c_double
+        lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
+        lib.oracle_decode_e4m3fn.restype = ctypes.c_double
+        lib.oracle_decode_e4m3fn.argtypes = [ctypes.c_uint8]
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.oracle_round_bf16.restype = ctypes.c_uint16
+        lib.oracle_round_bf16.argtypes = [ctypes.c_double]
+        lib.oracle_round_bf16_array.restype = None
+        lib.oracle_round_bf16_array.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.oracle_gmm.restype = ctypes.c_int
+        lib.oracle_gmm.argtypes = [vp, i32, i64, i64,
+                                   vp, i32, i64, i64, i32,
+                                   vp, i64, i64,
+                                   vp, vp, i32,
+                                   vp, i64,
+                                   vp, i64,
+                                   vp, vp]
+        _lib = lib
+    return _lib
+
+
+def decode_bf16(bits: int) -> float:
+    return _load().oracle_decode_bf16(bits & 0xFFFF)
+
+
+def round_bf16_bits(x: float) -> int:
+    return _load().oracle_round_bf16(float(x))
+
+
+def decode_e4m3fn(code: int) -> float:
+    return _load().oracle_decode_e4m3fn(code & 0xFF)
+
+
+def _cpu(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if t is None:
+        return None
+    return t.detach().to("cpu").contiguous()
+
+
+def _code(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _DTYPE_CODE:
+        raise OracleError(f"{name}: unsupported dtype {t.dtype}")
+    return _DTYPE_CODE[t.dtype]
+
+
+def gmm_reference(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,
+                  group_offset: int = 0, transpose_rhs: bool = False,
+                  rhs_scale: Optional[torch.Tensor] = None,
+                  rhs_bias: Optional[torch.Tensor] = None,
+                  lhs_scale: Optional[torch.Tensor] = None,
+                  rows: Optional[Sequence[int]] = None,
+                  return_row_group: bool = False):
+    """Reference rows of gmm(lhs, rhs, group_sizes, ...) in float64.
+
+    lhs [M,K]; rhs [Ga,N,K] (transpose_rhs False) or [Ga,K,N] (True);
+    group_sizes [G] int32; rhs_scale f32 [Ga,nb,1,N]; rhs_bias [Ga,1,N];
+    lhs_scale f32 [M,nb].  ``rows`` selects output rows (all when None).
+    Returns a float64 numpy array [len(rows), N] (and the group of each row,
+    -1 for none, when return_row_group)."""
+    lib = _load()
+    lhs, rhs, gs = _cpu(lhs), _cpu(rhs), _cpu(group_sizes)
+    rhs_scale, rhs_bias, lhs_scale = _cpu(rhs_scale), _cpu(rhs_bias), _cpu(lhs_scale)
+    if lhs.dim() != 2 or rhs.dim() != 3 or gs.dim() != 1 or gs.dtype != torch.int32:
+        raise OracleError("bad ranks / group_sizes dtype")
+    M, K = lhs.shape
+    Ga = rhs.shape[0]
+    N = rhs.shape[2] if transpose_rhs else rhs.shape[1]
+    Kr = rhs.shape[1] if transpose_rhs else rhs.shape[2]
+    if Kr != K:
+        raise OracleError("lhs / rhs contraction sizes differ")
+    nb = 1
+    if rhs_scale is not None:
+        if rhs_scale.dtype != torch.float32 or tuple(rhs_scale.shape[::2]) != (Ga, 1) \
+                or rhs_scale.shape[3] != N:
+            raise OracleError("rhs_scale must be f32 [Ga,nb,1,N]")
+        nb = rhs_scale.shape[1]
+    if lhs_scale is not None:
+        if lhs_scale.dtype != torch.float32 or lhs_scale.dim() != 2 or lhs_scale.shape[0] != M:
+            raise OracleError("lhs_scale must be f32 [M,nb]")
+        if rhs_scale is not None and lhs_scale.shape[1] != nb:
+            raise OracleError("lhs_scale and rhs_scale disagree on nb")
+        nb = lhs_scale.shape[1]
+    if rhs_bias is not None and tuple(rhs_bias.shape) != (Ga, 1, N):
+        raise OracleError("rhs_bias must be [Ga,1,N]")
+    if rows is None:
+        rows_arr = None
+        n_rows = M
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n_rows = rows_arr.shape[0]
+    out = np.zeros((n_rows, N), dtype=np.float64)
+    rg = np.zeros((n_rows,), dtype=np.int64)
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    rc = lib.oracle_gmm(
+        ptr(lhs), _code(lhs, "lhs"), M, K,
+        ptr(rhs), _code(rhs, "rhs"), Ga, N, int(bool(transpose_rhs)),
+        ptr(gs), gs.shape[0], int(group_offset),
+        ptr(rhs_scale), ptr(rhs_bias), _code(rhs_bias, "rhs_bias") if rhs_bias is not None else 0,
+        ptr(lhs_scale), nb,
+        None if rows_arr is None else rows_arr.ctypes.data, n_rows,
+        out.ctypes.data, rg.ctypes.data)
+    if rc != OK:
+        raise OracleError({E_ARG: "invalid arguments", E_DATA: "invalid group sizes / offset",
+                           E_NOMEM: "out of memory"}.get(rc, str(rc)))
+    return (out, rg) if return_row_group else out
+
+
+def round_to(ref: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
+    """Round float64 reference values once to the output dtype, to nearest
+    with ties to even (float32: C's double->float conversion; bfloat16:
+    oracle_round_bf16, which never rounds twice through float32)."""
+    ref = np.ascontiguousarray(ref, dtype=np.float64)
+    if dtype == torch.float32:
+        return torch.from_numpy(ref.astype(np.float32))
+    if dtype != torch.bfloat16:
+        raise OracleError(f"unsupported output dtype {dtype}")
+    bits = np.empty(ref.shape, dtype=np.uint16)
+    _load().oracle_round_bf16_array(ref.ctypes.data, ref.size, bits.ctypes.data)
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)

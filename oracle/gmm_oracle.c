@@ -1,0 +1,233 @@
+/*
+ * gmm_oracle.c -- plain CPU reference for grouped matrix multiplication.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg do.  It shares no code, header or table with the HIP path.
+ *
+ * What it computes is the plain definition of the Megablox grouped matmul
+ * (tpu-inference 0.13.2 wheel diff page, megablox/gmm.py, docstring of gmm():
+ * each group's contiguous block of lhs rows is multiplied by that group's
+ * slice of rhs), with the extras the same function's kernel body applies:
+ *
+ *   rows of group g are  [o[g], o[g+1])  with  o[0] = 0,
+ *                        o[g+1] = o[g] + group_sizes[g]
+ *       (make_group_metadata: group offsets are the cumulative sum of the
+ *        group sizes, like CSR row offsets)
+ *   only groups s .. s+Ga-1 are computed, Ga = rhs.shape[0], and rhs, scale
+ *   and bias are indexed by g - s
+ *       (gmm(): group_offset argument; kernel index maps subtract the offset)
+ *   out[r, n] = sum_b scale[g-s, b, 0, n] * lscale[r, b] *
+ *                     (sum over k in block b of lhs[r, k] * W(g-s, n, k))
+ *               + bias[g-s, 0, n]
+ *       (kernel _accum: the accumulator is reset per quantisation block,
+ *        multiplied by that block's rhs_scale, and the bias is added once;
+ *        the per-token lhs scale is the activation scale of the block-scaled
+ *        W8A8 GEMM on the metrale gemm_quant.rs page, doc comment of
+ *        fp8_gemm_t_blockscaled)
+ *   W(h, n, k) = rhs[h, n, k]   when transpose_rhs == 0  (NT, rhs [Ga,N,K])
+ *              = rhs[h, k, n]   when transpose_rhs == 1  (NN, rhs [Ga,K,N],
+ *                the forward weight read in place as in the MaxText PR
+ *                "transposed-RHS gmm_v2 kernel for the backward dlhs")
+ *   every row outside [o[s], o[s+Ga]) is 0
+ *       (gmm(): _zero_uninitialized_memory; applied to every such row)
+ *
+ * Arithmetic: every input element is decoded exactly to double; products and
+ * sums are formed in double with k ascending; the result is returned in
+ * double, before any rounding to the output type.  Rounding to the output
+ * type is left to the caller.
+ *
+ * Element decoders are written from the format definitions:
+ *   f32      IEEE-754 binary32.
+ *   bf16     the upper 16 bits of a binary32.
+ *   e4m3fn   1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent
+ *            field 0 encodes subnormals m/8 * 2^-6; S.1111.111 is NaN; there
+ *            are no infinities (OCP 8-bit floating point specification).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_BF16 1
+#define OR_E4M3FN 2
+
+#define OR_OK 0
+#define OR_E_ARG (-1)
+#define OR_E_DATA (-4)
+#define OR_E_NOMEM (-5)
+
+double oracle_decode_bf16(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+double oracle_decode_e4m3fn(uint8_t code) {
+  int sign = (code >> 7) & 1;
+  int e = (code >> 3) & 0xF;
+  int m = code & 0x7;
+  double v;
+  if (e == 0xF && m == 0x7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, -6);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -v : v;
+}
+
+/*
+ * Round a double once to bfloat16, to nearest with ties to even (the cast of
+ * the fp32 accumulator to the output type in the kernel body of gmm();
+ * the rounding mode is not stated there, nearest-even is read in).
+ * bfloat16 keeps 8 significant bits over binary32's exponent range:
+ * quantum 2^(e-7) for |x| in [2^e, 2^(e+1)), e >= -126, and 2^-133 below.
+ * Overflow gives infinity.
+ */
+uint16_t oracle_round_bf16(double x) {
+  float f;
+  uint32_t u;
+  if (x != x) return 0x7FC0;
+  if (x == 0.0 || isinf(x)) {
+    f = (float)x;
+  } else {
+    int e;
+    frexp(x, &e);            /* x = m * 2^e, 0.5 <= |m| < 1 */
+    e -= 1;                  /* now |x| in [2^e, 2^(e+1)) */
+    if (e < -126) e = -126;
+    double q = ldexp(1.0, e - 7);
+    double r = nearbyint(x / q) * q;  /* default rounding: nearest, ties to even */
+    if (fabs(r) >= ldexp(1.0, 128)) r = x > 0 ? INFINITY : -INFINITY;
+    f = (float)r;            /* exact: r has at most 8 significant bits */
+  }
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
+void oracle_round_bf16_array(const double* x, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_round_bf16(x[i]);
+}
+
+static double load_elem(const void* base, int dtype, int64_t idx) {
+  switch (dtype) {
+    case OR_F32: return (double)((const float*)base)[idx];
+    case OR_BF16: return oracle_decode_bf16(((const uint16_t*)base)[idx]);
+    case OR_E4M3FN: return oracle_decode_e4m3fn(((const uint8_t*)base)[idx]);
+    default: return NAN;
+  }
+}
+
+static int dtype_ok(int d) { return d == OR_F32 || d == OR_BF16 || d == OR_E4M3FN; }
+
+/*
+ * Group offsets o[0..G] (int64, so no overflow) from group_sizes.
+ * Returns OR_E_DATA for a negative size or a total beyond M.
+ */
+int oracle_group_offsets(const int32_t* group_sizes, int64_t G, int64_t M, int64_t* o) {
+  o[0] = 0;
+  for (int64_t g = 0; g < G; ++g) {
+    if (group_sizes[g] < 0) return OR_E_DATA;
+    o[g + 1] = o[g] + group_sizes[g];
+  }
+  if (o[G] > M) return OR_E_DATA;
+  return OR_OK;
+}
+
+/*
+ * oracle_gmm: reference values for a set of output rows.
+ *
+ *   lhs          [M, K] of lhs_dtype, row-major.
+ *   rhs          [Ga, N, K] (transpose_rhs == 0) or [Ga, K, N] (== 1).
+ *   group_sizes  [G] int32.
+ *   group_offset s; groups s .. s+Ga-1 are active.  Requires 0 <= s and
+ *                s + Ga <= G.
+ *   rhs_scale    NULL or f32 [Ga, nb, 1, N]; K % nb == 0.
+ *   rhs_bias     NULL or [Ga, 1, N] of bias_dtype.
+ *   lhs_scale    NULL or f32 [M, nb].
+ *   nb           number of quantisation blocks (1 when no scale is given).
+ *   rows         NULL (all M rows, in order) or n_rows row indices.
+ *   out          [n_rows, N] double: reference value of each requested row.
+ *   row_group    NULL or [n_rows] int64: the group of each row, -1 if none.
+ *
+ * Returns OR_OK, OR_E_ARG for inconsistent arguments, OR_E_DATA for invalid
+ * group sizes or group offset, OR_E_NOMEM.
+ */
+int oracle_gmm(const void* lhs, int lhs_dtype, int64_t M, int64_t K,
+               const void* rhs, int rhs_dtype, int64_t Ga, int64_t N, int transpose_rhs,
+               const int32_t* group_sizes, int64_t G, int64_t group_offset,
+               const float* rhs_scale, const void* rhs_bias, int bias_dtype,
+               const float* lhs_scale, int64_t nb,
+               const int64_t* rows, int64_t n_rows,
+               double* out, int64_t* row_group) {
+  if (M < 0 || K <= 0 || N <= 0 || Ga < 0 || G < 0 || nb <= 0) return OR_E_ARG;
+  if (!dtype_ok(lhs_dtype) || !dtype_ok(rhs_dtype)) return OR_E_ARG;
+  if (rhs_bias && !dtype_ok(bias_dtype)) return OR_E_ARG;
+  if (K % nb != 0) return OR_E_ARG;
+  if (!rhs_scale && !lhs_scale && nb != 1) return OR_E_ARG;
+  if (rows == NULL) n_rows = M;
+  for (int64_t i = 0; i < n_rows; ++i) {
+    int64_t r = rows ? rows[i] : i;
+    if (r < 0 || r >= M) return OR_E_ARG;
+  }
+  const int64_t s = group_offset;
+  if (s < 0 || s + Ga > G) return OR_E_DATA;
+
+  int64_t* o = (int64_t*)malloc(sizeof(int64_t) * (size_t)(G + 1));
+  if (!o) return OR_E_NOMEM;
+  int rc = oracle_group_offsets(group_sizes, G, M, o);
+  if (rc != OR_OK) { free(o); return rc; }
+
+  /* Rows that belong to no active group are zero. */
+  for (int64_t i = 0; i < n_rows; ++i) {
+    for (int64_t n = 0; n < N; ++n) out[i * N + n] = 0.0;
+    if (row_group) row_group[i] = -1;
+  }
+
+  const int64_t blk = K / nb;
+  double* w = (double*)malloc(sizeof(double) * (size_t)(N * K));
+  if (!w) { free(o); return OR_E_NOMEM; }
+
+  for (int64_t g = s; g < s + Ga; ++g) {
+    const int64_t lo = o[g], hi = o[g + 1];
+    if (hi == lo) continue;
+    int any = 0;
+    for (int64_t i = 0; i < n_rows && !any; ++i) {
+      int64_t r = rows ? rows[i] : i;
+      any = (r >= lo && r < hi);
+    }
+    if (!any) continue;
+    const int64_t h = g - s;
+
+    /* This group's weight, decoded exactly, as W(n, k). */
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t k = 0; k < K; ++k) {
+        int64_t idx = transpose_rhs ? (h * K + k) * N + n : (h * N + n) * K + k;
+        w[n * K + k] = load_elem(rhs, rhs_dtype, idx);
+      }
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_rows; ++i) {
+      const int64_t r = rows ? rows[i] : i;
+      if (r < lo || r >= hi) continue;
+      if (row_group) row_group[i] = g;
+      for (int64_t n = 0; n < N; ++n) {
+        double t = 0.0;
+        for (int64_t b = 0; b < nb; ++b) {
+          double p = 0.0;
+          for (int64_t k = b * blk; k < (b + 1) * blk; ++k)
+            p += load_elem(lhs, lhs_dtype, r * K + k) * w[n * K + k];
+          if (rhs_scale) p *= (double)rhs_scale[(h * nb + b) * N + n];
+          if (lhs_scale) p *= (double)lhs_scale[r * nb + b];
+          t += p;
+        }
+        if (rhs_bias) t += load_elem(rhs_bias, bias_dtype, h * N + n);
+        out[i * N + n] = t;
+      }
+    }
+  }
+  free(w);
+  free(o);
+  return OR_OK;
+}
