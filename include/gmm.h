@@ -138,6 +138,15 @@ gmm_status gmm_run(gmm_handle* h,
 gmm_status gmm_device_flags(gmm_handle* h, void* stream, uint32_t* flags);
 
 /*
+ * gmm_set_tile_policy: choose the output tile family of later gmm_run calls
+ * on h.  0 (the default) picks from the problem shape; 1 forces the small
+ * decode tiles (32 x 64); 2 forces the big tiles (256 x 128).  The result
+ * differs only in the order of fp32 additions.  Returns GMM_E_INVALID for
+ * another value.  For tests and tuning.
+ */
+gmm_status gmm_set_tile_policy(gmm_handle* h, int policy);
+
+/*
  * gmm_debug_worklist: run the device code that turns group_sizes and the
  * group offset into group-aligned m-tiles -- the same device functions every
  * gmm_run kernel starts with -- and write the tiles it finds.

@@ -1,0 +1,11 @@
+"""Grouped matrix multiplication (gmm) for AMD MI355X (gfx950).
+
+The computation runs in hand-written HIP kernels behind the C ABI of
+libgmm.so (include/gmm.h); this package is the thin Python binding over it.
+Build the library with ``moe_grouped_matrix_amd.build.build()``."""
+from ._binding import (EXPORTED, FLAG_BAD_OFFSET, FLAG_NEGATIVE_SIZE, FLAG_SIZES_EXCEED_M,  # noqa: F401
+                       LIB_PATH, GmmDeviceDataError, GmmError, GmmInvalid, GmmUnsupported,
+                       debug_worklist, device_flags, gmm, handle, load, set_tile_policy)
+
+__all__ = ["gmm", "device_flags", "debug_worklist", "set_tile_policy", "load", "handle",
+           "GmmError", "GmmInvalid", "GmmUnsupported", "GmmDeviceDataError", "LIB_PATH"]

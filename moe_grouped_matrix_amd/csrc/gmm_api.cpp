@@ -1,0 +1,302 @@
+// gmm_api.cpp -- the C ABI of libgmm.so (declared in include/gmm.h).
+//
+// Argument checks mirror the shape and dtype validation of the Megablox gmm
+// (tpu-inference 0.13.2 wheel diff page, megablox/gmm.py, _validate_args and
+// the checks at the top of gmm()); everything they reject returns
+// GMM_E_INVALID before any work is queued.  The kernels themselves live in
+// gmm_kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/gmm.h"
+#include "gmm_launch.hpp"
+
+struct gmm_handle {
+  int device = 0;
+  int cu_count = 0;
+  uint32_t* flags = nullptr;  // device word
+  int tile_policy = 0;        // 0 auto, 1 small tiles, 2 big tiles
+  std::string err;
+};
+
+namespace {
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+gmm_status fail(gmm_handle* h, gmm_status st, const std::string& msg) {
+  if (h) h->err = msg;
+  return st;
+}
+
+std::string shape_str(const gmm_tensor* t) {
+  std::string s = "(";
+  for (int i = 0; i < t->ndim && i < 4; ++i) {
+    if (i) s += ",";
+    s += std::to_string(t->shape[i]);
+  }
+  return s + ")";
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(int dtype) {
+  switch (dtype) {
+    case GMM_F32: return 4;
+    case GMM_BF16: return 2;
+    case GMM_F8E4M3FN: return 1;
+    case GMM_I32: return 4;
+    default: return 0;
+  }
+}
+
+long long numel(const gmm_tensor* t) {
+  long long n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+bool overlaps(const gmm_tensor* a, const gmm_tensor* b) {
+  if (!a || !b || !a->data || !b->data) return false;
+  const char* a0 = static_cast<const char*>(a->data);
+  const char* b0 = static_cast<const char*>(b->data);
+  const char* a1 = a0 + numel(a) * elem_size(a->dtype);
+  const char* b1 = b0 + numel(b) * elem_size(b->dtype);
+  return a0 < b1 && b0 < a1;
+}
+
+}  // namespace
+
+extern "C" {
+
+gmm_status gmm_create(gmm_handle** out, int device) {
+  if (!out) return GMM_E_INVALID;
+  *out = nullptr;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return GMM_E_HIP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return GMM_E_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GMM_E_UNSUPPORTED;
+  gmm_handle* h = new gmm_handle();
+  h->device = device;
+  h->cu_count = prop.multiProcessorCount;
+  DeviceGuard g(device);
+  if (hipMalloc(&h->flags, sizeof(uint32_t)) != hipSuccess) {
+    delete h;
+    return GMM_E_HIP;
+  }
+  if (hipMemset(h->flags, 0, sizeof(uint32_t)) != hipSuccess) {
+    (void)hipFree(h->flags);
+    delete h;
+    return GMM_E_HIP;
+  }
+  *out = h;
+  return GMM_OK;
+}
+
+gmm_status gmm_destroy(gmm_handle* h) {
+  if (!h) return GMM_OK;
+  {
+    DeviceGuard g(h->device);
+    if (h->flags) (void)hipFree(h->flags);
+  }
+  delete h;
+  return GMM_OK;
+}
+
+const char* gmm_last_error(const gmm_handle* h) { return h ? h->err.c_str() : "null handle"; }
+
+// Test hook: 0 chooses tiles from the problem shape, 1 forces the small
+// (decode) tiles, 2 the big tiles.  Results differ only in fp32 summation
+// order.
+gmm_status gmm_set_tile_policy(gmm_handle* h, int policy) {
+  if (!h || policy < 0 || policy > 2) return GMM_E_INVALID;
+  h->tile_policy = policy;
+  return GMM_OK;
+}
+
+gmm_status gmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs,
+                   const gmm_tensor* group_sizes, const gmm_tensor* rhs_scale,
+                   const gmm_tensor* rhs_bias, const gmm_tensor* lhs_scale,
+                   const int32_t* group_offset, int transpose_rhs, const gmm_tensor* out,
+                   void* stream) {
+  if (!h) return GMM_E_INVALID;
+  h->err.clear();
+  if (!lhs || !rhs || !group_sizes || !out) return fail(h, GMM_E_INVALID, "lhs, rhs, group_sizes and out are required");
+  if (lhs->ndim != 2) return fail(h, GMM_E_INVALID, "expected a 2-tensor for lhs, got ndim=" + std::to_string(lhs->ndim));
+  if (rhs->ndim != 3) return fail(h, GMM_E_INVALID, "expected a 3-tensor for rhs, got ndim=" + std::to_string(rhs->ndim));
+  if (group_sizes->ndim != 1 || group_sizes->dtype != GMM_I32)
+    return fail(h, GMM_E_INVALID, "expected a 1-d int32 group_sizes");
+  if (out->ndim != 2) return fail(h, GMM_E_INVALID, "expected a 2-tensor for out");
+
+  const long long M = lhs->shape[0], K = lhs->shape[1];
+  const long long Ga = rhs->shape[0];
+  const long long N = transpose_rhs ? rhs->shape[2] : rhs->shape[1];
+  const long long Kr = transpose_rhs ? rhs->shape[1] : rhs->shape[2];
+  const long long G = group_sizes->shape[0];
+  if (Kr != K)
+    return fail(h, GMM_E_INVALID, "lhs and rhs disagree on the contraction size: lhs " + shape_str(lhs) +
+                                      ", rhs " + shape_str(rhs));
+  if (M < 0 || K <= 0 || N <= 0 || Ga < 0) return fail(h, GMM_E_INVALID, "negative or zero extent");
+  if (out->shape[0] != M || out->shape[1] != N)
+    return fail(h, GMM_E_INVALID, "out must be [M,N] = [" + std::to_string(M) + "," + std::to_string(N) + "], got " + shape_str(out));
+  if (out->dtype != GMM_F32 && out->dtype != GMM_BF16) return fail(h, GMM_E_INVALID, "out must be f32 or bf16");
+  if (G < 1) return fail(h, GMM_E_INVALID, "group_sizes must hold at least one group");
+  if (Ga > G) return fail(h, GMM_E_INVALID, "rhs holds more groups than group_sizes");
+
+  gmmk::KernelChoice kc{};
+  const int ld = lhs->dtype, rd = rhs->dtype;
+  if (ld == GMM_F32 && rd == GMM_F32) {
+    kc.op = gmmk::Op::F32;
+  } else if (ld == GMM_BF16 && rd == GMM_BF16) {
+    kc.op = gmmk::Op::BF16;
+  } else if (ld == GMM_BF16 && rd == GMM_F8E4M3FN) {
+    kc.op = gmmk::Op::BF16;
+    kc.b_fp8 = true;
+  } else if (ld == GMM_F8E4M3FN && rd == GMM_F8E4M3FN) {
+    kc.op = gmmk::Op::FP8;
+  } else {
+    if (elem_size(ld) == 0 || elem_size(rd) == 0 || ld == GMM_I32 || rd == GMM_I32)
+      return fail(h, GMM_E_INVALID, "unsupported lhs / rhs dtype");
+    return fail(h, GMM_E_UNSUPPORTED, "unsupported (lhs, rhs) dtype pair");
+  }
+  kc.nn = transpose_rhs != 0;
+  if (kc.nn && (kc.b_fp8 || kc.op == gmmk::Op::FP8))
+    return fail(h, GMM_E_UNSUPPORTED, "e4m3 weights are read in the [G,N,K] layout only");
+
+  long long nb = 1;
+  if (rhs_scale) {
+    if (rhs_scale->ndim != 4 || rhs_scale->dtype != GMM_F32)
+      return fail(h, GMM_E_INVALID, "expected an f32 4-tensor for rhs_scale");
+    nb = rhs_scale->shape[1];
+    if (rhs_scale->shape[0] != Ga || rhs_scale->shape[2] != 1 || rhs_scale->shape[3] != N || nb < 1)
+      return fail(h, GMM_E_INVALID, "expected rhs_scale of shape (Ga, nb, 1, N), got " + shape_str(rhs_scale));
+  }
+  if (lhs_scale) {
+    if (lhs_scale->ndim != 2 || lhs_scale->dtype != GMM_F32 || lhs_scale->shape[0] != M || lhs_scale->shape[1] < 1)
+      return fail(h, GMM_E_INVALID, "expected lhs_scale of shape (M, nb), f32");
+    if (rhs_scale && lhs_scale->shape[1] != nb)
+      return fail(h, GMM_E_INVALID, "lhs_scale and rhs_scale disagree on the number of blocks");
+    nb = lhs_scale->shape[1];
+  }
+  if (K % nb) return fail(h, GMM_E_INVALID, "K must be a multiple of the number of quantisation blocks");
+  if (rhs_bias) {
+    if (rhs_bias->ndim != 3 || rhs_bias->shape[0] != Ga || rhs_bias->shape[1] != 1 || rhs_bias->shape[2] != N)
+      return fail(h, GMM_E_INVALID, "expected rhs_bias of shape (Ga, 1, N), got " + shape_str(rhs_bias));
+    if (rhs_bias->dtype != GMM_F32 && rhs_bias->dtype != GMM_BF16)
+      return fail(h, GMM_E_INVALID, "rhs_bias must be f32 or bf16");
+  }
+  kc.scaled = rhs_scale != nullptr || lhs_scale != nullptr;
+
+  // Limits of the kernels (valid problems outside them are unsupported).
+  const int kt = gmmk::k_tile(kc.op);
+  const long long blk = K / nb;
+  if (G > gmmk::kMaxGroups) return fail(h, GMM_E_UNSUPPORTED, "more than 1024 groups");
+  if (M >= (1LL << 31) || N >= (1LL << 31) || K >= (1LL << 31))
+    return fail(h, GMM_E_UNSUPPORTED, "extent beyond 2^31");
+  if (N % 8) return fail(h, GMM_E_UNSUPPORTED, "N must be a multiple of 8");
+  if (K % kt) return fail(h, GMM_E_UNSUPPORTED, "K must be a multiple of " + std::to_string(kt) + " for this dtype");
+  if (kc.scaled && blk % kt)
+    return fail(h, GMM_E_UNSUPPORTED, "the quantisation block K/nb must be a multiple of " + std::to_string(kt));
+  const long long bsb = elem_size(rd);
+  if (K * N * bsb >= 0x7FFFFFF0LL || 256LL * K * elem_size(ld) >= 0x7FFFFFF0LL)
+    return fail(h, GMM_E_UNSUPPORTED, "one group's weight (or a 256-row lhs tile) exceeds 2 GiB");
+
+  const gmm_tensor* ins[] = {lhs, rhs, group_sizes, rhs_scale, rhs_bias, lhs_scale};
+  for (const gmm_tensor* t : ins) {
+    if (!t) continue;
+    if (numel(t) > 0 && !t->data) return fail(h, GMM_E_INVALID, "null data pointer");
+    if (!aligned16(t->data)) return fail(h, GMM_E_INVALID, "tensor data must be 16-byte aligned");
+    if (overlaps(t, out)) return fail(h, GMM_E_INVALID, "out overlaps an input");
+  }
+  if (M > 0 && !out->data) return fail(h, GMM_E_INVALID, "null out pointer");
+  if (!aligned16(out->data) || !aligned16(group_offset))
+    return fail(h, GMM_E_INVALID, "out and group_offset must be 16-byte aligned");
+  if (M == 0) return GMM_OK;
+
+  if (h->tile_policy == 1)
+    kc.size = gmmk::SizeClass::Small;
+  else if (h->tile_policy == 2)
+    kc.size = gmmk::SizeClass::Big;
+  else
+    kc.size = (M >= 8192 && M >= 512 * (Ga > 0 ? Ga : 1)) ? gmmk::SizeClass::Big : gmmk::SizeClass::Small;
+
+  gmmk::Params p{};
+  p.lhs = lhs->data;
+  p.rhs = rhs->data;
+  p.group_sizes = static_cast<const int32_t*>(group_sizes->data);
+  p.group_offset = group_offset;
+  p.rhs_scale = rhs_scale ? static_cast<const float*>(rhs_scale->data) : nullptr;
+  p.rhs_bias = rhs_bias ? rhs_bias->data : nullptr;
+  p.lhs_scale = lhs_scale ? static_cast<const float*>(lhs_scale->data) : nullptr;
+  p.out = const_cast<void*>(out->data);
+  p.flags = h->flags;
+  p.M = (int32_t)M;
+  p.K = (int32_t)K;
+  p.N = (int32_t)N;
+  p.G = (int32_t)G;
+  p.Ga = (int32_t)Ga;
+  p.nb = (int32_t)nb;
+  p.blk = (int32_t)blk;
+  p.bias_f32 = rhs_bias && rhs_bias->dtype == GMM_F32;
+  p.out_f32 = out->dtype == GMM_F32;
+
+  DeviceGuard g(h->device);
+  hipError_t e = gmmk::launch_gmm(p, kc, h->cu_count, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(h, GMM_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return GMM_OK;
+}
+
+gmm_status gmm_device_flags(gmm_handle* h, void* stream, uint32_t* flags) {
+  if (!h || !flags) return GMM_E_INVALID;
+  DeviceGuard g(h->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  if (hipStreamSynchronize(st) != hipSuccess ||
+      hipMemcpy(&v, h->flags, sizeof v, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemset(h->flags, 0, sizeof v) != hipSuccess)
+    return fail(h, GMM_E_HIP, "reading the device flags failed");
+  *flags = v;
+  if (v) return fail(h, GMM_E_DEVICE_DATA, "invalid device-resident group_sizes or group offset (flags " + std::to_string(v) + ")");
+  return GMM_OK;
+}
+
+gmm_status gmm_debug_worklist(gmm_handle* h, const gmm_tensor* group_sizes, const int32_t* group_offset,
+                              int64_t num_active, int64_t M, int32_t tm, int32_t* tiles, int64_t capacity,
+                              int32_t* count, void* stream) {
+  if (!h) return GMM_E_INVALID;
+  h->err.clear();
+  if (!group_sizes || group_sizes->ndim != 1 || group_sizes->dtype != GMM_I32 || !group_sizes->data)
+    return fail(h, GMM_E_INVALID, "expected a 1-d int32 group_sizes");
+  const long long G = group_sizes->shape[0];
+  if (G < 1 || G > gmmk::kMaxGroups) return fail(h, GMM_E_UNSUPPORTED, "1 <= G <= 1024 required");
+  if (num_active < 0 || num_active > G) return fail(h, GMM_E_INVALID, "num_active must be in [0, G]");
+  if (M < 0 || M >= (1LL << 31)) return fail(h, GMM_E_INVALID, "M out of range");
+  if (tm < 1 || tm > 4096) return fail(h, GMM_E_INVALID, "tm must be in [1, 4096]");
+  if (!count || (capacity > 0 && !tiles) || capacity < 0) return fail(h, GMM_E_INVALID, "bad output buffers");
+  gmmk::Params p{};
+  p.group_sizes = static_cast<const int32_t*>(group_sizes->data);
+  p.group_offset = group_offset;
+  p.flags = h->flags;
+  p.M = (int32_t)M;
+  p.G = (int32_t)G;
+  p.Ga = (int32_t)num_active;
+  DeviceGuard g(h->device);
+  hipError_t e = gmmk::launch_worklist(p, tm, tiles, capacity, count, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(h, GMM_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return GMM_OK;
+}
+
+}  // extern "C"

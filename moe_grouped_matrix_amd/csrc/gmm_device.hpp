@@ -1,0 +1,601 @@
+// gmm_device.hpp -- device code of the gfx950 grouped matmul.
+//
+// One persistent kernel family computes the whole operation in a single
+// launch:
+//   1. every workgroup turns group_sizes and the group offset into group
+//      offsets and a table of group-aligned m-tiles, in LDS (the group
+//      offsets of make_group_metadata on the tpu-inference 0.13.2 wheel diff
+//      page, megablox/gmm.py; tiles start at each group's first row, so no
+//      tile holds rows of two groups);
+//   2. it then takes work items in turn: an item is an (m-tile, n-tile) pair
+//      computed with MFMA from LDS-staged, double-buffered K tiles, or a
+//      slice of the rows outside the active groups, which it zeroes
+//      (_zero_uninitialized_memory on the same page).
+// The contraction, the per-block scale fold and the bias follow the kernel
+// body of gmm() on that page (_accum); the per-token lhs scale follows the
+// block-scaled W8A8 GEMM of the metrale gemm_quant.rs page
+// (fp8_gemm_t_blockscaled); the in-place [G,K,N] weight read follows the
+// MaxText PR "Megablox: transposed-RHS gmm_v2 kernel for the backward dlhs".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gmm_params.hpp"
+
+namespace gmmk {
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Group plan kept in LDS for the whole life of a workgroup.
+struct Plan {
+  int32_t tile_start[kMaxGroups + 1];  // first m-tile of active group h
+  int32_t row_start[kMaxGroups + 1];   // o[s + h], clamped to [0, M]
+  long long wave_tot[16];
+  int32_t s, ga, n_mtiles;
+  unsigned int flags;
+};
+
+// ---------------------------------------------------------------------------
+// prologue: group offsets and m-tile table
+
+// Exclusive prefix sum of one value per thread over the workgroup.
+template <int T>
+__device__ inline long long block_excl_scan(long long v, long long* wave_tot, long long* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  long long incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    long long y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) wave_tot[w] = incl;
+  __syncthreads();
+  long long base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < T / 64; ++i) {
+    long long x = wave_tot[i];
+    if (i < w) base += x;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
+}
+
+// Builds the plan for m-tiles of height bm.  Values outside the contract are
+// clamped so that every later access stays in bounds, and reported in flags:
+// negative sizes count as 0, offsets beyond M are cut to M, an offset outside
+// [0, G-Ga] is clamped into [0, G] with Ga cut to G - s.
+template <int T>
+__device__ void build_plan(const Params& p, Plan& pl, int bm) {
+  constexpr int EMAX = (kMaxGroups + T - 1) / T;
+  const int tid = threadIdx.x;
+  uint32_t flags = 0;
+  int s = p.group_offset ? p.group_offset[0] : 0;
+  if (s < 0 || s > p.G - p.Ga) {
+    flags |= kFlagBadOffset;
+    s = s < 0 ? 0 : (s > p.G ? p.G : s);
+  }
+  const int ga = p.Ga < p.G - s ? p.Ga : p.G - s;
+
+  // o[g+1] for the groups this thread owns (a contiguous run of E groups).
+  const int E = (p.G + T - 1) / T;
+  long long loc[EMAX];
+  long long sum = 0;
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    const int g = tid * E + e;
+    long long v = 0;
+    if (e < E && g < p.G) {
+      int x = p.group_sizes[g];
+      if (x < 0) {
+        flags |= kFlagNegative;
+        x = 0;
+      }
+      v = x;
+    }
+    sum += v;
+    loc[e] = sum;
+  }
+  long long total;
+  const long long excl = block_excl_scan<T>(sum, pl.wave_tot, &total);
+  if (total > p.M) flags |= kFlagExceed;
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    const int g = tid * E + e;
+    if (e < E && g < p.G) {
+      const int h = g + 1 - s;
+      if (h >= 0 && h <= ga) {
+        long long o = excl + loc[e];
+        pl.row_start[h] = (int)(o < p.M ? o : p.M);
+      }
+    }
+  }
+  if (tid == 0 && s == 0) pl.row_start[0] = 0;
+  __syncthreads();
+
+  // m-tiles per active group, then their prefix sum.
+  const int E2 = (ga + T - 1) / T;
+  long long loc2[EMAX];
+  long long sum2 = 0;
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    const int h = tid * E2 + e;
+    long long c = 0;
+    if (e < E2 && h < ga) c = (pl.row_start[h + 1] - pl.row_start[h] + bm - 1) / bm;
+    sum2 += c;
+    loc2[e] = sum2;
+  }
+  long long total2;
+  const long long excl2 = block_excl_scan<T>(sum2, pl.wave_tot, &total2);
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    const int h = tid * E2 + e;
+    if (e < E2 && h < ga) pl.tile_start[h + 1] = (int)(excl2 + loc2[e]);
+  }
+  if (tid == 0) {
+    pl.tile_start[0] = 0;
+    pl.s = s;
+    pl.ga = ga;
+    pl.n_mtiles = (int)total2;
+  }
+  // Block-wide OR of the flags (only workgroup 0 reports them).
+  if (flags) atomicOr(&pl.flags, flags);
+  __syncthreads();
+}
+
+// Active group (relative index h) that holds m-tile t, 0 <= t < n_mtiles:
+// the largest h with tile_start[h] <= t.  Empty groups own no tile and are
+// never returned.
+__device__ inline int find_group(const Plan& pl, int t) {
+  int lo = 0, hi = pl.ga;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pl.tile_start[mid] <= t)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+__device__ inline void report_flags(const Params& p, const Plan& pl) {
+  if (blockIdx.x == 0 && threadIdx.x == 0 && pl.flags) atomicOr(p.flags, (uint32_t)pl.flags);
+}
+
+// Position of a logical work item among the workgroups of one round: the
+// hardware hands workgroups to the 8 XCDs in turn, so workgroup b runs on
+// XCD b % 8; giving each XCD a contiguous run of items keeps the operands
+// those items share in that XCD's L2.
+__device__ inline int xcd_slot(int b, int P) {
+  if (P % 8) return b;
+  return (b % 8) * (P / 8) + b / 8;
+}
+
+// ---------------------------------------------------------------------------
+// element helpers
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long bytes) {
+  int n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0 : (int)(bytes < 0 ? 0 : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufferRsrcWord3);
+}
+
+// 8 e4m3fn bytes widened to 8 bf16 (exact: every e4m3fn value is a bf16).
+__device__ inline i32x4 e4m3x8_to_bf16x8(i32x2 v) {
+  i32x4 r;
+  bf16x2 t;
+  t = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[0], 1.0f, false);
+  r[0] = __builtin_bit_cast(int, t);
+  t = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[0], 1.0f, true);
+  r[1] = __builtin_bit_cast(int, t);
+  t = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[1], 1.0f, false);
+  r[2] = __builtin_bit_cast(int, t);
+  t = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[1], 1.0f, true);
+  r[3] = __builtin_bit_cast(int, t);
+  return r;
+}
+
+__device__ inline float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// 16-byte chunk c (0..7) of a 128-byte LDS row r is stored at chunk
+// c ^ swz(r).  Sixteen consecutive rows read at one logical chunk hit sixteen
+// distinct 16-byte bank groups, with 32 or 64 banks.
+__device__ inline int swz(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ inline int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
+
+// ---------------------------------------------------------------------------
+// tile configurations
+
+template <Op OP, bool NN_, bool BFP8_, int BM_, int BN_, int WM_, int WN_, bool SCALED_>
+struct Cfg {
+  static constexpr Op op = OP;
+  static constexpr bool NN = NN_;        // rhs is [Ga,K,N]
+  static constexpr bool B_FP8 = BFP8_;   // e4m3 rhs widened to bf16 operands
+  static constexpr bool SCALED = SCALED_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int T = 64 * WM * WN;
+  static constexpr int ES = OP == Op::F32 ? 4 : (OP == Op::BF16 ? 2 : 1);  // operand bytes
+  static constexpr int BK = 128 / ES;       // K elements per 128-byte LDS row
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 16, FN = TN / 16;
+  static constexpr int A_CH = BM * 8 / T;   // 16-byte A chunks per thread
+  static constexpr int B_CH = BN * 8 / T;   // 16-byte B operand chunks per thread
+  static constexpr int KB = 16 / ES;        // K elements per 16-byte chunk
+  static constexpr int NW = BN * 8 / T;     // NN: n-columns per thread block
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  static constexpr int LDS = 2 * (A_BYTES + B_BYTES);
+  static constexpr int BSB = B_FP8 ? 1 : ES;  // rhs storage bytes per element
+  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
+  static_assert(A_CH >= 1 && A_CH * T == BM * 8, "A tile must split evenly");
+  static_assert(B_CH >= 1 && B_CH * T == BN * 8, "B tile must split evenly");
+  static_assert(!NN || (!B_FP8 && OP != Op::FP8), "NN needs f32 or bf16 weights");
+  static_assert(!NN || NW == 2 || NW == 4 || NW == 8, "NN thread block width");
+  static_assert(!B_FP8 || OP == Op::BF16, "e4m3 weights widen to bf16");
+};
+
+// ---------------------------------------------------------------------------
+// the kernel
+
+template <class C>
+struct Stage {
+  i32x4 a[C::A_CH];
+  // NT: B_CH chunks of operand (or e4m3 half-chunks in .x/.y when B_FP8);
+  // NN: KB rows of NW elements, packed into B_CH chunks.
+  i32x4 b[C::B_CH];
+};
+
+template <class C>
+__device__ inline void load_tile(const C&, Stage<C>& st, __amdgpu_buffer_rsrc_t ar,
+                                 __amdgpu_buffer_rsrc_t br, int kt, int K, int N, int n0) {
+  const int tid = threadIdx.x;
+  const int arow_bytes = K * C::ES;
+#pragma unroll
+  for (int i = 0; i < C::A_CH; ++i) {
+    const int c = tid + i * C::T;
+    const int r = c >> 3, cc = c & 7;
+    st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, r * arow_bytes + kt * 128 + cc * 16, 0, 0);
+  }
+  if constexpr (!C::NN) {
+#pragma unroll
+    for (int i = 0; i < C::B_CH; ++i) {
+      const int c = tid + i * C::T;
+      const int r = c >> 3, cc = c & 7;
+      if constexpr (C::B_FP8) {
+        i32x2 v = __builtin_amdgcn_raw_buffer_load_b64(br, r * K + kt * 64 + cc * 8, 0, 0);
+        st.b[i][0] = v[0];
+        st.b[i][1] = v[1];
+      } else {
+        st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(br, r * K * C::ES + kt * 128 + cc * 16, 0, 0);
+      }
+    }
+  } else {
+    // Thread block: KB consecutive k rows x NW consecutive n columns.
+    constexpr int NBLK = C::BN / C::NW;
+    const int nb = tid % NBLK, kb = tid / NBLK;
+    const int nbase = n0 + nb * C::NW;
+    const int kbase = kt * C::BK + kb * C::KB;
+    constexpr int RB = C::NW * C::ES;  // bytes per row piece: 4, 8 or 16
+    int* words = reinterpret_cast<int*>(&st.b[0]);
+#pragma unroll
+    for (int kr = 0; kr < C::KB; ++kr) {
+      const int off = ((kbase + kr) * N + nbase) * C::ES;
+      if constexpr (RB == 4) {
+        words[kr] = __builtin_amdgcn_raw_buffer_load_b32(br, off, 0, 0);
+      } else if constexpr (RB == 8) {
+        i32x2 v = __builtin_amdgcn_raw_buffer_load_b64(br, off, 0, 0);
+        words[2 * kr] = v[0];
+        words[2 * kr + 1] = v[1];
+      } else {
+        i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(br, off, 0, 0);
+        words[4 * kr + 0] = v[0];
+        words[4 * kr + 1] = v[1];
+        words[4 * kr + 2] = v[2];
+        words[4 * kr + 3] = v[3];
+      }
+    }
+  }
+}
+
+template <class C>
+__device__ inline void store_tile(const C&, const Stage<C>& st, char* sa, char* sb) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < C::A_CH; ++i) {
+    const int c = tid + i * C::T;
+    *reinterpret_cast<i32x4*>(sa + lds_off(c >> 3, c & 7)) = st.a[i];
+  }
+  if constexpr (!C::NN) {
+#pragma unroll
+    for (int i = 0; i < C::B_CH; ++i) {
+      const int c = tid + i * C::T;
+      i32x4 v = st.b[i];
+      if constexpr (C::B_FP8) v = e4m3x8_to_bf16x8(i32x2{st.b[i][0], st.b[i][1]});
+      *reinterpret_cast<i32x4*>(sb + lds_off(c >> 3, c & 7)) = v;
+    }
+  } else {
+    constexpr int NBLK = C::BN / C::NW;
+    const int nb = tid % NBLK, kb = tid / NBLK;
+    const int* words = reinterpret_cast<const int*>(&st.b[0]);
+#pragma unroll
+    for (int j = 0; j < C::NW; ++j) {
+      i32x4 v;
+      if constexpr (C::ES == 2) {
+        // element (kr, j) is the 16-bit half j&1 of word kr*NW/2 + j/2
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w0 = (uint32_t)words[(2 * q) * (C::NW / 2) + j / 2];
+          const uint32_t w1 = (uint32_t)words[(2 * q + 1) * (C::NW / 2) + j / 2];
+          const uint32_t lo = (j & 1) ? (w0 >> 16) : (w0 & 0xFFFFu);
+          const uint32_t hi = (j & 1) ? (w1 & 0xFFFF0000u) : (w1 << 16);
+          v[q] = (int)(lo | hi);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = words[q * C::NW + j];
+      }
+      const int r = nb * C::NW + j;
+      *reinterpret_cast<i32x4*>(sb + lds_off(r, kb)) = v;
+    }
+  }
+}
+
+// acc[fm][fn] += A(wave rows fm) * B(wave cols fn) over one 128-byte K row.
+template <class C>
+__device__ inline void mma_tile(f32x4 (&acc)[C::FM][C::FN], const char* sa, const char* sb) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w / C::WN, wn = w % C::WN;
+  const int q = lane >> 4, r16 = lane & 15;
+  if constexpr (C::op == Op::FP8) {
+    i32x8 bf[C::FN];
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int r = wn * C::TN + fn * 16 + r16;
+      i32x4 lo = *reinterpret_cast<const i32x4*>(sb + lds_off(r, q));
+      i32x4 hi = *reinterpret_cast<const i32x4*>(sb + lds_off(r, q + 4));
+      bf[fn] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int r = wm * C::TM + fm * 16 + r16;
+      i32x4 lo = *reinterpret_cast<const i32x4*>(sa + lds_off(r, q));
+      i32x4 hi = *reinterpret_cast<const i32x4*>(sa + lds_off(r, q + 4));
+      i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[fn], acc[fm][fn],
+                                                                       0, 0, 0, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      i32x4 bfr[C::FN];
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) {
+        const int r = wn * C::TN + fn * 16 + r16;
+        bfr[fn] = *reinterpret_cast<const i32x4*>(sb + lds_off(r, q + 4 * kk));
+      }
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm) {
+        const int r = wm * C::TM + fm * 16 + r16;
+        const i32x4 af = *reinterpret_cast<const i32x4*>(sa + lds_off(r, q + 4 * kk));
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
+          if constexpr (C::op == Op::BF16) {
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, af), __builtin_bit_cast(bf16x8, bfr[fn]), acc[fm][fn],
+                0, 0, 0);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                  __int_as_float(af[j]), __int_as_float(bfr[fn][j]), acc[fm][fn], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <class C>
+__device__ inline void zero_item(const Params& p, long long begin, long long end) {
+  char* out = reinterpret_cast<char*>(p.out);
+  const i32x4 z = {0, 0, 0, 0};
+  for (long long off = begin + (long long)threadIdx.x * 16; off < end; off += (long long)C::T * 16)
+    *reinterpret_cast<i32x4*>(out + off) = z;
+}
+
+template <class C>
+__global__ __launch_bounds__(C::T) void gmm_kernel(Params p) {
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ Plan pl;
+  if (threadIdx.x == 0) pl.flags = 0;
+  __syncthreads();
+  build_plan<C::T>(p, pl, C::BM);
+  report_flags(p, pl);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / C::WN, wn = w % C::WN;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int M = p.M, N = p.N, K = p.K;
+  const int out_es = p.out_f32 ? 4 : 2;
+  const long long row_bytes = (long long)N * out_es;
+  const int n_ntiles = (N + C::BN - 1) / C::BN;
+  const long long n_gemm = (long long)pl.n_mtiles * n_ntiles;
+  const int lo_row = pl.row_start[0], hi_row = pl.row_start[pl.ga];
+  const long long z1_bytes = (long long)lo_row * row_bytes;
+  const long long z2_bytes = (long long)(M - hi_row) * row_bytes;
+  const long long z1 = (z1_bytes + kZeroChunk - 1) / kZeroChunk;
+  const long long z2 = (z2_bytes + kZeroChunk - 1) / kZeroChunk;
+  const long long n_items = n_gemm + z1 + z2;
+  const int KT = K / C::BK;
+  const int P = gridDim.x;
+  const int slot = xcd_slot(blockIdx.x, P);
+
+  for (long long L = slot; L < n_items; L += P) {
+    if (L >= n_gemm) {
+      long long z = L - n_gemm;
+      if (z < z1) {
+        long long b = z * kZeroChunk;
+        zero_item<C>(p, b, b + kZeroChunk < z1_bytes ? b + kZeroChunk : z1_bytes);
+      } else {
+        z -= z1;
+        long long base = (long long)hi_row * row_bytes;
+        long long b = base + z * kZeroChunk;
+        long long e = b + kZeroChunk;
+        long long end = base + z2_bytes;
+        zero_item<C>(p, b, e < end ? e : end);
+      }
+      continue;
+    }
+    const int t = (int)(L / n_ntiles);
+    const int j = (int)(L % n_ntiles);
+    const int h = find_group(pl, t);
+    const int row0 = pl.row_start[h] + (t - pl.tile_start[h]) * C::BM;
+    const int rows_left = pl.row_start[h + 1] - row0;
+    const int rows = rows_left < C::BM ? rows_left : C::BM;
+    const int n0 = j * C::BN;
+    const int ncols = N - n0 < C::BN ? N - n0 : C::BN;
+
+    const char* lhs = reinterpret_cast<const char*>(p.lhs) + (long long)row0 * K * C::ES;
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(lhs, (long long)rows * K * C::ES);
+    const char* rhs_h = reinterpret_cast<const char*>(p.rhs) + (long long)h * N * K * C::BSB;
+    __amdgpu_buffer_rsrc_t br;
+    if constexpr (C::NN)
+      br = make_rsrc(rhs_h, (long long)K * N * C::BSB);
+    else
+      br = make_rsrc(rhs_h + (long long)n0 * K * C::BSB, (long long)ncols * K * C::BSB);
+
+    f32x4 acc[C::FM][C::FN];
+    f32x4 tot[C::SCALED ? C::FM : 1][C::SCALED ? C::FN : 1];
+#pragma unroll
+    for (int a = 0; a < C::FM; ++a)
+#pragma unroll
+      for (int b = 0; b < C::FN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (C::SCALED) {
+#pragma unroll
+      for (int a = 0; a < C::FM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::FN; ++b) tot[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const C cfg{};
+    Stage<C> st;
+    load_tile(cfg, st, ar, br, 0, K, N, n0);
+    store_tile(cfg, st, smem, smem + C::A_BYTES);
+    __syncthreads();
+
+    const int kt_per_blk = C::SCALED ? p.blk / C::BK : 0;
+    float rs[C::SCALED ? C::FN : 1];
+    float ls[C::SCALED ? C::FM : 1][4];
+    for (int kt = 0; kt < KT; ++kt) {
+      char* sa = smem + (kt & 1) * (C::A_BYTES + C::B_BYTES);
+      char* sb = sa + C::A_BYTES;
+      if constexpr (C::SCALED) {
+        if (kt % kt_per_blk == 0) {
+          // this block's scales, read now and used when the block ends
+          const int b = kt / kt_per_blk;
+#pragma unroll
+          for (int fn = 0; fn < C::FN; ++fn) {
+            const int col = n0 + wn * C::TN + fn * 16 + r16;
+            rs[fn] = (p.rhs_scale && col < N) ? p.rhs_scale[((long long)h * p.nb + b) * N + col] : 1.f;
+          }
+#pragma unroll
+          for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = wm * C::TM + fm * 16 + 4 * q + i;
+              ls[fm][i] = (p.lhs_scale && r < rows) ? p.lhs_scale[(long long)(row0 + r) * p.nb + b] : 1.f;
+            }
+        }
+      }
+      if (kt + 1 < KT) load_tile(cfg, st, ar, br, kt + 1, K, N, n0);
+      mma_tile<C>(acc, sa, sb);
+      if constexpr (C::SCALED) {
+        if ((kt + 1) % kt_per_blk == 0) {
+#pragma unroll
+          for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) tot[fm][fn][i] += acc[fm][fn][i] * (rs[fn] * ls[fm][i]);
+              acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+      }
+      if (kt + 1 < KT) {
+        char* na = smem + ((kt + 1) & 1) * (C::A_BYTES + C::B_BYTES);
+        store_tile(cfg, st, na, na + C::A_BYTES);
+      }
+      __syncthreads();
+    }
+
+    // epilogue: bias, round, masked store
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int cl = wn * C::TN + fn * 16 + r16;
+      const int col = n0 + cl;
+      float bias = 0.f;
+      if (p.rhs_bias && cl < ncols) {
+        const long long bi = (long long)h * N + col;
+        bias = p.bias_f32 ? reinterpret_cast<const float*>(p.rhs_bias)[bi]
+                          : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.rhs_bias)[bi]);
+      }
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rl = wm * C::TM + fm * 16 + 4 * q + i;
+          if (rl < rows && cl < ncols) {
+            float v;
+            if constexpr (C::SCALED)
+              v = tot[fm][fn][i];
+            else
+              v = acc[fm][fn][i];
+            v += bias;
+            const long long oi = (long long)(row0 + rl) * N + col;
+            if (p.out_f32)
+              reinterpret_cast<float*>(p.out)[oi] = v;
+            else
+              reinterpret_cast<uint16_t*>(p.out)[oi] = f32_to_bf16_rne(v);
+          }
+        }
+    }
+  }
+}
+
+// The plan-building device code above, run on its own to export the tiles.
+__global__ __launch_bounds__(256) void worklist_kernel(Params p, int tm, int32_t* tiles,
+                                                       long long capacity, int32_t* count) {
+  __shared__ Plan pl;
+  if (threadIdx.x == 0) pl.flags = 0;
+  __syncthreads();
+  build_plan<256>(p, pl, tm);
+  for (int t = threadIdx.x; t < pl.n_mtiles; t += 256) {
+    if (t >= capacity) break;
+    const int h = find_group(pl, t);
+    const int row0 = pl.row_start[h] + (t - pl.tile_start[h]) * tm;
+    const int left = pl.row_start[h + 1] - row0;
+    tiles[3 * t + 0] = pl.s + h;
+    tiles[3 * t + 1] = row0;
+    tiles[3 * t + 2] = left < tm ? left : tm;
+  }
+  if (threadIdx.x == 0) {
+    count[0] = pl.n_mtiles;
+    count[1] = pl.row_start[0];
+    count[2] = pl.row_start[pl.ga];
+    count[3] = (int)pl.flags;
+  }
+}
+
+}  // namespace gmmk

@@ -1,0 +1,97 @@
+// gmm_kernels.hip -- instantiations of the gfx950 grouped-matmul kernel
+// family and their launchers.
+#include <atomic>
+
+#include "gmm_device.hpp"
+#include "gmm_launch.hpp"
+
+namespace gmmk {
+
+namespace {
+
+// Tile shapes.  Big: 256 x 128 output tile, four waves of 128 x 64 (for
+// large groups); with scales, eight waves of 64 x 64, since the per-block
+// partial and the running total both stay in registers.  Small: 32 x 64,
+// four waves of 32 x 16 (decode-sized groups).  F32 uses 64 x 64 tiles of
+// four 32 x 32 waves.
+template <Op OP, bool NN, bool BF8, bool SC, SizeClass SZ>
+struct Pick {
+  using type = Cfg<OP, NN, BF8, 256, 128, SC ? 4 : 2, 2, SC>;
+};
+template <Op OP, bool NN, bool BF8, bool SC>
+struct Pick<OP, NN, BF8, SC, SizeClass::Small> {
+  using type = Cfg<OP, NN, BF8, 32, 64, 1, 4, SC>;
+};
+
+template <class C>
+hipError_t launch_cfg(const Params& p, int cu_count, hipStream_t stream) {
+  static std::atomic<int> occ_cache{0};
+  int occ = occ_cache.load();
+  if (occ <= 0) {
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gmm_kernel<C>, C::T, 0);
+    if (e != hipSuccess) return e;
+    if (occ < 1) occ = 1;
+    occ_cache.store(occ);
+  }
+  // Upper bound on work items: group-aligned m-tiles are at most
+  // ceil(M/BM) + Ga, times the n-tiles, plus the zero-fill chunks.
+  const long long n_tiles = (p.N + C::BN - 1) / C::BN;
+  const long long m_tiles = (p.M + C::BM - 1) / C::BM + p.Ga;
+  const long long row_bytes = (long long)p.N * (p.out_f32 ? 4 : 2);
+  const long long zero_items = ((long long)p.M * row_bytes + kZeroChunk - 1) / kZeroChunk + 2;
+  const long long bound = m_tiles * n_tiles + zero_items;
+  long long grid = (long long)cu_count * occ;
+  if (grid > bound) grid = bound;
+  if (grid >= 8) grid -= grid % 8;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(gmm_kernel<C>, dim3((unsigned)grid), dim3(C::T), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <Op OP, bool NN, bool BF8, bool SC>
+hipError_t by_size(const Params& p, SizeClass sz, int cu, hipStream_t st) {
+  if constexpr (OP == Op::F32) return launch_cfg<Cfg<Op::F32, NN, false, 64, 64, 2, 2, SC>>(p, cu, st);
+  if (sz == SizeClass::Big) return launch_cfg<typename Pick<OP, NN, BF8, SC, SizeClass::Big>::type>(p, cu, st);
+  return launch_cfg<typename Pick<OP, NN, BF8, SC, SizeClass::Small>::type>(p, cu, st);
+}
+
+template <Op OP, bool NN, bool BF8>
+hipError_t by_scaled(const Params& p, const KernelChoice& c, int cu, hipStream_t st) {
+  if (c.scaled) return by_size<OP, NN, BF8, true>(p, c.size, cu, st);
+  return by_size<OP, NN, BF8, false>(p, c.size, cu, st);
+}
+
+}  // namespace
+
+int tile_m(const KernelChoice& c) {
+  if (c.op == Op::F32) return 64;
+  return c.size == SizeClass::Big ? 256 : 32;
+}
+
+hipError_t launch_gmm(const Params& p, const KernelChoice& c, int cu, hipStream_t st) {
+  switch (c.op) {
+    case Op::F32:
+      if (c.b_fp8) return hipErrorInvalidValue;
+      return c.nn ? by_scaled<Op::F32, true, false>(p, c, cu, st)
+                  : by_scaled<Op::F32, false, false>(p, c, cu, st);
+    case Op::BF16:
+      if (c.b_fp8) {
+        if (c.nn) return hipErrorInvalidValue;
+        return by_scaled<Op::BF16, false, true>(p, c, cu, st);
+      }
+      return c.nn ? by_scaled<Op::BF16, true, false>(p, c, cu, st)
+                  : by_scaled<Op::BF16, false, false>(p, c, cu, st);
+    case Op::FP8:
+      if (c.nn || c.b_fp8) return hipErrorInvalidValue;
+      return by_scaled<Op::FP8, false, false>(p, c, cu, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_worklist(const Params& p, int tm, int32_t* tiles, long long capacity,
+                           int32_t* count, hipStream_t stream) {
+  hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(256), 0, stream, p, tm, tiles, capacity, count);
+  return hipGetLastError();
+}
+
+}  // namespace gmmk

@@ -1,0 +1,34 @@
+// gmm_launch.hpp -- host-side launch entry points of the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gmm_params.hpp"
+
+namespace gmmk {
+
+enum class SizeClass { Small = 0, Big = 1 };
+
+struct KernelChoice {
+  Op op;
+  bool nn;      // rhs [Ga,K,N]
+  bool b_fp8;   // e4m3 rhs widened to bf16 operands
+  bool scaled;  // rhs_scale and/or lhs_scale present
+  SizeClass size;
+};
+
+// K elements of one K tile for an operand type (the K granularity).
+inline int k_tile(Op op) { return op == Op::F32 ? 32 : (op == Op::BF16 ? 64 : 128); }
+
+// m-tile height the kernel uses for this choice.
+int tile_m(const KernelChoice& c);
+
+// Queue the gmm kernel.  Returns hipSuccess or the launch error.
+hipError_t launch_gmm(const Params& p, const KernelChoice& c, int cu_count, hipStream_t stream);
+
+// Queue the worklist export kernel (one workgroup).
+hipError_t launch_worklist(const Params& p, int tm, int32_t* tiles, long long capacity,
+                           int32_t* count, hipStream_t stream);
+
+}  // namespace gmmk

@@ -1,0 +1,35 @@
+// gmm_params.hpp -- kernel arguments and constants shared by the host
+// launchers and the device code of the gfx950 grouped matmul.
+#pragma once
+
+#include <stdint.h>
+
+namespace gmmk {
+
+// Operand type fed to the matrix cores.
+enum class Op { F32, BF16, FP8 };
+
+constexpr int kMaxGroups = 1024;
+constexpr uint32_t kFlagNegative = 0x1u;
+constexpr uint32_t kFlagExceed = 0x2u;
+constexpr uint32_t kFlagBadOffset = 0x4u;
+// Bytes of inactive rows zeroed by one work item.
+constexpr int kZeroChunk = 64 * 1024;
+// dword 3 of a raw buffer resource on gfx9-family parts (32-bit data format).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+struct Params {
+  const void* lhs;
+  const void* rhs;
+  const int32_t* group_sizes;
+  const int32_t* group_offset;  // device scalar or nullptr
+  const float* rhs_scale;       // [Ga, nb, 1, N] or nullptr
+  const void* rhs_bias;         // [Ga, 1, N] or nullptr
+  const float* lhs_scale;       // [M, nb] or nullptr
+  void* out;                    // [M, N]
+  uint32_t* flags;
+  int32_t M, K, N, G, Ga, nb, blk;
+  int32_t bias_f32, out_f32;
+};
+
+}  // namespace gmmk

@@ -1,0 +1,236 @@
+"""HIP path against the oracle, element by element, at sizes the oracle
+finishes in seconds (several tiles in M, N and K, ragged group boundaries,
+empty groups, an N tail), for every dtype path and both tile families.
+Also the probes that must hold bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import (active_range, assert_zero_rows, compare, reference, run_gpu)
+
+pytestmark = pytest.mark.gpu
+
+POLICIES = [("auto", 0), ("small", 1), ("big", 2)]
+
+
+@pytest.fixture(params=POLICIES, ids=[p[0] for p in POLICIES])
+def tile_policy(request):
+    import moe_grouped_matrix_amd as m
+    m.set_tile_policy(request.param[1])
+    yield request.param[1]
+    m.set_tile_policy(0)
+
+
+@pytest.mark.parametrize("name", list(workloads.SMALL))
+def test_small_workloads_all_elements(name, tile_policy):
+    case = workloads.SMALL[name]().to("cuda")
+    print(f"case {name} policy {tile_policy} M={case.M} K={case.K} N={case.N} "
+          f"G={case.group_sizes.numel()} Ga={case.num_active}", flush=True)
+    out = run_gpu(case)
+    ref = reference(case)
+    lo, hi = active_range(case)
+    assert_zero_rows(out, lo, hi)
+    compare(out.cpu()[lo:hi], ref[lo:hi], case.out_dtype, name)
+    import moe_grouped_matrix_amd as m
+    assert m.device_flags() == 0
+
+
+def _case(lhs, rhs, sizes, **kw):
+    return workloads.Case("probe", lhs.cuda(), rhs.cuda(),
+                          torch.tensor(sizes, dtype=torch.int32, device="cuda"),
+                          **{k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in kw.items()})
+
+
+PATHS = [
+    # (lhs dtype, rhs dtype, transpose_rhs, K granule)
+    (torch.float32, torch.float32, False, 32),
+    (torch.float32, torch.float32, True, 32),
+    (torch.bfloat16, torch.bfloat16, False, 64),
+    (torch.bfloat16, torch.bfloat16, True, 64),
+    (torch.bfloat16, torch.float8_e4m3fn, False, 64),
+    (torch.float8_e4m3fn, torch.float8_e4m3fn, False, 128),
+]
+PATH_IDS = ["f32_nt", "f32_nn", "bf16_nt", "bf16_nn", "bf16xe4m3_nt", "e4m3xe4m3_nt"]
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_bias_probe_maps_every_row_to_its_group(path, tile_policy):
+    """rhs = 0 and bias[g] = g+1 (exact in bf16): every active row must read
+    exactly its group's number, every other row 0."""
+    ld, rd, T, kg = path
+    sizes = [0, 37, 1, 0, 64, 65, 3, 0, 255, 2]
+    M, K, N = sum(sizes) + 21, 2 * kg, 136
+    Ga = len(sizes) - 2
+    lhs = torch.randn(M, K).to(ld)
+    rhs = torch.zeros(Ga, K, N) if T else torch.zeros(Ga, N, K)
+    bias = (torch.arange(Ga, dtype=torch.float32) + 3)[:, None, None].expand(Ga, 1, N).contiguous()
+    for bias_dtype in (torch.float32, torch.bfloat16):
+        case = _case(lhs, rhs.to(rd), sizes, group_offset=1, transpose_rhs=T,
+                     rhs_bias=bias.to(bias_dtype), out_dtype=torch.float32)
+        out = run_gpu(case).cpu()
+        ref, rg = reference(case, return_row_group=True)
+        assert torch.equal(out, oracle.round_to(ref, torch.float32))
+        want = np.where(rg >= 0, rg - 1 + 3, 0).astype(np.float64)
+        assert np.array_equal(out[:, 0].numpy(), want)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_exact_small_integer_inputs_are_bit_exact(path, tile_policy):
+    """Small integers make every product and partial sum exact in fp32, so the
+    rounded outputs must equal the oracle's bit for bit, whatever the order."""
+    ld, rd, T, kg = path
+    g = torch.Generator().manual_seed(1)
+    sizes = [33, 0, 70, 257, 5]
+    M, K, N = sum(sizes) + 7, 4 * kg, 200
+    lhs = torch.randint(-3, 4, (M, K), generator=g).to(torch.float32).to(ld)
+    shape = (len(sizes), K, N) if T else (len(sizes), N, K)
+    rhs = torch.randint(-3, 4, shape, generator=g).to(torch.float32).to(rd)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        case = _case(lhs, rhs, sizes, transpose_rhs=T, out_dtype=out_dtype)
+        out = run_gpu(case).cpu()
+        want = oracle.round_to(reference(case), out_dtype)
+        assert torch.equal(out.view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32),
+                           want.view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32))
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_scaled_exact_inputs_are_bit_exact(path, tile_policy):
+    """Power-of-two block scales, per-row scales and a bias keep the integer
+    arithmetic exact: bit-exact against the oracle."""
+    ld, rd, T, kg = path
+    if T:
+        pytest.skip("scaled NN uses the same fold as NT; covered by the NT paths")
+    g = torch.Generator().manual_seed(2)
+    sizes = [40, 0, 90, 3]
+    nb = 3
+    M, K, N = sum(sizes) + 5, nb * (128 if kg == 128 else 2 * kg), 72
+    lhs = torch.randint(-3, 4, (M, K), generator=g).to(torch.float32).to(ld)
+    rhs = torch.randint(-3, 4, (len(sizes), N, K), generator=g).to(torch.float32).to(rd)
+    rs = 2.0 ** torch.randint(-3, 4, (len(sizes), nb, 1, N), generator=g).to(torch.float32)
+    ls = 2.0 ** torch.randint(-2, 3, (M, nb), generator=g).to(torch.float32)
+    bias = torch.randint(-8, 9, (len(sizes), 1, N), generator=g).to(torch.bfloat16)
+    for kw in (dict(rhs_scale=rs), dict(rhs_scale=rs, rhs_bias=bias), dict(lhs_scale=ls),
+               dict(rhs_scale=rs, lhs_scale=ls, rhs_bias=bias)):
+        case = _case(lhs, rhs, sizes, out_dtype=torch.float32, **kw)
+        out = run_gpu(case).cpu()
+        assert torch.equal(out, oracle.round_to(reference(case), torch.float32)), list(kw)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_transpose_identity(dtype, tile_policy):
+    """gmm(L, W, transpose_rhs) == gmm(L, W^T) on the explicitly transposed
+    weight: the NN path stages the same operands, so the bits agree."""
+    g = torch.Generator().manual_seed(3)
+    sizes = [100, 0, 300, 17]
+    M, K, N = 430, 192, 264
+    lhs = torch.randn(M, K, generator=g).to(dtype)
+    w = torch.randn(len(sizes), K, N, generator=g).to(dtype)
+    nn = run_gpu(_case(lhs, w, sizes, transpose_rhs=True, out_dtype=torch.float32))
+    nt = run_gpu(_case(lhs, w.transpose(1, 2).contiguous(), sizes, out_dtype=torch.float32))
+    assert torch.equal(nn, nt)
+
+
+def test_identity_probe_power_of_two():
+    """W_g = 2^j_g * I reproduces the rows times 2^j_g exactly (NT and NN)."""
+    sizes = [20, 0, 45, 7]
+    M, K = 80, 128
+    lhs = torch.randn(M, K).to(torch.bfloat16)
+    eye = torch.eye(K)
+    w = torch.stack([eye * 2.0 ** j for j in (-2, 5, 0, 3)]).to(torch.bfloat16)
+    for T in (False, True):
+        out = run_gpu(_case(lhs, w, sizes, transpose_rhs=T, out_dtype=torch.bfloat16)).cpu()
+        o = np.concatenate([[0], np.cumsum(sizes)])
+        for gi, j in enumerate((-2, 5, 0, 3)):
+            a, b = o[gi], o[gi + 1]
+            assert torch.equal(out[a:b].float(), lhs[a:b].float() * 2.0 ** j)
+        assert torch.all(out[o[-1]:] == 0)
+
+
+def test_brute_force_tiny_compositions():
+    """Many small compositions of rows into groups, including zero groups and
+    sizes one either side of the tile heights, for both tile families."""
+    import moe_grouped_matrix_amd as m
+    rng = np.random.default_rng(4)
+    K, N = 64, 64
+    for policy in (1, 2):
+        m.set_tile_policy(policy)
+        try:
+            for trial in range(40):
+                G = int(rng.integers(1, 6))
+                sizes = [int(x) for x in rng.choice([0, 1, 2, 31, 32, 33, 63, 255, 256, 257], size=G)]
+                M = sum(sizes) + int(rng.integers(0, 3))
+                if M == 0:
+                    continue
+                s = int(rng.integers(0, G))
+                ga = int(rng.integers(0, G - s + 1))
+                lhs = torch.randn(M, K).to(torch.bfloat16)
+                rhs = torch.randn(max(ga, 0), N, K).to(torch.bfloat16)
+                case = _case(lhs, rhs, sizes, group_offset=s, out_dtype=torch.float32)
+                print(f"brute policy={policy} sizes={sizes} s={s} ga={ga}", flush=True)
+                out = run_gpu(case).cpu()
+                ref = reference(case)
+                assert np.allclose(out.numpy(), ref, rtol=1e-5, atol=1e-4)
+                lo, hi = active_range(case)
+                assert_zero_rows(out, lo, hi)
+        finally:
+            m.set_tile_policy(0)
+
+
+def test_no_active_group_writes_zeros_everywhere():
+    sizes = [10, 20, 5]
+    lhs = torch.randn(40, 64).to(torch.bfloat16)
+    for s in range(4):
+        case = _case(lhs, torch.zeros(0, 32, 64).to(torch.bfloat16), sizes, group_offset=s,
+                     out_dtype=torch.bfloat16)
+        out = torch.full((40, 32), 7.0, dtype=torch.bfloat16, device="cuda")
+        import moe_grouped_matrix_amd as m
+        m.gmm(case.lhs, case.rhs, case.group_sizes, group_offset=s, out=out)
+        torch.cuda.synchronize()
+        assert int((out.view(torch.int16) != 0).sum()) == 0
+
+
+def test_single_group_is_dense_matmul():
+    g = torch.Generator().manual_seed(5)
+    lhs = torch.randn(300, 256, generator=g).to(torch.bfloat16)
+    w = torch.randn(1, 136, 256, generator=g).to(torch.bfloat16)
+    out = run_gpu(_case(lhs, w, [300], out_dtype=torch.float32)).cpu().double()
+    want = lhs.double() @ w[0].double().t()
+    assert (out - want).abs().max() <= 1e-4 * want.abs().max()
+
+
+def test_invalid_device_data_is_flagged_and_in_bounds():
+    import moe_grouped_matrix_amd as m
+    m.device_flags()
+    lhs = torch.randn(64, 64).to(torch.bfloat16).cuda()
+    rhs = torch.randn(3, 32, 64).to(torch.bfloat16).cuda()
+    for sizes, off, flag in (([10, -5, 20], None, m.FLAG_NEGATIVE_SIZE),
+                             ([40, 40, 40], None, m.FLAG_SIZES_EXCEED_M)):
+        gs = torch.tensor(sizes, dtype=torch.int32, device="cuda")
+        out = m.gmm(lhs, rhs, gs, group_offset=off)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
+        assert m.device_flags() & flag
+    gs = torch.tensor([10, 10, 10, 10], dtype=torch.int32, device="cuda")
+    m.gmm(lhs, rhs, gs, group_offset=2)
+    assert m.device_flags() & m.FLAG_BAD_OFFSET
+
+
+def test_host_validation_errors():
+    import moe_grouped_matrix_amd as m
+    lhs = torch.randn(16, 64).to(torch.bfloat16).cuda()
+    rhs = torch.randn(2, 32, 64).to(torch.bfloat16).cuda()
+    gs = torch.tensor([8, 8], dtype=torch.int32, device="cuda")
+    with pytest.raises(m.GmmInvalid):
+        m.gmm(lhs, rhs[:, :, :32].contiguous(), gs)
+    with pytest.raises(m.GmmInvalid):
+        m.gmm(lhs, rhs, gs.to(torch.float32))
+    with pytest.raises(m.GmmInvalid):
+        m.gmm(lhs, rhs, gs, rhs_bias=torch.zeros(2, 1, 31, device="cuda"))
+    with pytest.raises(m.GmmUnsupported):
+        m.gmm(lhs[:, :48].contiguous(), rhs[:, :, :48].contiguous(), gs)
+    with pytest.raises(m.GmmUnsupported):
+        m.gmm(lhs, rhs.to(torch.float8_e4m3fn).transpose(1, 2).contiguous(), gs, transpose_rhs=True)
+    with pytest.raises(m.GmmUnsupported):
+        m.gmm(lhs.float(), rhs, gs)
