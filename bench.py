@@ -1,0 +1,247 @@
+"""Benchmark of the grouped matmul on one MI355X.
+
+A step is one pass of the whole hot path for a 128-expert top-8 MoE layer in
+bf16: the up-projection forward gmm (lhs [262144,1408] x rhs [128,1408,1408],
+an NT product) followed by the down-projection backward dlhs gmm (dout
+[262144,1408] x the forward weight [128,1408,704] read in place, an NN
+product).  Each gmm call is one kernel launch that builds the group offsets
+and tile table, zero-fills inactive rows and runs the MFMA tiles.  Inputs are
+seeded synthetic tensors already resident in HBM.
+
+Prints one JSON line: TFLOP/s over the timed steps (algorithmic FLOPs, i.e.
+2 * active rows * N * K), the roofline of the dominant kernel measured with
+HIP events on the launch stream, and the CPU oracle timed on a bounded sample
+of the same workload.
+
+  python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # dense MFMA TFLOP/s (MI355X)
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "moe_grouped_matrix_amd", "csrc", f)
+                  for f in ("gmm_device.hpp", "gmm_params.hpp", "gmm_kernels.hip")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None
+    when there are none for this workload or the kernels changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def build_cases(workload: str, device):
+    import workloads
+    names = {"fwd+dlhs": ["moe_fwd_bf16", "moe_dlhs_bf16"]}.get(workload, [workload])
+    return [workloads.FULL[n](device=device) for n in names]
+
+
+def op_peak(case):
+    import torch
+    if case.lhs.dtype == torch.float8_e4m3fn:
+        return "fp8", PEAK["fp8"]
+    if case.lhs.dtype == torch.float32:
+        return "f32", PEAK["f32"]
+    return "bf16", PEAK["bf16"]
+
+
+def cpu_baseline(cases, target_s: float = 12.0):
+    """Time the oracle on a bounded sample of each case: a few rows of a few
+    groups, packed into a sub-problem with the same K, N and weights (every
+    row costs the same arithmetic as in the full problem)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+
+    oracle.build(force=False)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    flops_total = 0.0
+    secs_total = 0.0
+    descr = []
+    # calibrate on a handful of rows, then size the sample to ~target_s
+    rows_per = 4
+    for phase in ("calibrate", "measure"):
+        flops_total = secs_total = 0.0
+        descr = []
+        for case in cases:
+            sizes = case.sizes_list()
+            groups = [g for g in range(case.group_offset, case.group_offset + case.num_active)
+                      if sizes[g] > 0][:32]
+            o = np.concatenate([[0], np.cumsum(sizes)])
+            idx, sub_sizes = [], []
+            for g in groups:
+                n = min(rows_per, sizes[g])
+                idx.extend(range(int(o[g]), int(o[g]) + n))
+                sub_sizes.append(n)
+            idx_t = torch.tensor(idx, device=case.lhs.device)
+            h_idx = torch.tensor([g - case.group_offset for g in groups], device=case.lhs.device)
+            sub = workloads.Case(
+                case.name, case.lhs.index_select(0, idx_t).cpu(), case.rhs.index_select(0, h_idx).cpu(),
+                torch.tensor(sub_sizes, dtype=torch.int32), transpose_rhs=case.transpose_rhs,
+                rhs_scale=None if case.rhs_scale is None else case.rhs_scale.index_select(0, h_idx).cpu(),
+                rhs_bias=None if case.rhs_bias is None else case.rhs_bias.index_select(0, h_idx).cpu(),
+                lhs_scale=None if case.lhs_scale is None else case.lhs_scale.index_select(0, idx_t).cpu(),
+                out_dtype=case.out_dtype)
+            t0 = time.perf_counter()
+            oracle.gmm_reference(sub.lhs, sub.rhs, sub.group_sizes, transpose_rhs=sub.transpose_rhs,
+                                 rhs_scale=sub.rhs_scale, rhs_bias=sub.rhs_bias, lhs_scale=sub.lhs_scale)
+            secs_total += time.perf_counter() - t0
+            flops_total += 2.0 * len(idx) * case.N * case.K
+            descr.append(f"{case.name}: {len(idx)} rows of {len(groups)} groups")
+        if phase == "calibrate":
+            scale = target_s / max(secs_total, 1e-3)
+            rows_per = max(1, int(rows_per * scale))
+    return {"value": flops_total / secs_total / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "; ".join(descr) + f" (fp64 oracle, {secs_total:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fwd+dlhs",
+                    help="fwd+dlhs (default) or one of tiny_fp32, moe_fwd_bf16, moe_dlhs_bf16, "
+                         "decode_fp8w, w8a8_fp8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import moe_grouped_matrix_amd as gmm_amd
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cases = build_cases(args.workload, dev)
+    outs = [torch.empty((c.M, c.N), dtype=c.out_dtype, device=dev) for c in cases]
+    offs = [torch.tensor([c.group_offset], dtype=torch.int32, device=dev) if c.group_offset else None
+            for c in cases]
+    stream = torch.cuda.current_stream(dev)
+
+    def launch(i):
+        c = cases[i]
+        gmm_amd.gmm(c.lhs, c.rhs, c.group_sizes, rhs_scale=c.rhs_scale, rhs_bias=c.rhs_bias,
+                    lhs_scale=c.lhs_scale, group_offset=offs[i], transpose_rhs=c.transpose_rhs,
+                    out=outs[i])
+
+    for _ in range(args.warmup):
+        for i in range(len(cases)):
+            launch(i)
+    torch.cuda.synchronize()
+    if gmm_amd.device_flags() != 0:
+        raise RuntimeError("device data flags set")
+
+    # HIP events around every launch of the timed steps, on the launch stream.
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in cases] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i in range(len(cases)):
+            ev[s][i][0].record(stream)
+            launch(i)
+            ev[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_kernel_ms = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+                     for i in range(len(cases))]
+    flops = [c.flops() for c in cases]
+    step_flops = sum(flops)
+    value = step_flops * args.steps / wall / 1e12
+
+    # dominant kernel: the case with the largest total event time
+    tot = [sum(x) for x in per_kernel_ms]
+    d = max(range(len(cases)), key=lambda i: tot[i])
+    dc = cases[d]
+    avg_ms = statistics.mean(per_kernel_ms[d])
+    kind, peak = op_peak(dc)
+    mem_bound = dc.name == "decode_fp8w"
+    if mem_bound:
+        achieved = dc.algorithmic_bytes() / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        achieved = flops[d] / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak}
+    roof["traffic"] = measured_traffic(dc.name)
+    roof["kernel"] = dc.name
+    roof["avg_launch_ms"] = avg_ms
+
+    detail = {}
+    for i, c in enumerate(cases):
+        ms = statistics.median(per_kernel_ms[i])
+        k, pk = op_peak(c)
+        detail[c.name] = {"median_ms": ms, "tflops": flops[i] / (ms * 1e-3) / 1e12,
+                          "frac_peak": flops[i] / (ms * 1e-3) / 1e12 / pk,
+                          "gbs_algorithmic": c.algorithmic_bytes() / (ms * 1e-3) / 1e9,
+                          "active_rows": c.active_rows()}
+
+    metric = ("grouped-GEMM TFLOP/s and % MFMA peak, 128-expert bf16 fwd+dlhs"
+              if args.workload == "fwd+dlhs" else f"grouped-GEMM TFLOP/s, {args.workload}")
+    line = {
+        "metric": metric,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3", "f32": "f32"}[op_peak(cases[0])[0]]
+        if not any(c.rhs.dtype == torch.float8_e4m3fn and c.lhs.dtype == torch.bfloat16 for c in cases)
+        else "bf16 x fp8-e4m3",
+        "data": "synthetic (seeded; router group sizes, normal values)",
+        "config": {"workload": " + ".join(c.name for c in cases),
+                   "shapes": [{"M": c.M, "K": c.K, "N": c.N, "G": int(c.group_sizes.numel()),
+                               "Ga": c.num_active, "transpose_rhs": c.transpose_rhs} for c in cases],
+                   "frac_of_peak": value / PEAK[op_peak(cases[0])[0]]},
+        "roofline": roof,
+        "detail": detail,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cases)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
