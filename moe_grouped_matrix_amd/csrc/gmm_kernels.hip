@@ -2,6 +2,7 @@
 // family and their launchers.
 #include <atomic>
 
+#include "gmm_big.hpp"
 #include "gmm_device.hpp"
 #include "gmm_launch.hpp"
 
@@ -48,9 +49,27 @@ hipError_t launch_cfg(const Params& p, int cu_count, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <class C>
+hipError_t launch_big(const Params& p, int cu_count, hipStream_t stream) {
+  const long long n_tiles = (p.N + C::BN - 1) / C::BN;
+  const long long m_tiles = (p.M + C::BM - 1) / C::BM + p.Ga;
+  long long grid = cu_count;  // one 256-thread workgroup per CU (LDS-bound)
+  if (grid > m_tiles * n_tiles && m_tiles * n_tiles >= 8) grid = m_tiles * n_tiles;
+  if (grid >= 8) grid -= grid % 8;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(gmm_big_kernel<C>, dim3((unsigned)grid), dim3(C::T), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <Op OP, bool NN, bool BF8, bool SC>
 hipError_t by_size(const Params& p, SizeClass sz, int cu, hipStream_t st) {
   if constexpr (OP == Op::F32) return launch_cfg<Cfg<Op::F32, NN, false, 64, 64, 2, 2, SC>>(p, cu, st);
+  if constexpr (OP == Op::BF16 && !BF8 && !SC) {
+    if (sz == SizeClass::Big) {
+      if (p.out_f32) return launch_big<BigCfg<NN, true>>(p, cu, st);
+      return launch_big<BigCfg<NN, false>>(p, cu, st);
+    }
+  }
   if (sz == SizeClass::Big) return launch_cfg<typename Pick<OP, NN, BF8, SC, SizeClass::Big>::type>(p, cu, st);
   return launch_cfg<typename Pick<OP, NN, BF8, SC, SizeClass::Small>::type>(p, cu, st);
 }
