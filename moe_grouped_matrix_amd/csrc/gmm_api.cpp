@@ -11,7 +11,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/gmm.h"
+#include "gmm.h"
 #include "gmm_launch.hpp"
 
 struct gmm_handle {

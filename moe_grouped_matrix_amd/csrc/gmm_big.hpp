@@ -9,9 +9,10 @@
 // half a tile of MFMA work.
 //
 // K is consumed 32 at a time.  A K tile of both operands (256 rows x 64 bytes
-// each, 32 KB) sits in one of four LDS stages that form a ring: while the
-// waves multiply one stage, the next three -- of the same output tile, or the
-// first ones of the workgroup's next output tile -- are in flight.  Operands
+// each, 32 KB) sits in one of four LDS stages that form a ring.  While the
+// waves multiply step s (fragments already in registers), they read step
+// s+1's fragments from LDS, and steps s+2..s+4 -- of the same output tile, or
+// the first ones of the workgroup's next output tile -- are in flight.  Operands
 // reach LDS by direct-to-LDS buffer loads (no staging registers), except a
 // [G,K,N] weight, which goes through registers to be transposed to the
 // K-contiguous layout the MFMA operands need.
@@ -164,6 +165,21 @@ __device__ __forceinline__ BigSrc big_src(const Params& p, const BigItem& it) {
   return s;
 }
 
+// Queue the direct-to-LDS loads of K step kt (both operands when NT, lhs
+// only when NN) into LDS stage `st`; voff are this lane's row offsets.
+template <class C>
+__device__ __forceinline__ void dma_stage(const BigSrc& src, const int (&voff)[C::DMA_PER_OPERAND], int kt,
+                                          char* st, int w) {
+#pragma unroll
+  for (int i = 0; i < C::DMA_PER_OPERAND; ++i) {
+    char* dst = st + (w * C::ROWS_PER_WAVE + i * 16) * C::ROW;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.a, (lds_ptr_t)dst, 16, voff[i], kt * C::ROW, 0, 0);
+    if constexpr (!C::NN)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src.b, (lds_ptr_t)(dst + C::A_BYTES), 16, voff[i], kt * C::ROW,
+                                               0, 0);
+  }
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt low bits [3:0], high bits [15:14]; expcnt [6:4] and lgkmcnt [11:8]
 // left at their maxima).
@@ -173,63 +189,24 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Wait until at most n vector-memory loads of this wave are outstanding,
-// rounding n down to a supported immediate (waiting longer is always safe).
-__device__ __forceinline__ void wait_loads_at_most(int n) {
-  if (n >= 32)
-    wait_vmcnt<32>();
-  else if (n >= 24)
-    wait_vmcnt<24>();
-  else if (n >= 16)
-    wait_vmcnt<16>();
-  else if (n >= 12)
-    wait_vmcnt<12>();
-  else if (n >= 8)
-    wait_vmcnt<8>();
-  else if (n >= 4)
-    wait_vmcnt<4>();
-  else
-    wait_vmcnt<0>();
-}
-
-// Position in a workgroup's stream of K steps: item L (linear tile index),
-// its K tile kt, and the decoded item.
-struct Cursor {
-  int step;
-  int L;
-  int kt;
-  BigItem it;
-};
+// Fragment rows start at multiples of 16, so a fragment's swizzled chunk
+// depends only on the lane: lane (q, r16) reads row base + r16, chunk
+// q ^ swz64(r16).  Fragment f of a wave is then one base address plus an
+// immediate f * 16 rows.  (Rows past a half tile's share may run into the B
+// part of the stage: they are read, never used.)
+__device__ __forceinline__ int frag_lane_off(int q, int r16) { return r16 * 64 + ((q ^ swz64(r16)) << 4); }
 
 template <class C>
-__device__ __forceinline__ void advance(Cursor& c, const Plan& pl, int KT, int P, int n_items, int n_ntiles,
-                                        int N, int w) {
-  ++c.step;
-  if (++c.kt == KT) {
-    c.kt = 0;
-    c.L += P;
-    if (c.L < n_items) c.it = decode_big<C>(pl, c.L, n_ntiles, N, w);
-  }
+__device__ __forceinline__ void read_a_at(i32x4& a, const char* base, int fm) {
+  a = *reinterpret_cast<const i32x4*>(base + fm * 16 * C::ROW);
 }
 
 template <class C>
-__device__ __forceinline__ void read_frags(i32x4 (&a)[C::FM], i32x4 (&b)[C::FN], const char* stage,
-                                           const BigItem& it, int q, int r16) {
-  // Rows past a half tile's share are read too (wrapped into the tile; the
-  // values are never used): unconditional reads keep the LDS queue full.
+__device__ __forceinline__ void read_b_at(i32x4 (&b)[C::FN], const char* base) {
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm)
-    a[fm] = *reinterpret_cast<const i32x4*>(stage + lds_off64((it.rbase + fm * 16 + r16) & (C::BM - 1), q));
-  const char* sb = stage + C::A_BYTES;
-#pragma unroll
-  for (int fn = 0; fn < C::FN; ++fn)
-    b[fn] = *reinterpret_cast<const i32x4*>(sb + lds_off64(it.cbase + fn * 16 + r16, q));
+  for (int fn = 0; fn < C::FN; ++fn) b[fn] = *reinterpret_cast<const i32x4*>(base + fn * 16 * C::ROW);
 }
 
-// acc[fm][fn] += a[fm] b[fn] for F0 <= fm < F1.  Half tiles run rows
-// [0, FM/2) only; one conditional block for the upper rows keeps the
-// accumulators in place (finer branching makes the register allocator copy
-// them around).
 template <class C, int F0, int F1>
 __device__ __forceinline__ void mfma_rows(f32x4 (&acc)[C::FM][C::FN], const i32x4 (&a)[C::FM],
                                           const i32x4 (&b)[C::FN]) {
@@ -316,130 +293,142 @@ void gmm_big_kernel(Params p) {
 
   const int n_ntiles = (N + C::BN - 1) / C::BN;
   const int n_items = __builtin_amdgcn_readfirstlane(pl.n_mtiles) * n_ntiles;
-  const int KT = K / C::BK;
+  const int KT = K / C::BK;  // K steps per item; the launcher guarantees KT >= S
   if (slot >= n_items) return;
-  // This workgroup's items are slot, slot + P, ...; their K tiles form one
-  // stream of `total` steps.
-  const int total = (n_items - slot + P - 1) / P * KT;
 
-  Cursor first;
-  first.step = 0;
-  first.L = slot;
-  first.kt = 0;
-  first.it = decode_big<C>(pl, slot, n_ntiles, N, w);
+  // This workgroup's items are slot, slot + P, ...; their K steps form one
+  // stream.  Loads run S steps ahead of the multiplication, fragment reads
+  // one step ahead, NN weight loads two steps ahead -- within the current
+  // item or, near its end, in the next one.
+  BigItem cur = decode_big<C>(pl, slot, n_ntiles, N, w);
+  int cur_L = slot;
+  BigItem nxt = cur;
+  if (slot + P < n_items) nxt = decode_big<C>(pl, slot + P, n_ntiles, N, w);
+  BigSrc cur_src = big_src<C>(p, cur), nxt_src = big_src<C>(p, nxt);
 
-  // Loads per step and wave: DMA_A (+ DMA_B when NT) direct-to-LDS, plus 8
-  // register loads of the weight when NN.  Loads retire in order, so "all
-  // loads up to step x's have landed" is "at most <loads issued after
-  // them> outstanding".
-  constexpr int DMA_A = C::DMA_PER_OPERAND;
-  constexpr int DMA_STEP = C::NN ? DMA_A : 2 * DMA_A;
-  constexpr int NN_STEP = C::NN_LOADS;
-
-  Cursor ld = first;  // next step whose operands go to LDS
-  BigSrc ld_src = big_src<C>(p, ld.it);
-  auto issue = [&]() __attribute__((always_inline)) {
-    char* st = smem + (ld.step % C::S) * C::STAGE;
-    dma_rows<C>(ld_src.a, K * 2, ld.kt, st);
-    if constexpr (!C::NN) dma_rows<C>(ld_src.b, K * 2, ld.kt, st + C::A_BYTES);
-    const int old_L = ld.L;
-    advance<C>(ld, pl, KT, P, n_items, n_ntiles, N, w);
-    if (ld.L != old_L && ld.step < total) ld_src = big_src<C>(p, ld.it);
+  // Per-lane byte offsets of this wave's direct-to-LDS rows (the K step adds
+  // a scalar offset): operand rows r = 16 i + lane/4 of the wave's share.
+  const int row_bytes = K * 2;
+  int dma_voff[C::DMA_PER_OPERAND];
+#pragma unroll
+  for (int i = 0; i < C::DMA_PER_OPERAND; ++i) {
+    const int r = w * C::ROWS_PER_WAVE + i * 16 + (lane >> 2);
+    dma_voff[i] = r * row_bytes + (((lane & 3) ^ swz64(r)) << 4);
+  }
+  auto dma = [&](const BigSrc& src, int kt, int stage) __attribute__((always_inline)) {
+    dma_stage<C>(src, dma_voff, kt, smem + stage * C::STAGE, w);
   };
-
-  // NN: the weight part of step x goes through registers: loaded in the
-  // iteration of step x-1, written to LDS at its end.  nn_step is the next
-  // such step; it is always cur.step + 1 once the loop runs.
-  int nn_step = 0;
   int nb[8 * C::NWN / 2];
   auto nn_load_for = [&](const BigItem& it, int kt) __attribute__((always_inline)) {
     const char* rhs_h = reinterpret_cast<const char*>(p.rhs) + (long long)it.h * N * K * 2;
     nn_load<C>(make_rsrc(rhs_h, (long long)K * N * 2), N, it.n0, kt, nb);
   };
-  auto nn_store_for = [&](int step) __attribute__((always_inline)) {
-    nn_store<C>(nb, smem + (step % C::S) * C::STAGE + C::A_BYTES);
-  };
 
-  // Loads issued after the DMA of step x, as of the top of the iteration of
-  // step x.  DMA(x) is issued in the prologue when x < S, else in the
-  // iteration of step x-S+1 (refilling the stage read in step x-S), after
-  // that iteration's NN loads.
-  auto newer_than = [&](int x) __attribute__((always_inline)) {
-    int n = DMA_STEP * (ld.step - x - 1);
-    if constexpr (C::NN) {
-      // NN loads of step y are issued in the iteration of step y-1 (step 0's
-      // in the prologue, after its DMAs); those after DMA(x) are y >= y0.
-      const int y0 = x < C::S ? 0 : x - C::S + 3;
-      n += NN_STEP * (nn_step - y0 > 0 ? nn_step - y0 : 0);
-    }
-    return n;
-  };
-
-  // Prologue: S stages in flight; the NN weight of step 0 in LDS.
+  // Prologue: the first S steps in flight (the launcher guarantees the
+  // first item has KT >= S steps); NN weights of steps 0 and 1 in LDS.
 #pragma unroll
-  for (int s = 0; s < C::S; ++s)
-    if (ld.step < total) issue();
+  for (int s = 0; s < C::S; ++s) dma(cur_src, s, s);
   if constexpr (C::NN) {
-    nn_load_for(first.it, 0);
-    nn_store_for(0);
-    nn_step = 1;
+    nn_load_for(cur, 0);
+    nn_store<C>(nb, smem + C::A_BYTES);
+    nn_load_for(cur, 1);
+    nn_store<C>(nb, smem + C::STAGE + C::A_BYTES);
   }
-  wait_loads_at_most(newer_than(0));
+  wait_vmcnt<0>();
   __syncthreads();
 
-  Cursor cur = first;
-  // the item after cur's (for the NN weight one step ahead)
-  BigItem nxt = first.it;
-  if (C::NN && slot + P < n_items) nxt = decode_big<C>(pl, slot + P, n_ntiles, N, w);
   f32x4 acc[C::FM][C::FN];
 #pragma unroll
   for (int x = 0; x < C::FM; ++x)
 #pragma unroll
     for (int y = 0; y < C::FN; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  while (cur.step < total) {
-    const int s = cur.step;
-    const char* st = smem + (s % C::S) * C::STAGE;
-    if (s > 0) {
-      // this step's operands: this wave's loads, then every wave's (the
-      // barrier also frees the stage refilled below, read in step s-1)
-      wait_loads_at_most(newer_than(s));
-      __syncthreads();
-    }
-    i32x4 a[C::FM], b[C::FN];
-    read_frags<C>(a, b, st, cur.it, q, r16);
-    const bool nn_more = C::NN && nn_step < total;
-    if constexpr (C::NN) {
-      if (nn_more) {
-        if (cur.kt + 1 < KT)
-          nn_load_for(cur.it, cur.kt + 1);
+  const int lane_off = frag_lane_off(q, r16);
+  i32x4 a[C::FM], b0[C::FN], b1[C::FN];
+  {
+    const char* abase = smem + cur.rbase * C::ROW + lane_off;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) read_a_at<C>(a[fm], abase, fm);
+    read_b_at<C>(b0, smem + C::A_BYTES + cur.cbase * C::ROW + lane_off);
+  }
+
+  // Loads issued per step and wave: DMA_STEP direct-to-LDS, plus (NN) 8
+  // weight loads two steps ahead.  In steady state the loads of the next
+  // step have completed once at most STEADY newer loads are outstanding
+  // (loads retire in order; outstanding stores only make the wait longer).
+  constexpr int DMA_STEP = C::NN ? C::DMA_PER_OPERAND : 2 * C::DMA_PER_OPERAND;
+  constexpr int STEADY = C::NN ? 2 * DMA_STEP : (C::S - 2) * DMA_STEP;
+
+  int stage = 0;  // stage of the current step
+  for (int L = slot;;) {
+    const bool last_item = L + P >= n_items;
+    for (int kt = 0; kt < KT; ++kt) {
+      const bool more = !(last_item && kt == KT - 1);  // a step follows
+      const int st1 = (stage + 1) & (C::S - 1);
+      if (more) {
+        // step s+1's operands: this wave's loads, then every wave's; the
+        // barrier also frees the current stage (its fragments are in
+        // registers) for the refill below
+        if (last_item && kt + C::S > KT)
+          wait_vmcnt<0>();  // fewer newer loads near the end of the stream
         else
-          nn_load_for(nxt, 0);
+          wait_vmcnt<STEADY>();
+        __syncthreads();
+        const BigItem& it1 = kt + 1 < KT ? cur : nxt;
+        read_b_at<C>(b1, smem + st1 * C::STAGE + C::A_BYTES + it1.cbase * C::ROW + lane_off);
+        if constexpr (C::NN) {
+          if (!(last_item && kt + 2 >= KT)) {
+            if (kt + 2 < KT)
+              nn_load_for(cur, kt + 2);
+            else
+              nn_load_for(nxt, kt + 2 - KT);
+          }
+        }
+        // refill the current stage with step s+S
+        if (kt + C::S < KT)
+          dma(cur_src, kt + C::S, stage);
+        else if (!last_item)
+          dma(nxt_src, kt + C::S - KT, stage);
       }
-    }
-    if (s > 0 && ld.step < total) issue();
-    const BigItem& it = cur.it;
-    mfma_rows<C, 0, C::FM / 2>(acc, a, b);
-    if (!it.half) mfma_rows<C, C::FM / 2, C::FM>(acc, a, b);
-    if constexpr (C::NN) {
-      if (nn_more) {
-        nn_store_for(nn_step);
-        ++nn_step;
+      const BigItem& it1 = kt + 1 < KT ? cur : nxt;
+      const char* abase = smem + st1 * C::STAGE + it1.rbase * C::ROW + lane_off;
+      // rows [0, FM/2) always; the upper rows only for full tiles.  Each A
+      // fragment is refilled with step s+1's right after its last use.
+#pragma unroll
+      for (int fm = 0; fm < C::FM / 2; ++fm) {
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[fm]),
+                                                                __builtin_bit_cast(bf16x8, b0[fn]),
+                                                                acc[fm][fn], 0, 0, 0);
+        read_a_at<C>(a[fm], abase, fm);
       }
-    }
-    if (cur.kt == KT - 1) {
-      if (!it.half)
-        big_epilogue<C, C::FM>(p, acc, it, q, r16);
-      else
-        big_epilogue<C, C::FM / 2>(p, acc, it, q, r16);
+      if (!cur.half) mfma_rows<C, C::FM / 2, C::FM>(acc, a, b0);
 #pragma unroll
-      for (int x = 0; x < C::FM; ++x)
+      for (int fm = C::FM / 2; fm < C::FM; ++fm) read_a_at<C>(a[fm], abase, fm);
+      if constexpr (C::NN) {
+        if (more && !(last_item && kt + 2 >= KT)) nn_store<C>(nb, smem + ((stage + 2) & (C::S - 1)) * C::STAGE + C::A_BYTES);
+      }
 #pragma unroll
-        for (int y = 0; y < C::FN; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int fn = 0; fn < C::FN; ++fn) b0[fn] = b1[fn];
+      stage = st1;
     }
-    const int old_L = cur.L;
-    advance<C>(cur, pl, KT, P, n_items, n_ntiles, N, w);
-    if (C::NN && cur.L != old_L && cur.L + P < n_items) nxt = decode_big<C>(pl, cur.L + P, n_ntiles, N, w);
+    if (!cur.half)
+      big_epilogue<C, C::FM>(p, acc, cur, q, r16);
+    else
+      big_epilogue<C, C::FM / 2>(p, acc, cur, q, r16);
+    if (last_item) break;
+#pragma unroll
+    for (int x = 0; x < C::FM; ++x)
+#pragma unroll
+      for (int y = 0; y < C::FN; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+    L += P;
+    cur = nxt;
+    cur_src = nxt_src;
+    if (L + P < n_items) {
+      nxt = decode_big<C>(pl, L + P, n_ntiles, N, w);
+      nxt_src = big_src<C>(p, nxt);
+    }
   }
 }
 

@@ -40,6 +40,14 @@ def test_library_exports_every_declared_symbol(lib_path):
     assert sorted(m.EXPORTED) == _declared()
 
 
+def test_library_has_no_undefined_internal_symbols(lib_path):
+    """Every kernel launched from the host has its launch stub in the library
+    (a kernel the host compiler silently failed to instantiate would show up
+    here as an undefined symbol and only fail at load time on a GPU machine)."""
+    syms = subprocess.run(["nm", "-D", "--undefined-only", lib_path], capture_output=True, text=True).stdout
+    assert "gmmk" not in syms, [l for l in syms.splitlines() if "gmmk" in l]
+
+
 def test_product_package_never_references_the_oracle():
     pkg = os.path.join(ROOT, "moe_grouped_matrix_amd")
     for dirpath, _, files in os.walk(pkg):
