@@ -2,21 +2,32 @@
 // operands, no scales; an optional bias).
 //
 // Output tiles are 256 x 256 (group-aligned in M, as in the general kernel),
-// computed by eight waves (two per SIMD) of 128 x 64 each.  A group's last
-// m-tile and the last n-tile of a row are usually partial; when the valid
-// part is at most 128 rows or 128 columns the eight waves switch to 64 x 64
-// each, laid out 2 x 4 or 4 x 2 over the valid half, so such a tile costs
-// half a tile of MFMA work.
+// computed by eight waves, two per SIMD, of 128 x 64 each with 32x32x16 bf16
+// MFMAs.  Two waves per SIMD keep the matrix core busy while either of them
+// waits on a barrier or an LDS read.  The weight fragment is the MFMA's first
+// operand, so a lane holds runs of output columns of one row.  When a tile's
+// valid part is at most 128 rows or 128 columns, the waves switch to 64 x 64
+// each, laid out over the valid half, so such a tile costs half a tile of
+// MFMA work.
 //
-// K is consumed 32 at a time.  A K tile of both operands (256 rows x 64 bytes
-// each, 32 KB) sits in one of four LDS stages that form a ring.  While the
-// waves multiply step s (fragments already in registers), they read step
-// s+1's fragments from LDS, and steps s+2..s+4 -- of the same output tile, or
-// the first ones of the workgroup's next output tile -- are in flight.  Operands
-// reach LDS by direct-to-LDS buffer loads (no staging registers), except a
-// [G,K,N] weight, which goes through registers to be transposed to the
-// K-contiguous layout the MFMA operands need.
+// K is consumed 32 at a time.  A K step of both operands (32 KB) sits in one
+// of four LDS stages that form a ring: while the waves multiply step s, they
+// read step s+1's fragments from LDS into the registers each MFMA has just
+// consumed, and steps s+2 and s+3 -- of the same output tile or, near its
+// end, the first ones of the workgroup's next tile -- are in flight.  Both
+// operands reach LDS by direct-to-LDS buffer loads.  The lhs and an [G,N,K]
+// weight are stored K-contiguous (64-byte rows); an [G,K,N] weight keeps its
+// N-contiguous layout (512-byte K rows) and its fragments are read with the
+// LDS transpose read.
+//
+// The epilogue exchanges half-rows between the two halves of the wave
+// (permlane32 swap) so each lane stores eight consecutive columns with one
+// 16-byte buffer store.  Stores outside the tile's valid rows and columns
+// are dropped by the buffer range check, so every wave issues the same
+// number of memory instructions per tile, which the wait counts rely on.
 #pragma once
+
+#include <type_traits>
 
 #include "gmm_device.hpp"
 
@@ -28,30 +39,36 @@ struct BigCfg {
   static constexpr bool OUT_F32 = OUT_F32_;
   static constexpr int BM = 256, BN = 256;
   static constexpr int WM = 2, WN = 4, NWAVES = WM * WN, T = 64 * NWAVES;
-  static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
-  static constexpr int BK = 32;          // K per stage (one 16x16x32 MFMA)
-  static constexpr int ROW = BK * 2;     // bytes per LDS row
-  static constexpr int A_BYTES = BM * ROW, B_BYTES = BN * ROW;
+  static constexpr int FM = 4, FN = 2;    // 32 x 32 blocks of a full-tile wave (128 x 64)
+  static constexpr int BK = 32;           // K per stage (two 32x32x16 MFMA steps)
+  static constexpr int ROW = BK * 2;      // bytes of a K-contiguous operand row in a stage
+  static constexpr int NN_ROW = BN * 2;   // bytes of an N-contiguous weight K row
+  static constexpr int A_BYTES = BM * ROW, B_BYTES = BN * BK * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int S = 4;            // stages in the ring
-  static constexpr int LDS = S * STAGE;
-  // direct-to-LDS instructions per wave per operand and stage (1 KB each)
-  static constexpr int ROWS_PER_WAVE = BM / NWAVES;
-  static constexpr int DMA_PER_OPERAND = ROWS_PER_WAVE * ROW / 1024;
-  // NN weight tile per thread: 8 k rows x NWN n columns
-  static constexpr int NWN = BN * BK / T / 8;
-  static constexpr int NN_LOADS = 8;
-  static_assert(DMA_PER_OPERAND >= 1 && ROWS_PER_WAVE % 16 == 0, "DMA split");
-  static_assert(NWN == 2 || NWN == 4, "NN thread block");
+  static constexpr int S = 4;  // stages in the ring
+  static constexpr int RING = S * STAGE;
+  static constexpr int BIAS_SLOT = 2048;  // a tile's bias row (<= 1 KB) and range-checked padding
+  static constexpr int LDS = RING + 2 * BIAS_SLOT;
+  // direct-to-LDS instructions (1 KB each) per wave, operand and stage
+  static constexpr int DMA_A = A_BYTES / 1024 / NWAVES, DMA_B = B_BYTES / 1024 / NWAVES;
+  static constexpr int DMA_STEP = DMA_A + DMA_B;
+  static constexpr int es_out = OUT_F32 ? 4 : 2;
+  // stores per wave and tile: 16-byte stores of 8 columns, per 32 x 32 block
+  static constexpr int ST_BLOCK = OUT_F32 ? 4 : 2;
+  static constexpr int E_FULL = FM * FN * ST_BLOCK, E_HALF = (FM / 2) * FN * ST_BLOCK;
+  static_assert(DMA_A == 2 && DMA_B == 2, "DMA split");
+  static_assert(NN_ROW * BK == B_BYTES, "NN weight stage");
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // 64-byte LDS rows: 16-byte chunk c of row r is stored at chunk c ^ swz64(r).
-// Sixteen consecutive rows read at one logical chunk land in sixteen distinct
-// (row parity, chunk) bank groups.
+// Eight consecutive rows read at one logical chunk cover all 32 banks.
 __device__ __forceinline__ int swz64(int r) { return (r >> 1) & 3; }
-__device__ __forceinline__ int lds_off64(int r, int c) { return r * 64 + ((c ^ swz64(r)) << 4); }
+// 512-byte K rows of an N-contiguous weight: chunk c of K row k is stored at
+// chunk c ^ swzkn(k).  A transpose read of four K rows x 16 columns then
+// touches eight distinct 16-byte bank groups.
+__device__ __forceinline__ int swzkn(int k) { return 2 * (k & 3); }
 
 struct BigItem {
   int h, row0, rows, n0, ncols;
@@ -76,108 +93,122 @@ __device__ __forceinline__ BigItem decode_big(const Plan& pl, int L, int n_ntile
   const bool half_m = it.rows <= C::BM / 2, half_n = it.ncols <= C::BN / 2;
   it.half = half_m || half_n;
   if (!it.half) {  // 2 x 4 waves of 128 x 64
-    it.rbase = (w / C::WN) * C::TM;
-    it.cbase = (w % C::WN) * C::TN;
-  } else if (half_m) {  // 2 x 4 waves of 64 x 64 over 128 x 256
-    it.rbase = (w / C::WN) * (C::TM / 2);
-    it.cbase = (w % C::WN) * C::TN;
+    it.rbase = (w / C::WN) * 128;
+    it.cbase = (w % C::WN) * 64;
+  } else if (!half_n) {  // 2 x 4 waves of 64 x 64 over 128 x 256
+    it.rbase = (w / 4) * 64;
+    it.cbase = (w % 4) * 64;
   } else {  // 4 x 2 waves of 64 x 64 over 256 x 128
-    it.rbase = (w / C::WM) * (C::TM / 2);
-    it.cbase = (w % C::WM) * C::TN;
+    it.rbase = (w / 2) * 64;
+    it.cbase = (w % 2) * 64;
   }
   return it;
 }
 
-// Direct-to-LDS loads of 256 rows x 64 bytes (K columns [32 kt, 32 kt + 32))
-// of a row-major operand.  One instruction fills 1 KB = 16 rows; wave w fills
-// rows [w R, w R + R), R = 256 / waves.  Rows past the resource's end read as
-// zero.
-template <class C>
-__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, int row_bytes, int kt, char* dst) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int i = 0; i < C::DMA_PER_OPERAND; ++i) {
-    const int r0 = w * C::ROWS_PER_WAVE + i * 16;
-    const int r = r0 + (lane >> 2);
-    const int c = (lane & 3) ^ swz64(r);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + r0 * C::ROW), 16, r * row_bytes + c * 16,
-                                             kt * C::ROW, 0, 0);
-  }
-}
-
-// NN weight tile: thread t holds 8 consecutive k rows x NWN consecutive n
-// columns, to be written transposed into LDS.
-template <class C>
-__device__ __forceinline__ void nn_load(__amdgpu_buffer_rsrc_t rs, int N, int n0, int kt, int (&nb)[8 * C::NWN / 2]) {
-  constexpr int NB = C::BN / C::NWN;
-  const int tid = threadIdx.x;
-  const int nbk = tid % NB, kb = tid / NB;
-  const int nbase = n0 + nbk * C::NWN;
-#pragma unroll
-  for (int kr = 0; kr < 8; ++kr) {
-    const int k = kt * C::BK + kb * 8 + kr;
-    if constexpr (C::NWN == 2) {
-      nb[kr] = __builtin_amdgcn_raw_buffer_load_b32(rs, (k * N + nbase) * 2, 0, 0);
-    } else {
-      i32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, (k * N + nbase) * 2, 0, 0);
-      nb[2 * kr] = v[0];
-      nb[2 * kr + 1] = v[1];
-    }
-  }
-}
-
-template <class C>
-__device__ __forceinline__ void nn_store(const int (&nb)[8 * C::NWN / 2], char* sb) {
-  constexpr int NB = C::BN / C::NWN;
-  constexpr int WPR = C::NWN / 2;  // 32-bit words per k row
-  const int tid = threadIdx.x;
-  const int nbk = tid % NB, kb = tid / NB;
-#pragma unroll
-  for (int j = 0; j < C::NWN; ++j) {
-    i32x4 v;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t w0 = (uint32_t)nb[(2 * q) * WPR + j / 2];
-      const uint32_t w1 = (uint32_t)nb[(2 * q + 1) * WPR + j / 2];
-      const uint32_t lo = (j & 1) ? (w0 >> 16) : (w0 & 0xFFFFu);
-      const uint32_t hi = (j & 1) ? (w1 & 0xFFFF0000u) : (w1 << 16);
-      v[q] = (int)(lo | hi);
-    }
-    *reinterpret_cast<i32x4*>(sb + lds_off64(nbk * C::NWN + j, kb)) = v;
-  }
-}
-
+// Operand sources of an item as scalars (buffer resources are built at the
+// point of use, so they stay in scalar registers).  Reads past a range
+// return zero.
 struct BigSrc {
-  __amdgpu_buffer_rsrc_t a, b;
+  const char* a;     // lhs rows of the tile
+  const char* b;     // NT: weight rows of the n-tile; NN: the group's weight from column n0
+  const char* bias;  // the group's bias from column n0 (any address when absent)
+  int a_bytes, b_bytes, bias_bytes, ncols;
 };
 
 template <class C>
 __device__ __forceinline__ BigSrc big_src(const Params& p, const BigItem& it) {
   const int K = p.K, N = p.N;
   BigSrc s;
-  const char* lhs = reinterpret_cast<const char*>(p.lhs) + (long long)it.row0 * K * 2;
-  s.a = make_rsrc(lhs, (long long)it.rows * K * 2);
+  s.a = reinterpret_cast<const char*>(p.lhs) + (long long)it.row0 * K * 2;
+  s.a_bytes = it.rows * K * 2;
   const char* rhs_h = reinterpret_cast<const char*>(p.rhs) + (long long)it.h * N * K * 2;
-  if constexpr (C::NN)
-    s.b = make_rsrc(rhs_h, (long long)K * N * 2);
-  else
-    s.b = make_rsrc(rhs_h + (long long)it.n0 * K * 2, (long long)it.ncols * K * 2);
+  if constexpr (C::NN) {
+    s.b = rhs_h + (long long)it.n0 * 2;
+    s.b_bytes = K * N * 2 - it.n0 * 2;
+  } else {
+    s.b = rhs_h + (long long)it.n0 * K * 2;
+    s.b_bytes = it.ncols * K * 2;
+  }
+  const int bes = p.bias_f32 ? 4 : 2;
+  if (p.rhs_bias) {
+    s.bias = reinterpret_cast<const char*>(p.rhs_bias) + ((long long)it.h * N + it.n0) * bes;
+    s.bias_bytes = it.ncols * bes;
+  } else {
+    s.bias = reinterpret_cast<const char*>(p.lhs);
+    s.bias_bytes = 0;
+  }
+  s.ncols = it.ncols;
   return s;
 }
 
-// Queue the direct-to-LDS loads of K step kt (both operands when NT, lhs
-// only when NN) into LDS stage `st`; voff are this lane's row offsets.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const char* base, int bytes) {
+  const unsigned long long u = reinterpret_cast<unsigned long long>(base);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
+  const int n = __builtin_amdgcn_readfirstlane(bytes);
+  const char* b = reinterpret_cast<const char*>(((unsigned long long)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b), (short)0, n, kBufferRsrcWord3);
+}
+
+// Per-lane byte offsets of this wave's direct-to-LDS loads (the K step adds
+// a scalar offset).  K-contiguous operand: instruction i fills rows
+// 32 w + 16 i + lane/4.  N-contiguous weight: instruction i fills K rows
+// 4 w + 2 i + lane/32, 16-byte chunk lane%32 of each, which holds columns
+// bcol[i] + [0, 8) of the tile.
+struct DmaOff {
+  int a[2], b[2], bcol[2];
+};
+
 template <class C>
-__device__ __forceinline__ void dma_stage(const BigSrc& src, const int (&voff)[C::DMA_PER_OPERAND], int kt,
-                                          char* st, int w) {
+__device__ __forceinline__ DmaOff dma_offsets(int K, int N, int w, int lane) {
+  DmaOff d;
 #pragma unroll
-  for (int i = 0; i < C::DMA_PER_OPERAND; ++i) {
-    char* dst = st + (w * C::ROWS_PER_WAVE + i * 16) * C::ROW;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.a, (lds_ptr_t)dst, 16, voff[i], kt * C::ROW, 0, 0);
-    if constexpr (!C::NN)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(src.b, (lds_ptr_t)(dst + C::A_BYTES), 16, voff[i], kt * C::ROW,
-                                               0, 0);
+  for (int i = 0; i < 2; ++i) {
+    const int r = w * 32 + i * 16 + (lane >> 2);
+    d.a[i] = r * K * 2 + (((lane & 3) ^ swz64(r)) << 4);
+    if constexpr (C::NN) {
+      const int k = 4 * w + 2 * i + (lane >> 5);
+      const int c = (lane & 31) ^ swzkn(k);
+      d.b[i] = k * N * 2 + c * 16;
+      d.bcol[i] = c * 8;
+    } else {
+      d.b[i] = d.a[i];
+      d.bcol[i] = 0;
+    }
   }
+  return d;
+}
+
+// Queue the direct-to-LDS loads of K step kt into stage `st`: two 1 KB
+// instructions per operand and wave.  N-contiguous weight columns past the
+// tile's valid part get an out-of-range offset (they would otherwise wrap
+// into the next K row, or past the end of the last group's weight).
+template <class C>
+__device__ __forceinline__ void dma_stage(const BigSrc& src, const DmaOff& off, int kt, int N, char* st, int w) {
+  const __amdgpu_buffer_rsrc_t ra = uniform_rsrc(src.a, src.a_bytes);
+  const __amdgpu_buffer_rsrc_t rb = uniform_rsrc(src.b, src.b_bytes);
+  char* da = st + w * 2048;
+  char* db = st + C::A_BYTES + w * 2048;
+  const int sa = kt * C::ROW;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(da + i * 1024), 16, off.a[i], sa, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if constexpr (C::NN) {
+      const int vo = off.bcol[i] < src.ncols ? off.b[i] + kt * C::BK * N * 2 : (int)0x80000000;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(db + i * 1024), 16, vo, 0, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(db + i * 1024), 16, off.b[i], sa, 0, 0);
+    }
+  }
+}
+
+// The tile's bias row into an LDS slot: wave w copies bytes [256 w, 256 w + 256)
+// (zeros past the row, or everywhere without a bias).
+__device__ __forceinline__ void dma_bias(const BigSrc& src, char* slot, int w, int lane) {
+  const __amdgpu_buffer_rsrc_t r = uniform_rsrc(src.bias, src.bias_bytes);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(slot + w * 256), 4, w * 256 + lane * 4, 0, 0, 0);
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -189,78 +220,148 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Fragment rows start at multiples of 16, so a fragment's swizzled chunk
-// depends only on the lane: lane (q, r16) reads row base + r16, chunk
-// q ^ swz64(r16).  Fragment f of a wave is then one base address plus an
-// immediate f * 16 rows.  (Rows past a half tile's share may run into the B
-// part of the stage: they are read, never used.)
-__device__ __forceinline__ int frag_lane_off(int q, int r16) { return r16 * 64 + ((q ^ swz64(r16)) << 4); }
+// Workgroup barrier without a memory fence.  The K loop orders its LDS
+// traffic itself: a wave's direct-to-LDS loads are complete once the explicit
+// vmcnt wait before the barrier returns, and its fragment reads of a stage
+// are complete once the MFMAs that consume them have issued.  A fence here
+// would make the compiler drain every outstanding direct-to-LDS load before
+// the next LDS read, i.e. all the steps in flight.  The clobber keeps the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Waits until at most n vector-memory operations of this wave are
+// outstanding; n is one of the counts the K loop produces (anything else is
+// rounded down to a listed value, which only waits longer).
 template <class C>
-__device__ __forceinline__ void read_a_at(i32x4& a, const char* base, int fm) {
-  a = *reinterpret_cast<const i32x4*>(base + fm * 16 * C::ROW);
+__device__ __forceinline__ void wait_vmcnt_rt(int n) {
+  if (n >= 4 + C::E_FULL)
+    wait_vmcnt<4 + C::E_FULL>();
+  else if (n >= 4 + C::E_HALF)
+    wait_vmcnt<4 + C::E_HALF>();
+  else if (n >= 5)
+    wait_vmcnt<5>();
+  else if (n >= 4)
+    wait_vmcnt<4>();
+  else
+    wait_vmcnt<0>();
 }
 
-template <class C>
-__device__ __forceinline__ void read_b_at(i32x4 (&b)[C::FN], const char* base) {
-#pragma unroll
-  for (int fn = 0; fn < C::FN; ++fn) b[fn] = *reinterpret_cast<const i32x4*>(base + fn * 16 * C::ROW);
+// 32x32x16 fragments of a K-contiguous operand: lane (kh = lane / 32,
+// r32 = lane % 32) holds row base + 32 f + r32, K elements
+// [16 h + 8 kh, 16 h + 8 kh + 8) of the stage, i.e. 16-byte chunk 2 h + kh.
+// Fragment rows start at multiples of 32, so the swizzled chunk depends only
+// on the lane, and fragment (f, h) is one base address plus an immediate.
+__device__ __forceinline__ int frag_lane_off(int kh, int r32, int h) {
+  return r32 * 64 + (((2 * h + kh) ^ swz64(r32)) << 4);
 }
 
-template <class C, int F0, int F1>
-__device__ __forceinline__ void mfma_rows(f32x4 (&acc)[C::FM][C::FN], const i32x4 (&a)[C::FM],
-                                          const i32x4 (&b)[C::FN]) {
-#pragma unroll
-  for (int fm = F0; fm < F1; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
-      acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[fm]),
-                                                            __builtin_bit_cast(bf16x8, b[fn]), acc[fm][fn], 0, 0,
-                                                            0);
+// Fragment of an N-contiguous weight for tile columns
+// [cbase + 32 fn, cbase + 32 fn + 32) and K half h, from two LDS transpose
+// reads.  In read t, lane l (group q = l / 16, j = l % 16) points at K row
+// 16 h + 8 (q / 2) + 4 t + j / 4 and columns 16 (q % 2) + 4 (j % 4) + [0, 4)
+// of the block; the read hands lane l column l % 32 at K rows
+// 16 h + 8 (l / 32) + 4 t + [0, 4).  The lane part of the address is
+// nn_lane_off(fn); the K half and read add 512 (16 h + 4 t).
+__device__ __forceinline__ int nn_lane_off(int lane, int fn) {
+  const int q = lane >> 4, j = lane & 15;
+  const int krow = 8 * (q >> 1) + (j >> 2);
+  const int chunk = (4 * fn + 2 * (q & 1) + ((j >> 1) & 1)) ^ swzkn(j >> 2);
+  return krow * 512 + chunk * 16 + (j & 1) * 8;
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
+
+__device__ __forceinline__ i32x4 nn_frag(const char* p) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(p + 4 * 512));
+  const i32x2 l = __builtin_bit_cast(i32x2, lo), u = __builtin_bit_cast(i32x2, hi);
+  return i32x4{l[0], l[1], u[0], u[1]};
+}
+
+// Output block (fm, fn) of the wave: before the exchange, lane (kh, r32)
+// holds row rbase + 32 fm + r32 and, in register 4 g + i, column
+// cbase + 32 fn + 8 g + 4 kh + i.  For each pair of groups (g, g + 1) the
+// swap leaves lanes kh = 0 with columns 8 g + [0, 8) and lanes kh = 1 with
+// 8 (g + 1) + [0, 8), in order.
 template <class C, int FMA>
-__device__ __forceinline__ void big_epilogue(const Params& p, const f32x4 (&acc)[C::FM][C::FN],
-                                             const BigItem& it, int q, int r16) {
+__device__ __forceinline__ void big_epilogue(const Params& p, const f32x16 (&acc)[C::FM][C::FN], const BigItem& it,
+                                             const char* bias_slot, int kh, int r32) {
   const int N = p.N;
-  const int cl0 = it.cbase + r16;
-  // bias of this lane's columns (added once, after the products)
-  float bias[C::FN];
+  char* tile = reinterpret_cast<char*>(p.out) + ((long long)it.row0 * N + it.n0) * C::es_out;
+  const int nrec = ((it.rows - 1) * N + it.ncols) * C::es_out;
+  const __amdgpu_buffer_rsrc_t ro = uniform_rsrc(tile, nrec);
+  const bool has_bias = p.rhs_bias != nullptr;
+  const bool bias_f32 = p.bias_f32 != 0;
+  const int row_lane = r32 * N * C::es_out;
 #pragma unroll
   for (int fn = 0; fn < C::FN; ++fn) {
-    bias[fn] = 0.f;
-    const int cl = cl0 + fn * 16;
-    if (p.rhs_bias && cl < it.ncols) {
-      const long long bi = (long long)it.h * N + it.n0 + cl;
-      bias[fn] = p.bias_f32 ? reinterpret_cast<const float*>(p.rhs_bias)[bi]
-                            : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.rhs_bias)[bi]);
-    }
-  }
 #pragma unroll
-  for (int fm = 0; fm < FMA; ++fm) {
+    for (int gp = 0; gp < 4; gp += 2) {
+      // bias of columns cbase + 32 fn + 8 g + 4 kh + [0, 4), g = gp, gp + 1
+      float bias[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      if (has_bias) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rl = it.rbase + fm * 16 + 4 * q + i;
-      if (rl >= it.rows) continue;
-      const long long rbase = (long long)(it.row0 + rl) * N + it.n0 + cl0;
-      if constexpr (C::OUT_F32) {
-        float* op = reinterpret_cast<float*>(p.out) + rbase;
+        for (int x = 0; x < 2; ++x) {
+          const int c = it.cbase + fn * 32 + 8 * (gp + x) + 4 * kh;
+          if (bias_f32) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(bias_slot + c * 4);
+            bias[x][0] = v[0];
+            bias[x][1] = v[1];
+            bias[x][2] = v[2];
+            bias[x][3] = v[3];
+          } else {
+            const i32x2 v = *reinterpret_cast<const i32x2*>(bias_slot + c * 2);
+            bias[x][0] = __uint_as_float((uint32_t)v[0] << 16);
+            bias[x][1] = __uint_as_float((uint32_t)v[0] & 0xFFFF0000u);
+            bias[x][2] = __uint_as_float((uint32_t)v[1] << 16);
+            bias[x][3] = __uint_as_float((uint32_t)v[1] & 0xFFFF0000u);
+          }
+        }
+      }
+      // this lane's 8 columns after the swap start at cl; a store is in or
+      // out of the tile as a whole (ncols is a multiple of 8)
+      const int cl = it.cbase + fn * 32 + 8 * (gp + kh);
+      const bool col_ok = cl < it.ncols;
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
-          if (cl0 + fn * 16 < it.ncols) op[fn * 16] = acc[fm][fn][i] + bias[fn];
-      } else {
-        uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + rbase;
+      for (int fm = 0; fm < FMA; ++fm) {
+        const int voff = col_ok ? (it.rbase + fm * 32) * N * C::es_out + row_lane + cl * C::es_out
+                                : (int)0x80000000;
+        float v[2][4];
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
-          if (cl0 + fn * 16 < it.ncols) op[fn * 16] = f32_to_bf16_rne(acc[fm][fn][i] + bias[fn]);
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[x][i] = acc[fm][fn][4 * (gp + x) + i] + bias[x][i];
+        if constexpr (C::OUT_F32) {
+          int lo[4], hi[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0][i]), __float_as_uint(v[1][i]),
+                                                            false, false);
+            lo[i] = (int)r[0];
+            hi[i] = (int)r[1];
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(i32x4{lo[0], lo[1], lo[2], lo[3]}, ro, voff, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(i32x4{hi[0], hi[1], hi[2], hi[3]}, ro, voff + 16, 0, 0);
+        } else {
+          uint32_t x0[2], x1[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            x0[x] = (uint32_t)f32_to_bf16_rne(v[x][0]) | ((uint32_t)f32_to_bf16_rne(v[x][1]) << 16);
+            x1[x] = (uint32_t)f32_to_bf16_rne(v[x][2]) | ((uint32_t)f32_to_bf16_rne(v[x][3]) << 16);
+          }
+          const auto r0 = __builtin_amdgcn_permlane32_swap(x0[0], x0[1], false, false);
+          const auto r1 = __builtin_amdgcn_permlane32_swap(x1[0], x1[1], false, false);
+          __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1]}, ro, voff,
+                                                 0, 0);
+        }
       }
     }
   }
 }
 
 template <class C>
-__global__ __launch_bounds__(C::T) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gmm_big_kernel(Params p) {
+__global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   __shared__ Plan pl;
   if (threadIdx.x == 0) pl.flags = 0;
@@ -270,15 +371,14 @@ void gmm_big_kernel(Params p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int q = lane >> 4, r16 = lane & 15;
+  const int kh = lane >> 5, r32 = lane & 31;
   const int M = p.M, N = p.N, K = p.K;
   const int P = gridDim.x;
   const int slot = xcd_slot(blockIdx.x, P);
 
   // rows outside the active groups: zero them first (grid-stride)
   {
-    constexpr int out_es = C::OUT_F32 ? 4 : 2;
-    const long long row_bytes = (long long)N * out_es;
+    const long long row_bytes = (long long)N * C::es_out;
     const int lo_row = pl.row_start[0], hi_row = pl.row_start[pl.ga];
     char* out = reinterpret_cast<char*>(p.out);
     const i32x4 z = {0, 0, 0, 0};
@@ -297,135 +397,127 @@ void gmm_big_kernel(Params p) {
   if (slot >= n_items) return;
 
   // This workgroup's items are slot, slot + P, ...; their K steps form one
-  // stream.  Loads run S steps ahead of the multiplication, fragment reads
-  // one step ahead, NN weight loads two steps ahead -- within the current
-  // item or, near its end, in the next one.
+  // stream.  Loads run three steps ahead of the multiplication and fragment
+  // reads one step ahead -- within the current item or, near its end, in the
+  // next one.
   BigItem cur = decode_big<C>(pl, slot, n_ntiles, N, w);
-  int cur_L = slot;
   BigItem nxt = cur;
   if (slot + P < n_items) nxt = decode_big<C>(pl, slot + P, n_ntiles, N, w);
   BigSrc cur_src = big_src<C>(p, cur), nxt_src = big_src<C>(p, nxt);
+  const DmaOff doff = dma_offsets<C>(K, N, w, lane);
+  char* const bias0 = smem + C::RING;
 
-  // Per-lane byte offsets of this wave's direct-to-LDS rows (the K step adds
-  // a scalar offset): operand rows r = 16 i + lane/4 of the wave's share.
-  const int row_bytes = K * 2;
-  int dma_voff[C::DMA_PER_OPERAND];
+  // Prologue: the first tile's bias and steps 0..2; every older memory
+  // operation (the zero fill) is complete after the wait, so the loop's
+  // counts start from an empty queue.
+  dma_bias(cur_src, bias0, w, lane);
 #pragma unroll
-  for (int i = 0; i < C::DMA_PER_OPERAND; ++i) {
-    const int r = w * C::ROWS_PER_WAVE + i * 16 + (lane >> 2);
-    dma_voff[i] = r * row_bytes + (((lane & 3) ^ swz64(r)) << 4);
-  }
-  auto dma = [&](const BigSrc& src, int kt, int stage) __attribute__((always_inline)) {
-    dma_stage<C>(src, dma_voff, kt, smem + stage * C::STAGE, w);
-  };
-  int nb[8 * C::NWN / 2];
-  auto nn_load_for = [&](const BigItem& it, int kt) __attribute__((always_inline)) {
-    const char* rhs_h = reinterpret_cast<const char*>(p.rhs) + (long long)it.h * N * K * 2;
-    nn_load<C>(make_rsrc(rhs_h, (long long)K * N * 2), N, it.n0, kt, nb);
-  };
-
-  // Prologue: the first S steps in flight (the launcher guarantees the
-  // first item has KT >= S steps); NN weights of steps 0 and 1 in LDS.
-#pragma unroll
-  for (int s = 0; s < C::S; ++s) dma(cur_src, s, s);
-  if constexpr (C::NN) {
-    nn_load_for(cur, 0);
-    nn_store<C>(nb, smem + C::A_BYTES);
-    nn_load_for(cur, 1);
-    nn_store<C>(nb, smem + C::STAGE + C::A_BYTES);
-  }
+  for (int s = 0; s < C::S - 1; ++s) dma_stage<C>(cur_src, doff, s, N, smem + s * C::STAGE, w);
   wait_vmcnt<0>();
   __syncthreads();
 
-  f32x4 acc[C::FM][C::FN];
-#pragma unroll
-  for (int x = 0; x < C::FM; ++x)
-#pragma unroll
-    for (int y = 0; y < C::FN; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int alo0 = frag_lane_off(kh, r32, 0), alo1 = frag_lane_off(kh, r32, 1);
+  const int blo0 = C::NN ? nn_lane_off(lane, 0) : alo0;
+  const int blo1 = C::NN ? nn_lane_off(lane, 1) : alo1;
 
-  const int lane_off = frag_lane_off(q, r16);
-  i32x4 a[C::FM], b0[C::FN], b1[C::FN];
-  {
-    const char* abase = smem + cur.rbase * C::ROW + lane_off;
+  // fragment (f, h) of the step in stage `st`, for the layout of `it`
+  auto a_frag = [&](const char* st, const BigItem& it, int f, int h) __attribute__((always_inline)) {
+    return *reinterpret_cast<const i32x4*>(st + it.rbase * C::ROW + f * 32 * C::ROW + (h ? alo1 : alo0));
+  };
+  auto b_frag = [&](const char* st, const BigItem& it, int f, int h) __attribute__((always_inline)) {
+    const char* bb = st + C::A_BYTES;
+    if constexpr (C::NN) {
+      return nn_frag(bb + it.cbase * 2 + (f ? blo1 : blo0) + h * 16 * C::NN_ROW);
+    } else {
+      return *reinterpret_cast<const i32x4*>(bb + it.cbase * C::ROW + f * 32 * C::ROW + (h ? blo1 : blo0));
+    }
+  };
+
+  i32x4 a[C::FM][2], b[C::FN][2];
 #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) read_a_at<C>(a[fm], abase, fm);
-    read_b_at<C>(b0, smem + C::A_BYTES + cur.cbase * C::ROW + lane_off);
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int f = 0; f < C::FM; ++f) a[f][h] = a_frag(smem, cur, f, h);
+#pragma unroll
+    for (int f = 0; f < C::FN; ++f) b[f][h] = b_frag(smem, cur, f, h);
   }
 
-  // Loads issued per step and wave: DMA_STEP direct-to-LDS, plus (NN) 8
-  // weight loads two steps ahead.  In steady state the loads of the next
-  // step have completed once at most STEADY newer loads are outstanding
-  // (loads retire in order; outstanding stores only make the wait longer).
-  constexpr int DMA_STEP = C::NN ? C::DMA_PER_OPERAND : 2 * C::DMA_PER_OPERAND;
-  constexpr int STEADY = C::NN ? 2 * DMA_STEP : (C::S - 2) * DMA_STEP;
-
+  f32x16 acc[C::FM][C::FN];
   int stage = 0;  // stage of the current step
-  for (int L = slot;;) {
-    const bool last_item = L + P >= n_items;
+  int L = slot;
+  bool last_item = L + P >= n_items;
+  int par = 0;     // bias slot of the current item
+  int e_prev = 0;  // stores issued by the previous item's epilogue
+
+  // One item's K steps.  FULL: 128 x 64 per wave; else 64 x 64 (fragments
+  // fm >= 2 are still read, for a following full item).
+  auto kloop = [&](auto full_tag) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    constexpr int FMA = FULL ? C::FM : C::FM / 2;
     for (int kt = 0; kt < KT; ++kt) {
-      const bool more = !(last_item && kt == KT - 1);  // a step follows
-      const int st1 = (stage + 1) & (C::S - 1);
-      if (more) {
-        // step s+1's operands: this wave's loads, then every wave's; the
-        // barrier also frees the current stage (its fragments are in
-        // registers) for the refill below
-        if (last_item && kt + C::S > KT)
-          wait_vmcnt<0>();  // fewer newer loads near the end of the stream
-        else
-          wait_vmcnt<STEADY>();
-        __syncthreads();
-        const BigItem& it1 = kt + 1 < KT ? cur : nxt;
-        read_b_at<C>(b1, smem + st1 * C::STAGE + C::A_BYTES + it1.cbase * C::ROW + lane_off);
-        if constexpr (C::NN) {
-          if (!(last_item && kt + 2 >= KT)) {
-            if (kt + 2 < KT)
-              nn_load_for(cur, kt + 2);
-            else
-              nn_load_for(nxt, kt + 2 - KT);
-          }
+      if (!(last_item && kt == KT - 1)) {  // step s+1 exists
+        // Step s+1's operands: this wave's loads, then every wave's.  Newer
+        // operations than those loads: step s+2's loads (four; five for a
+        // tile's first step, which also carries its bias row) and, in a
+        // tile's first two steps, the previous tile's stores.
+        int newer = 0;
+        if (!(last_item && kt + 2 >= KT)) newer = (kt + 2 == KT) ? C::DMA_STEP + 1 : C::DMA_STEP;
+        if (kt <= 1) newer += e_prev;
+        wait_vmcnt_rt<C>(newer);
+        ring_barrier();
+        // refill the stage step s-1 used (every wave is past it) with step s+3
+        char* st3 = smem + ((stage + 3) & (C::S - 1)) * C::STAGE;
+        if (kt + 3 < KT) {
+          dma_stage<C>(cur_src, doff, kt + 3, N, st3, w);
+        } else if (!last_item) {
+          if (kt + 3 == KT) dma_bias(nxt_src, bias0 + (par ^ 1) * C::BIAS_SLOT, w, lane);
+          dma_stage<C>(nxt_src, doff, kt + 3 - KT, N, st3, w);
         }
-        // refill the current stage with step s+S
-        if (kt + C::S < KT)
-          dma(cur_src, kt + C::S, stage);
-        else if (!last_item)
-          dma(nxt_src, kt + C::S - KT, stage);
       }
+      // MFMAs of step s; each fragment is refilled with step s+1's right
+      // after its last use (from an in-range stage even when no step follows)
+      const char* st1 = smem + ((stage + 1) & (C::S - 1)) * C::STAGE;
       const BigItem& it1 = kt + 1 < KT ? cur : nxt;
-      const char* abase = smem + st1 * C::STAGE + it1.rbase * C::ROW + lane_off;
-      // rows [0, FM/2) always; the upper rows only for full tiles.  Each A
-      // fragment is refilled with step s+1's right after its last use.
 #pragma unroll
-      for (int fm = 0; fm < C::FM / 2; ++fm) {
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[fm]),
-                                                                __builtin_bit_cast(bf16x8, b0[fn]),
-                                                                acc[fm][fn], 0, 0, 0);
-        read_a_at<C>(a[fm], abase, fm);
+        for (int fm = 0; fm < FMA; ++fm) {
+#pragma unroll
+          for (int fn = 0; fn < C::FN; ++fn)
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b[fn][h]),
+                                                                  __builtin_bit_cast(bf16x8, a[fm][h]),
+                                                                  acc[fm][fn], 0, 0, 0);
+          a[fm][h] = a_frag(st1, it1, fm, h);
+        }
+#pragma unroll
+        for (int fm = FMA; fm < C::FM; ++fm) a[fm][h] = a_frag(st1, it1, fm, h);
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) b[fn][h] = b_frag(st1, it1, fn, h);
       }
-      if (!cur.half) mfma_rows<C, C::FM / 2, C::FM>(acc, a, b0);
-#pragma unroll
-      for (int fm = C::FM / 2; fm < C::FM; ++fm) read_a_at<C>(a[fm], abase, fm);
-      if constexpr (C::NN) {
-        if (more && !(last_item && kt + 2 >= KT)) nn_store<C>(nb, smem + ((stage + 2) & (C::S - 1)) * C::STAGE + C::A_BYTES);
-      }
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn) b0[fn] = b1[fn];
-      stage = st1;
+      stage = (stage + 1) & (C::S - 1);
     }
-    if (!cur.half)
-      big_epilogue<C, C::FM>(p, acc, cur, q, r16);
-    else
-      big_epilogue<C, C::FM / 2>(p, acc, cur, q, r16);
-    if (last_item) break;
+    big_epilogue<C, FMA>(p, acc, cur, bias0 + par * C::BIAS_SLOT, kh, r32);
+    e_prev = FULL ? C::E_FULL : C::E_HALF;
+  };
+
+  while (true) {
 #pragma unroll
     for (int x = 0; x < C::FM; ++x)
 #pragma unroll
-      for (int y = 0; y < C::FN; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int y = 0; y < C::FN; ++y)
+#pragma unroll
+        for (int z = 0; z < 16; ++z) acc[x][y][z] = 0.f;
+    if (!cur.half)
+      kloop(std::true_type{});
+    else
+      kloop(std::false_type{});
+    if (last_item) break;
     L += P;
+    last_item = L + P >= n_items;
     cur = nxt;
     cur_src = nxt_src;
-    if (L + P < n_items) {
+    par ^= 1;
+    if (!last_item) {
       nxt = decode_big<C>(pl, L + P, n_ntiles, N, w);
       nxt_src = big_src<C>(p, nxt);
     }

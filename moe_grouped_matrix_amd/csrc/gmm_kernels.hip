@@ -53,7 +53,7 @@ template <class C>
 hipError_t launch_big(const Params& p, int cu_count, hipStream_t stream) {
   const long long n_tiles = (p.N + C::BN - 1) / C::BN;
   const long long m_tiles = (p.M + C::BM - 1) / C::BM + p.Ga;
-  long long grid = cu_count;  // one 256-thread workgroup per CU (LDS-bound)
+  long long grid = cu_count;  // one workgroup per CU (LDS-bound)
   if (grid > m_tiles * n_tiles && m_tiles * n_tiles >= 8) grid = m_tiles * n_tiles;
   if (grid >= 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
