@@ -269,14 +269,32 @@ __device__ __forceinline__ int nn_lane_off(int lane, int fn) {
   return krow * 512 + chunk * 16 + (j & 1) * 8;
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
+// LDS transpose reads are issued as inline assembly: the compiler does not
+// know which LDS bytes the builtin reads and drains every outstanding
+// direct-to-LDS load before it.  The memory clobber keeps the reads in
+// program order with the compiler's own LDS reads, and the results are
+// waited for explicitly (nn_frags_ready) since the compiler does not track
+// them.
+template <int OFF>
+__device__ __forceinline__ i32x2 ds_read_tr16(unsigned addr) {
+  i32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
 
-__device__ __forceinline__ i32x4 nn_frag(const char* p) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(p));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(p + 4 * 512));
-  const i32x2 l = __builtin_bit_cast(i32x2, lo), u = __builtin_bit_cast(i32x2, hi);
-  return i32x4{l[0], l[1], u[0], u[1]};
+template <int H>
+__device__ __forceinline__ i32x4 nn_frag(unsigned addr) {
+  const i32x2 lo = ds_read_tr16<H * 16 * 512>(addr);
+  const i32x2 hi = ds_read_tr16<H * 16 * 512 + 4 * 512>(addr);
+  return i32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Per K half the refills issue eight LDS operations in a fixed order (four
+// lhs fragments, then two weight fragments of two transpose reads each), so
+// a K half's weight fragments have completed once at most the eight
+// operations of the following half are outstanding.
+__device__ __forceinline__ void nn_frags_ready() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (8 << 8) | (0x3 << 14));
 }
 
 // Output block (fm, fn) of the wave: before the exchange, lane (kh, r32)
@@ -362,8 +380,11 @@ __device__ __forceinline__ void big_epilogue(const Params& p, const f32x16 (&acc
 
 template <class C>
 __global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
-  __shared__ Plan pl;
+  // One LDS array for the ring, the bias slots and the plan: with a second
+  // LDS variable the compiler tags LDS accesses with alias scopes and then
+  // drains every outstanding direct-to-LDS load before each fragment read.
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS + sizeof(Plan)];
+  Plan& pl = *reinterpret_cast<Plan*>(smem + C::LDS);
   if (threadIdx.x == 0) pl.flags = 0;
   __syncthreads();
   build_plan<C::T>(p, pl, C::BM);
@@ -427,7 +448,8 @@ __global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
   auto b_frag = [&](const char* st, const BigItem& it, int f, int h) __attribute__((always_inline)) {
     const char* bb = st + C::A_BYTES;
     if constexpr (C::NN) {
-      return nn_frag(bb + it.cbase * 2 + (f ? blo1 : blo0) + h * 16 * C::NN_ROW);
+      const unsigned addr = (unsigned)(size_t)(lds_ptr_t)(bb + it.cbase * 2 + (f ? blo1 : blo0));
+      return h ? nn_frag<1>(addr) : nn_frag<0>(addr);
     } else {
       return *reinterpret_cast<const i32x4*>(bb + it.cbase * C::ROW + f * 32 * C::ROW + (h ? blo1 : blo0));
     }
@@ -480,6 +502,7 @@ __global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
       const BigItem& it1 = kt + 1 < KT ? cur : nxt;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        if constexpr (C::NN) nn_frags_ready();
 #pragma unroll
         for (int fm = 0; fm < FMA; ++fm) {
 #pragma unroll
