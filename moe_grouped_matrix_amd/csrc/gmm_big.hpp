@@ -48,7 +48,9 @@ struct BigCfg {
   static constexpr int S = 4;  // stages in the ring
   static constexpr int RING = S * STAGE;
   static constexpr int BIAS_SLOT = 2048;  // a tile's bias row (<= 1 KB) and range-checked padding
-  static constexpr int LDS = RING + 2 * BIAS_SLOT;
+  // two bias slots (current and next tile) and a slot that takes the
+  // per-step bias operation when no bias row is due
+  static constexpr int LDS = RING + 3 * BIAS_SLOT;
   // direct-to-LDS instructions (1 KB each) per wave, operand and stage
   static constexpr int DMA_A = A_BYTES / 1024 / NWAVES, DMA_B = B_BYTES / 1024 / NWAVES;
   static constexpr int DMA_STEP = DMA_A + DMA_B;
@@ -56,6 +58,10 @@ struct BigCfg {
   // stores per wave and tile: 16-byte stores of 8 columns, per 32 x 32 block
   static constexpr int ST_BLOCK = OUT_F32 ? 4 : 2;
   static constexpr int E_FULL = FM * FN * ST_BLOCK, E_HALF = (FM / 2) * FN * ST_BLOCK;
+  // memory operations per wave: every K step issues DMA_OPS loads (operands
+  // and one bias piece); every tile's epilogue issues E stores (a half tile
+  // pads with range-dropped stores)
+  static constexpr int DMA_OPS = DMA_STEP + 1, E = E_FULL;
   static_assert(DMA_A == 2 && DMA_B == 2, "DMA split");
   static_assert(NN_ROW * BK == B_BYTES, "NN weight stage");
 };
@@ -211,6 +217,81 @@ __device__ __forceinline__ void dma_bias(const BigSrc& src, char* slot, int w, i
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(slot + w * 256), 4, w * 256 + lane * 4, 0, 0, 0);
 }
 
+// The DMA_OPS direct-to-LDS operations of one K step, prepared up front so
+// they can be issued one at a time between MFMAs: two 1 KB instructions per
+// operand, then this wave's 256-byte piece of the next tile's bias row (into
+// a spare slot, with a zero-size range, when no bias row is due).  A step
+// past the end of the workgroup's stream loads from zero-size ranges: the
+// operation count per step never changes.
+template <class C>
+struct StepDma {
+  __amdgpu_buffer_rsrc_t ra, rb, rbias;
+  char* da;
+  char* db;
+  char* dbias;
+  int sa, sb, vbias;
+  int vb[2];
+
+  template <int J>
+  __device__ __forceinline__ void issue(const DmaOff& off) const {
+    if constexpr (J < 2) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(da + J * 1024), 16, off.a[J], sa, 0, 0);
+    } else if constexpr (J < 4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(db + (J - 2) * 1024), 16, vb[J - 2], sb, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbias, (lds_ptr_t)dbias, 4, vbias, 0, 0, 0);
+    }
+  }
+  // J is a constant once the MFMA loop around the call is unrolled
+  __device__ __forceinline__ void issue_rt(int J, const DmaOff& off) const {
+    if (J == 0) issue<0>(off);
+    else if (J == 1) issue<1>(off);
+    else if (J == 2) issue<2>(off);
+    else if (J == 3) issue<3>(off);
+    else if (J == 4) issue<4>(off);
+  }
+};
+
+// Loads for K step kt + 3 of the current tile or, past its end, step
+// kt + 3 - KT of the next one (none past the end of the stream).
+template <class C>
+__device__ __forceinline__ StepDma<C> step_dma(const BigSrc& cur, const BigSrc& nxt, const DmaOff& off, int kt,
+                                               int KT, bool last_item, int N, char* st, char* bias_next,
+                                               char* bias_spare, int w, int lane) {
+  const bool in_cur = kt + 3 < KT;
+  const bool live = in_cur || !last_item;
+  const int k = in_cur ? kt + 3 : kt + 3 - KT;
+  const bool bias_due = live && !in_cur && k == 0;
+  const char* a = in_cur ? cur.a : nxt.a;
+  const char* b = in_cur ? cur.b : nxt.b;
+  const char* bias = in_cur ? cur.bias : nxt.bias;
+  const int a_bytes = live ? (in_cur ? cur.a_bytes : nxt.a_bytes) : 0;
+  const int b_bytes = live ? (in_cur ? cur.b_bytes : nxt.b_bytes) : 0;
+  const int bias_bytes = bias_due ? nxt.bias_bytes : 0;
+  const int ncols = in_cur ? cur.ncols : nxt.ncols;
+  StepDma<C> d;
+  d.ra = uniform_rsrc(a, a_bytes);
+  d.rb = uniform_rsrc(b, b_bytes);
+  d.rbias = uniform_rsrc(bias, bias_bytes);
+  d.da = st + w * 2048;
+  d.db = st + C::A_BYTES + w * 2048;
+  d.dbias = (bias_due ? bias_next : bias_spare) + w * 256;
+  d.sa = k * C::ROW;
+  d.vbias = w * 256 + lane * 4;
+  if constexpr (C::NN) {
+    // N-contiguous weight: the K step goes into the (range-checked) lane
+    // offset; columns past the tile's valid part are out of range
+    d.sb = 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) d.vb[i] = off.bcol[i] < ncols ? off.b[i] + k * C::BK * N * 2 : (int)0x80000000;
+  } else {
+    d.sb = d.sa;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) d.vb[i] = off.b[i];
+  }
+  return d;
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt low bits [3:0], high bits [15:14]; expcnt [6:4] and lgkmcnt [11:8]
 // left at their maxima).
@@ -228,23 +309,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 // the next LDS read, i.e. all the steps in flight.  The clobber keeps the
 // compiler from moving memory accesses across the barrier.
 __device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// Waits until at most n vector-memory operations of this wave are
-// outstanding; n is one of the counts the K loop produces (anything else is
-// rounded down to a listed value, which only waits longer).
-template <class C>
-__device__ __forceinline__ void wait_vmcnt_rt(int n) {
-  if (n >= 4 + C::E_FULL)
-    wait_vmcnt<4 + C::E_FULL>();
-  else if (n >= 4 + C::E_HALF)
-    wait_vmcnt<4 + C::E_HALF>();
-  else if (n >= 5)
-    wait_vmcnt<5>();
-  else if (n >= 4)
-    wait_vmcnt<4>();
-  else
-    wait_vmcnt<0>();
-}
 
 // 32x32x16 fragments of a K-contiguous operand: lane (kh = lane / 32,
 // r32 = lane % 32) holds row base + 32 f + r32, K elements
@@ -376,6 +440,10 @@ __device__ __forceinline__ void big_epilogue(const Params& p, const f32x16 (&acc
       }
     }
   }
+  // a half tile pads to the full tile's store count with range-dropped stores
+#pragma unroll
+  for (int i = FMA * C::FN * C::ST_BLOCK; i < C::E; ++i)
+    __builtin_amdgcn_raw_buffer_store_b128(i32x4{0, 0, 0, 0}, ro, (int)0x80000000, 0, 0);
 }
 
 template <class C>
@@ -427,6 +495,7 @@ __global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
   BigSrc cur_src = big_src<C>(p, cur), nxt_src = big_src<C>(p, nxt);
   const DmaOff doff = dma_offsets<C>(K, N, w, lane);
   char* const bias0 = smem + C::RING;
+  char* const bias_spare = bias0 + 2 * C::BIAS_SLOT;
 
   // Prologue: the first tile's bias and steps 0..2; every older memory
   // operation (the zero fill) is complete after the wait, so the loop's
@@ -468,8 +537,7 @@ __global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
   int stage = 0;  // stage of the current step
   int L = slot;
   bool last_item = L + P >= n_items;
-  int par = 0;     // bias slot of the current item
-  int e_prev = 0;  // stores issued by the previous item's epilogue
+  int par = 0;  // bias slot of the current item
 
   // One item's K steps.  FULL: 128 x 64 per wave; else 64 x 64 (fragments
   // fm >= 2 are still read, for a following full item).
@@ -477,27 +545,22 @@ __global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
     constexpr bool FULL = decltype(full_tag)::value;
     constexpr int FMA = FULL ? C::FM : C::FM / 2;
     for (int kt = 0; kt < KT; ++kt) {
-      if (!(last_item && kt == KT - 1)) {  // step s+1 exists
-        // Step s+1's operands: this wave's loads, then every wave's.  Newer
-        // operations than those loads: step s+2's loads (four; five for a
-        // tile's first step, which also carries its bias row) and, in a
-        // tile's first two steps, the previous tile's stores.
-        int newer = 0;
-        if (!(last_item && kt + 2 >= KT)) newer = (kt + 2 == KT) ? C::DMA_STEP + 1 : C::DMA_STEP;
-        if (kt <= 1) newer += e_prev;
-        wait_vmcnt_rt<C>(newer);
-        ring_barrier();
-        // refill the stage step s-1 used (every wave is past it) with step s+3
-        char* st3 = smem + ((stage + 3) & (C::S - 1)) * C::STAGE;
-        if (kt + 3 < KT) {
-          dma_stage<C>(cur_src, doff, kt + 3, N, st3, w);
-        } else if (!last_item) {
-          if (kt + 3 == KT) dma_bias(nxt_src, bias0 + (par ^ 1) * C::BIAS_SLOT, w, lane);
-          dma_stage<C>(nxt_src, doff, kt + 3 - KT, N, st3, w);
-        }
-      }
-      // MFMAs of step s; each fragment is refilled with step s+1's right
-      // after its last use (from an in-range stage even when no step follows)
+      // Step s+1's operands: this wave's loads, then every wave's.  Newer
+      // than those loads are step s+2's DMA_OPS and, in a tile's first two
+      // steps, the previous tile's E stores (after the prologue's full wait
+      // the first tile's counts only wait longer).  The barrier also frees
+      // the stage step s-1 used.
+      if (kt <= 1)
+        wait_vmcnt<C::DMA_OPS + C::E>();
+      else
+        wait_vmcnt<C::DMA_OPS>();
+      ring_barrier();
+      const StepDma<C> dma = step_dma<C>(cur_src, nxt_src, doff, kt, KT, last_item, N,
+                                         smem + ((stage + 3) & (C::S - 1)) * C::STAGE,
+                                         bias0 + (par ^ 1) * C::BIAS_SLOT, bias_spare, w, lane);
+      // MFMAs of step s, the step s+3 loads after the first five, and each
+      // fragment refilled with step s+1's right after its last use (from an
+      // in-range stage even when no step follows)
       const char* st1 = smem + ((stage + 1) & (C::S - 1)) * C::STAGE;
       const BigItem& it1 = kt + 1 < KT ? cur : nxt;
 #pragma unroll
@@ -506,21 +569,24 @@ __global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
 #pragma unroll
         for (int fm = 0; fm < FMA; ++fm) {
 #pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn)
+          for (int fn = 0; fn < C::FN; ++fn) {
             acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b[fn][h]),
                                                                   __builtin_bit_cast(bf16x8, a[fm][h]),
                                                                   acc[fm][fn], 0, 0, 0);
+            dma.issue_rt((h * FMA + fm) * C::FN + fn, doff);
+            __builtin_amdgcn_sched_barrier(0);  // keep this order
+          }
           a[fm][h] = a_frag(st1, it1, fm, h);
         }
 #pragma unroll
         for (int fm = FMA; fm < C::FM; ++fm) a[fm][h] = a_frag(st1, it1, fm, h);
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn) b[fn][h] = b_frag(st1, it1, fn, h);
+        __builtin_amdgcn_sched_barrier(0);
       }
       stage = (stage + 1) & (C::S - 1);
     }
     big_epilogue<C, FMA>(p, acc, cur, bias0 + par * C::BIAS_SLOT, kh, r32);
-    e_prev = FULL ? C::E_FULL : C::E_HALF;
   };
 
   while (true) {
