@@ -48,9 +48,7 @@ struct BigCfg {
   static constexpr int S = 4;  // stages in the ring
   static constexpr int RING = S * STAGE;
   static constexpr int BIAS_SLOT = 2048;  // a tile's bias row (<= 1 KB) and range-checked padding
-  // two bias slots (current and next tile) and a slot that takes the
-  // per-step bias operation when no bias row is due
-  static constexpr int LDS = RING + 3 * BIAS_SLOT;
+  static constexpr int LDS = RING + 2 * BIAS_SLOT;  // bias slots of the current and the next tile
   // direct-to-LDS instructions (1 KB each) per wave, operand and stage
   static constexpr int DMA_A = A_BYTES / 1024 / NWAVES, DMA_B = B_BYTES / 1024 / NWAVES;
   static constexpr int DMA_STEP = DMA_A + DMA_B;
@@ -58,9 +56,9 @@ struct BigCfg {
   // stores per wave and tile: 16-byte stores of 8 columns, per 32 x 32 block
   static constexpr int ST_BLOCK = OUT_F32 ? 4 : 2;
   static constexpr int E_FULL = FM * FN * ST_BLOCK, E_HALF = (FM / 2) * FN * ST_BLOCK;
-  // memory operations per wave: every K step issues DMA_OPS loads (operands
-  // and one bias piece); every tile's epilogue issues E stores (a half tile
-  // pads with range-dropped stores)
+  // memory operations per wave: a K step issues DMA_STEP loads (DMA_OPS for
+  // a tile's first step, with its bias row); a tile's epilogue issues E
+  // stores (a half tile pads with range-dropped stores)
   static constexpr int DMA_OPS = DMA_STEP + 1, E = E_FULL;
   static_assert(DMA_A == 2 && DMA_B == 2, "DMA split");
   static_assert(NN_ROW * BK == B_BYTES, "NN weight stage");
@@ -217,79 +215,47 @@ __device__ __forceinline__ void dma_bias(const BigSrc& src, char* slot, int w, i
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(slot + w * 256), 4, w * 256 + lane * 4, 0, 0, 0);
 }
 
-// The DMA_OPS direct-to-LDS operations of one K step, prepared up front so
-// they can be issued one at a time between MFMAs: two 1 KB instructions per
-// operand, then this wave's 256-byte piece of the next tile's bias row (into
-// a spare slot, with a zero-size range, when no bias row is due).  A step
-// past the end of the workgroup's stream loads from zero-size ranges: the
-// operation count per step never changes.
+// Direct-to-LDS sources of one tile, built once per tile (scalar
+// registers): buffer resources of both operands and of its bias row, and
+// for an N-contiguous weight the lane offsets with columns past the tile's
+// valid part out of range (they would otherwise wrap into the next K row,
+// or past the end of the last group's weight).  A tile past the end of the
+// workgroup's stream gets zero-size ranges: its loads still issue (and
+// write zeros to stages nobody reads), so every K step issues the same
+// number of memory operations.
 template <class C>
-struct StepDma {
+struct TileDma {
   __amdgpu_buffer_rsrc_t ra, rb, rbias;
-  char* da;
-  char* db;
-  char* dbias;
-  int sa, sb, vbias;
   int vb[2];
-
-  template <int J>
-  __device__ __forceinline__ void issue(const DmaOff& off) const {
-    if constexpr (J < 2) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(da + J * 1024), 16, off.a[J], sa, 0, 0);
-    } else if constexpr (J < 4) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(db + (J - 2) * 1024), 16, vb[J - 2], sb, 0, 0);
-    } else {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbias, (lds_ptr_t)dbias, 4, vbias, 0, 0, 0);
-    }
-  }
-  // J is a constant once the MFMA loop around the call is unrolled
-  __device__ __forceinline__ void issue_rt(int J, const DmaOff& off) const {
-    if (J == 0) issue<0>(off);
-    else if (J == 1) issue<1>(off);
-    else if (J == 2) issue<2>(off);
-    else if (J == 3) issue<3>(off);
-    else if (J == 4) issue<4>(off);
-  }
 };
 
-// Loads for K step kt + 3 of the current tile or, past its end, step
-// kt + 3 - KT of the next one (none past the end of the stream).
 template <class C>
-__device__ __forceinline__ StepDma<C> step_dma(const BigSrc& cur, const BigSrc& nxt, const DmaOff& off, int kt,
-                                               int KT, bool last_item, int N, char* st, char* bias_next,
-                                               char* bias_spare, int w, int lane) {
-  const bool in_cur = kt + 3 < KT;
-  const bool live = in_cur || !last_item;
-  const int k = in_cur ? kt + 3 : kt + 3 - KT;
-  const bool bias_due = live && !in_cur && k == 0;
-  const char* a = in_cur ? cur.a : nxt.a;
-  const char* b = in_cur ? cur.b : nxt.b;
-  const char* bias = in_cur ? cur.bias : nxt.bias;
-  const int a_bytes = live ? (in_cur ? cur.a_bytes : nxt.a_bytes) : 0;
-  const int b_bytes = live ? (in_cur ? cur.b_bytes : nxt.b_bytes) : 0;
-  const int bias_bytes = bias_due ? nxt.bias_bytes : 0;
-  const int ncols = in_cur ? cur.ncols : nxt.ncols;
-  StepDma<C> d;
-  d.ra = uniform_rsrc(a, a_bytes);
-  d.rb = uniform_rsrc(b, b_bytes);
-  d.rbias = uniform_rsrc(bias, bias_bytes);
-  d.da = st + w * 2048;
-  d.db = st + C::A_BYTES + w * 2048;
-  d.dbias = (bias_due ? bias_next : bias_spare) + w * 256;
-  d.sa = k * C::ROW;
-  d.vbias = w * 256 + lane * 4;
-  if constexpr (C::NN) {
-    // N-contiguous weight: the K step goes into the (range-checked) lane
-    // offset; columns past the tile's valid part are out of range
-    d.sb = 0;
+__device__ __forceinline__ TileDma<C> tile_dma(const BigSrc& src, const DmaOff& off, bool live) {
+  TileDma<C> d;
+  d.ra = uniform_rsrc(src.a, live ? src.a_bytes : 0);
+  d.rb = uniform_rsrc(src.b, live ? src.b_bytes : 0);
+  d.rbias = uniform_rsrc(src.bias, live ? src.bias_bytes : 0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) d.vb[i] = off.bcol[i] < ncols ? off.b[i] + k * C::BK * N * 2 : (int)0x80000000;
-  } else {
-    d.sb = d.sa;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) d.vb[i] = off.b[i];
-  }
+  for (int i = 0; i < 2; ++i) d.vb[i] = (C::NN && off.bcol[i] >= src.ncols) ? (int)0x80000000 : off.b[i];
   return d;
+}
+
+// Direct-to-LDS operation J of K step k into stage `st`: J = 0, 1 the lhs,
+// J = 2, 3 the weight (1 KB each per wave), J = 4 this wave's 256-byte piece
+// of the tile's bias row.
+template <class C, int J>
+__device__ __forceinline__ void dma_op(const TileDma<C>& d, const DmaOff& off, int k, int N, char* st,
+                                       char* bias_slot, int w, int vbias) {
+  if constexpr (J < 2) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_ptr_t)(st + w * 2048 + J * 1024), 16, off.a[J],
+                                             k * C::ROW, 0, 0);
+  } else if constexpr (J < 4) {
+    const int so = C::NN ? k * C::BK * N * 2 : k * C::ROW;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rb, (lds_ptr_t)(st + C::A_BYTES + w * 2048 + (J - 2) * 1024), 16,
+                                             d.vb[J - 2], so, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rbias, (lds_ptr_t)(bias_slot + w * 256), 4, vbias, 0, 0, 0);
+  }
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -325,7 +291,9 @@ __device__ __forceinline__ int frag_lane_off(int kh, int r32, int h) {
 // 16 h + 8 (q / 2) + 4 t + j / 4 and columns 16 (q % 2) + 4 (j % 4) + [0, 4)
 // of the block; the read hands lane l column l % 32 at K rows
 // 16 h + 8 (l / 32) + 4 t + [0, 4).  The lane part of the address is
-// nn_lane_off(fn); the K half and read add 512 (16 h + 4 t).
+// nn_lane_off(fn) for a block at column 0 of a 128-column half; the swizzle
+// flips chunk bit 3, so a block at column 64 mod 128 XORs that bit (byte
+// 128) into the lane part.  The K half and read add 512 (16 h + 4 t).
 __device__ __forceinline__ int nn_lane_off(int lane, int fn) {
   const int q = lane >> 4, j = lane & 15;
   const int krow = 8 * (q >> 1) + (j >> 2);
@@ -482,7 +450,7 @@ __global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
 
   const int n_ntiles = (N + C::BN - 1) / C::BN;
   const int n_items = __builtin_amdgcn_readfirstlane(pl.n_mtiles) * n_ntiles;
-  const int KT = K / C::BK;  // K steps per item; the launcher guarantees KT >= S
+  const int KT = K / C::BK;  // K steps per item; the launcher guarantees KT >= 5
   if (slot >= n_items) return;
 
   // This workgroup's items are slot, slot + P, ...; their K steps form one
@@ -495,7 +463,6 @@ __global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
   BigSrc cur_src = big_src<C>(p, cur), nxt_src = big_src<C>(p, nxt);
   const DmaOff doff = dma_offsets<C>(K, N, w, lane);
   char* const bias0 = smem + C::RING;
-  char* const bias_spare = bias0 + 2 * C::BIAS_SLOT;
 
   // Prologue: the first tile's bias and steps 0..2; every older memory
   // operation (the zero fill) is complete after the wait, so the loop's
@@ -517,7 +484,8 @@ __global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
   auto b_frag = [&](const char* st, const BigItem& it, int f, int h) __attribute__((always_inline)) {
     const char* bb = st + C::A_BYTES;
     if constexpr (C::NN) {
-      const unsigned addr = (unsigned)(size_t)(lds_ptr_t)(bb + it.cbase * 2 + (f ? blo1 : blo0));
+      const int cb = it.cbase * 2;  // byte offset of the wave's first column in a K row
+      const unsigned addr = (unsigned)(size_t)(lds_ptr_t)(bb + (cb & ~128) + ((f ? blo1 : blo0) ^ (cb & 128)));
       return h ? nn_frag<1>(addr) : nn_frag<0>(addr);
     } else {
       return *reinterpret_cast<const i32x4*>(bb + it.cbase * C::ROW + f * 32 * C::ROW + (h ? blo1 : blo0));
@@ -538,54 +506,82 @@ __global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
   int L = slot;
   bool last_item = L + P >= n_items;
   int par = 0;  // bias slot of the current item
+  TileDma<C> dcur = tile_dma<C>(cur_src, doff, true);
+  TileDma<C> dnxt = tile_dma<C>(nxt_src, doff, !last_item);
+  const int vbias = w * 256 + lane * 4;
 
-  // One item's K steps.  FULL: 128 x 64 per wave; else 64 x 64 (fragments
-  // fm >= 2 are still read, for a following full item).
-  auto kloop = [&](auto full_tag) __attribute__((always_inline)) {
+  // One K step s.  The tile's K loop runs in phases so each step's wait
+  // count and load source are constants: step s+1's operands are complete
+  // (this wave's loads, then every wave's after the barrier) once at most
+  // WAIT newer operations are outstanding -- step s+2's loads (four; five
+  // for a tile's first step, which also brings its bias row) and, in a
+  // tile's first two steps, the previous tile's E stores (after the
+  // prologue's full wait the first tile's counts only wait longer).  The
+  // barrier also frees the stage step s-1 used, which takes the loads of
+  // step s+3 (this tile's step kd, or the next tile's when NEXT), spread
+  // evenly over the MFMAs.  Each fragment is refilled with step s+1's --
+  // the next tile's layout in a tile's last step -- right after its last
+  // use (from an in-range stage even when no step follows).
+  auto kstep = [&](auto full_tag, auto wait_tag, auto next_tag, auto bias_tag, auto last_tag, int kd)
+      __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    constexpr int WAIT = decltype(wait_tag)::value;
+    constexpr bool NEXT = decltype(next_tag)::value, BIAS = decltype(bias_tag)::value;
+    constexpr bool LAST = decltype(last_tag)::value;
+    constexpr int FMA = FULL ? C::FM : C::FM / 2;
+    constexpr int NM = 2 * FMA * C::FN;  // MFMAs per step
+    constexpr int NOPS = BIAS ? C::DMA_OPS : C::DMA_STEP;
+    wait_vmcnt<WAIT>();
+    ring_barrier();
+    const TileDma<C>& d = NEXT ? dnxt : dcur;
+    char* st3 = smem + ((stage + 3) & (C::S - 1)) * C::STAGE;
+    char* bslot = bias0 + (par ^ 1) * C::BIAS_SLOT;
+    const char* st1 = smem + ((stage + 1) & (C::S - 1)) * C::STAGE;
+    const BigItem& it1 = LAST ? nxt : cur;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if constexpr (C::NN) nn_frags_ready();
+#pragma unroll
+      for (int fm = 0; fm < FMA; ++fm) {
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b[fn][h]),
+                                                                __builtin_bit_cast(bf16x8, a[fm][h]),
+                                                                acc[fm][fn], 0, 0, 0);
+          const int m = (h * FMA + fm) * C::FN + fn;
+          // with the bias piece it goes first (older than the operands)
+          if (m == 0 * NM / NOPS) { if constexpr (BIAS) dma_op<C, 4>(d, doff, kd, N, st3, bslot, w, vbias); else dma_op<C, 0>(d, doff, kd, N, st3, bslot, w, vbias); }
+          if (m == 1 * NM / NOPS) { if constexpr (BIAS) dma_op<C, 0>(d, doff, kd, N, st3, bslot, w, vbias); else dma_op<C, 1>(d, doff, kd, N, st3, bslot, w, vbias); }
+          if (m == 2 * NM / NOPS) { if constexpr (BIAS) dma_op<C, 1>(d, doff, kd, N, st3, bslot, w, vbias); else dma_op<C, 2>(d, doff, kd, N, st3, bslot, w, vbias); }
+          if (m == 3 * NM / NOPS) { if constexpr (BIAS) dma_op<C, 2>(d, doff, kd, N, st3, bslot, w, vbias); else dma_op<C, 3>(d, doff, kd, N, st3, bslot, w, vbias); }
+          if constexpr (BIAS) if (m == 4 * NM / NOPS) dma_op<C, 3>(d, doff, kd, N, st3, bslot, w, vbias);
+          __builtin_amdgcn_sched_barrier(0);  // keep this order
+        }
+        a[fm][h] = a_frag(st1, it1, fm, h);
+      }
+#pragma unroll
+      for (int fm = FMA; fm < C::FM; ++fm) a[fm][h] = a_frag(st1, it1, fm, h);
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) b[fn][h] = b_frag(st1, it1, fn, h);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    stage = (stage + 1) & (C::S - 1);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  using W0 = std::integral_constant<int, C::DMA_STEP + C::E>;  // first two steps of a tile
+  using W1 = std::integral_constant<int, C::DMA_STEP>;
+  using W2 = std::integral_constant<int, C::DMA_STEP + 1>;  // step s+2 is the next tile's first
+  // One tile: KT >= 5 steps (the launcher guarantees K >= 160).
+  auto ktile = [&](auto full_tag) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_tag)::value;
     constexpr int FMA = FULL ? C::FM : C::FM / 2;
-    for (int kt = 0; kt < KT; ++kt) {
-      // Step s+1's operands: this wave's loads, then every wave's.  Newer
-      // than those loads are step s+2's DMA_OPS and, in a tile's first two
-      // steps, the previous tile's E stores (after the prologue's full wait
-      // the first tile's counts only wait longer).  The barrier also frees
-      // the stage step s-1 used.
-      if (kt <= 1)
-        wait_vmcnt<C::DMA_OPS + C::E>();
-      else
-        wait_vmcnt<C::DMA_OPS>();
-      ring_barrier();
-      const StepDma<C> dma = step_dma<C>(cur_src, nxt_src, doff, kt, KT, last_item, N,
-                                         smem + ((stage + 3) & (C::S - 1)) * C::STAGE,
-                                         bias0 + (par ^ 1) * C::BIAS_SLOT, bias_spare, w, lane);
-      // MFMAs of step s, the step s+3 loads after the first five, and each
-      // fragment refilled with step s+1's right after its last use (from an
-      // in-range stage even when no step follows)
-      const char* st1 = smem + ((stage + 1) & (C::S - 1)) * C::STAGE;
-      const BigItem& it1 = kt + 1 < KT ? cur : nxt;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if constexpr (C::NN) nn_frags_ready();
-#pragma unroll
-        for (int fm = 0; fm < FMA; ++fm) {
-#pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn) {
-            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b[fn][h]),
-                                                                  __builtin_bit_cast(bf16x8, a[fm][h]),
-                                                                  acc[fm][fn], 0, 0, 0);
-            dma.issue_rt((h * FMA + fm) * C::FN + fn, doff);
-            __builtin_amdgcn_sched_barrier(0);  // keep this order
-          }
-          a[fm][h] = a_frag(st1, it1, fm, h);
-        }
-#pragma unroll
-        for (int fm = FMA; fm < C::FM; ++fm) a[fm][h] = a_frag(st1, it1, fm, h);
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) b[fn][h] = b_frag(st1, it1, fn, h);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      stage = (stage + 1) & (C::S - 1);
-    }
+    kstep(full_tag, W0{}, F_{}, F_{}, F_{}, 3);
+    kstep(full_tag, W0{}, F_{}, F_{}, F_{}, 4);
+    for (int kt = 2; kt + 3 < KT; ++kt) kstep(full_tag, W1{}, F_{}, F_{}, F_{}, kt + 3);
+    kstep(full_tag, W1{}, T_{}, T_{}, F_{}, 0);  // kt = KT-3: the next tile's step 0 and bias row
+    kstep(full_tag, W2{}, T_{}, F_{}, F_{}, 1);
+    kstep(full_tag, W1{}, T_{}, F_{}, T_{}, 2);
     big_epilogue<C, FMA>(p, acc, cur, bias0 + par * C::BIAS_SLOT, kh, r32);
   };
 
@@ -597,19 +593,21 @@ __global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
 #pragma unroll
         for (int z = 0; z < 16; ++z) acc[x][y][z] = 0.f;
     if (!cur.half)
-      kloop(std::true_type{});
+      ktile(std::true_type{});
     else
-      kloop(std::false_type{});
+      ktile(std::false_type{});
     if (last_item) break;
     L += P;
     last_item = L + P >= n_items;
     cur = nxt;
     cur_src = nxt_src;
+    dcur = dnxt;
     par ^= 1;
     if (!last_item) {
       nxt = decode_big<C>(pl, L + P, n_ntiles, N, w);
       nxt_src = big_src<C>(p, nxt);
     }
+    dnxt = tile_dma<C>(nxt_src, doff, !last_item);
   }
 }
 

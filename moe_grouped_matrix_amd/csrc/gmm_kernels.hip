@@ -65,8 +65,8 @@ template <Op OP, bool NN, bool BF8, bool SC>
 hipError_t by_size(const Params& p, SizeClass sz, int cu, hipStream_t st) {
   if constexpr (OP == Op::F32) return launch_cfg<Cfg<Op::F32, NN, false, 64, 64, 2, 2, SC>>(p, cu, st);
   if constexpr (OP == Op::BF16 && !BF8 && !SC) {
-    // the big kernel keeps S = 4 K steps of 32 in flight: K >= 128
-    if (sz == SizeClass::Big && p.K >= 4 * 32) {
+    // the big kernel runs a tile in five phases of K steps of 32: K >= 160
+    if (sz == SizeClass::Big && p.K >= 5 * 32) {
       if (p.out_f32) return launch_big<BigCfg<NN, true>>(p, cu, st);
       return launch_big<BigCfg<NN, false>>(p, cu, st);
     }
