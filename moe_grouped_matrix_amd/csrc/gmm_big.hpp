@@ -329,83 +329,116 @@ __device__ __forceinline__ void nn_frags_ready() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (8 << 8) | (0x3 << 14));
 }
 
-// Output block (fm, fn) of the wave: before the exchange, lane (kh, r32)
-// holds row rbase + 32 fm + r32 and, in register 4 g + i, column
-// cbase + 32 fn + 8 g + 4 kh + i.  For each pair of groups (g, g + 1) the
-// swap leaves lanes kh = 0 with columns 8 g + [0, 8) and lanes kh = 1 with
-// 8 (g + 1) + [0, 8), in order.
+// Staging rows of the epilogue: 128 bytes (eight 16-byte chunks); chunk c
+// of row r is stored at chunk c ^ swz_out(r), so that both the column-wise
+// writes (one chunk of 16 or 32 consecutive rows per LDS cycle) and the
+// row-wise reads (whole rows) hit distinct bank groups.
+__device__ __forceinline__ int swz_out(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Epilogue of one tile.  Block (fm, fn) of the wave, before the exchange:
+// lane (kh, r32) holds row rbase + 32 fm + r32 and, in register 4 g + i,
+// column cbase + 32 fn + 8 g + 4 kh + i.  For each pair of groups (g, g+1)
+// the permlane32 swap leaves lanes kh = 0 with columns 8 g + [0, 8) and
+// lanes kh = 1 with 8 (g+1) + [0, 8), in order.  Each 32-row block (per
+// column half for an f32 output) then passes through the wave's 4 KB
+// staging slice so that a store writes 8 whole 128-byte row segments
+// instead of 32 scattered 32-byte ones.  Stores outside the tile's valid
+// rows and columns are dropped by the range check; a half tile pads to the
+// full tile's store count E.
 template <class C, int FMA>
 __device__ __forceinline__ void big_epilogue(const Params& p, const f32x16 (&acc)[C::FM][C::FN], const BigItem& it,
-                                             const char* bias_slot, int kh, int r32) {
+                                             const char* bias_slot, char* stg, int kh, int r32, int lane) {
   const int N = p.N;
   char* tile = reinterpret_cast<char*>(p.out) + ((long long)it.row0 * N + it.n0) * C::es_out;
   const int nrec = ((it.rows - 1) * N + it.ncols) * C::es_out;
   const __amdgpu_buffer_rsrc_t ro = uniform_rsrc(tile, nrec);
   const bool has_bias = p.rhs_bias != nullptr;
   const bool bias_f32 = p.bias_f32 != 0;
-  const int row_lane = r32 * N * C::es_out;
+  const int srow = lane >> 3, schunk = lane & 7;  // store phase: row and chunk of this lane
+  const int wr_row = r32 * 128;                   // write phase: this lane's staging row
+  // columns cbase + 32 fn + 8 (gp + x) + 4 kh + [0, 4) of the bias row
+  auto load_bias = [&](int fn, int gp, float (&bias)[2][4]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int fn = 0; fn < C::FN; ++fn) {
-#pragma unroll
-    for (int gp = 0; gp < 4; gp += 2) {
-      // bias of columns cbase + 32 fn + 8 g + 4 kh + [0, 4), g = gp, gp + 1
-      float bias[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      if (has_bias) {
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const int c = it.cbase + fn * 32 + 8 * (gp + x) + 4 * kh;
-          if (bias_f32) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(bias_slot + c * 4);
-            bias[x][0] = v[0];
-            bias[x][1] = v[1];
-            bias[x][2] = v[2];
-            bias[x][3] = v[3];
-          } else {
-            const i32x2 v = *reinterpret_cast<const i32x2*>(bias_slot + c * 2);
-            bias[x][0] = __uint_as_float((uint32_t)v[0] << 16);
-            bias[x][1] = __uint_as_float((uint32_t)v[0] & 0xFFFF0000u);
-            bias[x][2] = __uint_as_float((uint32_t)v[1] << 16);
-            bias[x][3] = __uint_as_float((uint32_t)v[1] & 0xFFFF0000u);
-          }
-        }
+    for (int x = 0; x < 2; ++x) {
+      const int c = it.cbase + fn * 32 + 8 * (gp + x) + 4 * kh;
+      if (bias_f32) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(bias_slot + c * 4);
+        bias[x][0] = v[0];
+        bias[x][1] = v[1];
+        bias[x][2] = v[2];
+        bias[x][3] = v[3];
+      } else {
+        const i32x2 v = *reinterpret_cast<const i32x2*>(bias_slot + c * 2);
+        bias[x][0] = __uint_as_float((uint32_t)v[0] << 16);
+        bias[x][1] = __uint_as_float((uint32_t)v[0] & 0xFFFF0000u);
+        bias[x][2] = __uint_as_float((uint32_t)v[1] << 16);
+        bias[x][3] = __uint_as_float((uint32_t)v[1] & 0xFFFF0000u);
       }
-      // this lane's 8 columns after the swap start at cl; a store is in or
-      // out of the tile as a whole (ncols is a multiple of 8)
-      const int cl = it.cbase + fn * 32 + 8 * (gp + kh);
-      const bool col_ok = cl < it.ncols;
+    }
+  };
+  // rows srow + 8 i of the staged block back out, as whole row segments;
+  // col0: the block's first column in the tile, cw: columns per chunk
+  auto drain = [&](int fm, int col0, int cw) __attribute__((always_inline)) {
 #pragma unroll
-      for (int fm = 0; fm < FMA; ++fm) {
-        const int voff = col_ok ? (it.rbase + fm * 32) * N * C::es_out + row_lane + cl * C::es_out
-                                : (int)0x80000000;
-        float v[2][4];
+    for (int i = 0; i < 4; ++i) {
+      const int row = srow + 8 * i;
+      const i32x4 d = *reinterpret_cast<const i32x4*>(stg + row * 128 + ((schunk ^ swz_out(row)) << 4));
+      const int col = col0 + cw * schunk;
+      const int voff = col < it.ncols ? (it.rbase + fm * 32 + row) * N * C::es_out + col * C::es_out
+                                      : (int)0x80000000;
+      __builtin_amdgcn_raw_buffer_store_b128(d, ro, voff, 0, 0);
+    }
+  };
+  auto stage_write = [&](int chunk, i32x4 v) __attribute__((always_inline)) {
+    *reinterpret_cast<i32x4*>(stg + wr_row + ((chunk ^ swz_out(r32)) << 4)) = v;
+  };
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+  for (int fm = 0; fm < FMA; ++fm) {
+    if constexpr (C::OUT_F32) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[x][i] = acc[fm][fn][4 * (gp + x) + i] + bias[x][i];
-        if constexpr (C::OUT_F32) {
+      for (int fn = 0; fn < C::FN; ++fn) {
+#pragma unroll
+        for (int gp = 0; gp < 4; gp += 2) {
+          float bias[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+          if (has_bias) load_bias(fn, gp, bias);
           int lo[4], hi[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0][i]), __float_as_uint(v[1][i]),
-                                                            false, false);
+            const auto r = __builtin_amdgcn_permlane32_swap(
+                __float_as_uint(acc[fm][fn][4 * gp + i] + bias[0][i]),
+                __float_as_uint(acc[fm][fn][4 * (gp + 1) + i] + bias[1][i]), false, false);
             lo[i] = (int)r[0];
             hi[i] = (int)r[1];
           }
-          __builtin_amdgcn_raw_buffer_store_b128(i32x4{lo[0], lo[1], lo[2], lo[3]}, ro, voff, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b128(i32x4{hi[0], hi[1], hi[2], hi[3]}, ro, voff + 16, 0, 0);
-        } else {
+          // 32 columns of 4 bytes per staging row: chunks 2 (gp + kh) + {0, 1}
+          stage_write(2 * (gp + kh), i32x4{lo[0], lo[1], lo[2], lo[3]});
+          stage_write(2 * (gp + kh) + 1, i32x4{hi[0], hi[1], hi[2], hi[3]});
+        }
+        drain(fm, it.cbase + fn * 32, 4);
+      }
+    } else {
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) {
+#pragma unroll
+        for (int gp = 0; gp < 4; gp += 2) {
+          float bias[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+          if (has_bias) load_bias(fn, gp, bias);
           uint32_t x0[2], x1[2];
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
-            x0[x] = (uint32_t)f32_to_bf16_rne(v[x][0]) | ((uint32_t)f32_to_bf16_rne(v[x][1]) << 16);
-            x1[x] = (uint32_t)f32_to_bf16_rne(v[x][2]) | ((uint32_t)f32_to_bf16_rne(v[x][3]) << 16);
+            const int g = 4 * (gp + x);
+            x0[x] = (uint32_t)f32_to_bf16_rne(acc[fm][fn][g] + bias[x][0]) |
+                    ((uint32_t)f32_to_bf16_rne(acc[fm][fn][g + 1] + bias[x][1]) << 16);
+            x1[x] = (uint32_t)f32_to_bf16_rne(acc[fm][fn][g + 2] + bias[x][2]) |
+                    ((uint32_t)f32_to_bf16_rne(acc[fm][fn][g + 3] + bias[x][3]) << 16);
           }
           const auto r0 = __builtin_amdgcn_permlane32_swap(x0[0], x0[1], false, false);
           const auto r1 = __builtin_amdgcn_permlane32_swap(x1[0], x1[1], false, false);
-          __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1]}, ro, voff,
-                                                 0, 0);
+          // 64 columns of 2 bytes per staging row: chunk 4 fn + gp + kh
+          stage_write(4 * fn + gp + kh, i32x4{(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1]});
         }
       }
+      drain(fm, it.cbase, 8);
     }
   }
   // a half tile pads to the full tile's store count with range-dropped stores
@@ -532,6 +565,9 @@ __global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
     constexpr int NM = 2 * FMA * C::FN;  // MFMAs per step
     constexpr int NOPS = BIAS ? C::DMA_OPS : C::DMA_STEP;
     wait_vmcnt<WAIT>();
+    // in a tile's last step every wave's reads of the current stage are
+    // complete past the barrier: the epilogue stages its output there
+    if constexpr (LAST) __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
     ring_barrier();
     const TileDma<C>& d = NEXT ? dnxt : dcur;
     char* st3 = smem + ((stage + 3) & (C::S - 1)) * C::STAGE;
@@ -582,7 +618,10 @@ __global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
     kstep(full_tag, W1{}, T_{}, T_{}, F_{}, 0);  // kt = KT-3: the next tile's step 0 and bias row
     kstep(full_tag, W2{}, T_{}, F_{}, F_{}, 1);
     kstep(full_tag, W1{}, T_{}, F_{}, T_{}, 2);
-    big_epilogue<C, FMA>(p, acc, cur, bias0 + par * C::BIAS_SLOT, kh, r32);
+    // the last step's stage (the next tile's step 3 goes there after its
+    // first barrier) holds the epilogue's staging slices, 4 KB per wave
+    big_epilogue<C, FMA>(p, acc, cur, bias0 + par * C::BIAS_SLOT,
+                         smem + ((stage + 3) & (C::S - 1)) * C::STAGE + w * 4096, kh, r32, lane);
   };
 
   while (true) {
