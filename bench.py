@@ -74,7 +74,7 @@ def op_peak(case):
     return "bf16", PEAK["bf16"]
 
 
-def cpu_baseline(cases, target_s: float = 12.0):
+def cpu_baseline(cases, target_s: float = 20.0):
     """Time the oracle on a bounded sample of each case: a few rows of a few
     groups, packed into a sub-problem with the same K, N and weights (every
     row costs the same arithmetic as in the full problem)."""
@@ -89,9 +89,10 @@ def cpu_baseline(cases, target_s: float = 12.0):
     flops_total = 0.0
     secs_total = 0.0
     descr = []
-    # calibrate on a handful of rows, then size the sample to ~target_s
-    rows_per = 4
-    for phase in ("calibrate", "measure"):
+    # calibrate, then size the sample to ~target_s (re-measuring while the
+    # sample ran well short of it: per-group setup dominates small samples)
+    rows_per = 16
+    for phase in ("calibrate", "calibrate", "measure"):
         flops_total = secs_total = 0.0
         descr = []
         for case in cases:
@@ -122,51 +123,77 @@ def cpu_baseline(cases, target_s: float = 12.0):
         if phase == "calibrate":
             scale = target_s / max(secs_total, 1e-3)
             rows_per = max(1, int(rows_per * scale))
+            if secs_total > 0.5 * target_s:
+                break
     return {"value": flops_total / secs_total / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": "; ".join(descr) + f" (fp64 oracle, {secs_total:.1f} s)"}
 
 
 class ClockSampler:
-    """Samples the shader clock and socket power with amd-smi in a
-    background thread while the timed steps run (read-only queries)."""
+    """Samples the shader clock and socket power with amd-smi (read-only
+    queries) from a shell loop started as a child process before this
+    process touches the GPU; the samples taken while the timed steps run
+    are kept."""
+
+    LOOP = "while true; do date +T%s.%N; amd-smi metric -c -p 2>/dev/null; sleep 0.2; done"
 
     def __init__(self):
-        import threading
-        self.samples = []
-        self._stop = threading.Event()
-        self._t = threading.Thread(target=self._run, daemon=True)
-
-    def _run(self):
-        import re
+        import shutil
         import subprocess
-        while not self._stop.is_set():
+        import tempfile
+        self.proc = None
+        self.path = None
+        # a profiler's preloaded library has initialised the GPU already: no
+        # child process may be started from here then
+        profiled = "rocprof" in os.environ.get("LD_PRELOAD", "") or any(
+            k.startswith("ROCPROF") for k in os.environ)
+        if profiled or shutil.which("amd-smi") is None:
+            return
+        fd, self.path = tempfile.mkstemp(prefix="bench_clock_", suffix=".txt")
+        self.fh = os.fdopen(fd, "w")
+        try:
+            self.proc = subprocess.Popen(["bash", "-c", self.LOOP], stdout=self.fh, stderr=subprocess.DEVNULL)
+        except OSError:
+            self.fh.close()
+            os.unlink(self.path)
+            self.path = None
+
+    def stop(self):
+        if self.proc is not None and self.proc.poll() is None:
+            self.proc.terminate()
             try:
-                txt = subprocess.run(["amd-smi", "metric", "-c", "-p"], capture_output=True, text=True,
-                                     timeout=10).stdout
-            except (OSError, subprocess.SubprocessError):
-                return
-            clk = [int(x) for x in re.findall(r"GFX_\d+:\s*CLK:\s*(\d+) MHz", txt.replace("\n", " "))]
-            pw = re.findall(r"SOCKET_POWER:\s*(\d+) W", txt)
-            if clk:
-                self.samples.append((sum(clk) / len(clk), int(pw[0]) if pw else None))
-            self._stop.wait(0.2)
+                self.proc.wait(timeout=10)
+            except Exception:
+                self.proc.kill()
+            self.fh.close()
 
-    def __enter__(self):
-        self._t.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        self._t.join(timeout=15)
-
-    def summary(self):
-        if not self.samples:
+    def summary(self, t0: float, t1: float):
+        """Mean clock and power over samples stamped in [t0, t1] (epoch s)."""
+        import re
+        if self.path is None:
             return None
-        mhz = statistics.mean(c for c, _ in self.samples)
-        pw = [p for _, p in self.samples if p is not None]
-        return {"sclk_mhz": round(mhz), "socket_power_w": round(statistics.mean(pw)) if pw else None,
-                "samples": len(self.samples)}
+        with open(self.path) as fh:
+            txt = fh.read()
+        os.unlink(self.path)
+        clk, pw = [], []
+        for block in txt.split("T")[1:]:
+            try:
+                ts = float(block.split()[0])
+            except (ValueError, IndexError):
+                continue
+            if not (t0 <= ts <= t1):
+                continue
+            c = [int(x) for x in re.findall(r"CLK:\s*(\d+) MHz", block)]
+            p = re.findall(r"SOCKET_POWER:\s*(\d+) W", block)
+            if c:
+                clk.append(sum(c) / len(c))
+            if p:
+                pw.append(int(p[0]))
+        if not clk:
+            return None
+        return {"sclk_mhz": round(statistics.mean(clk)), "samples": len(clk),
+                "socket_power_w": round(statistics.mean(pw)) if pw else None}
 
 
 def main():
@@ -184,6 +211,10 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
+
+    clock = ClockSampler()  # before the first GPU call: it starts a child process
+    import atexit
+    atexit.register(clock.stop)
 
     import torch
 
@@ -216,23 +247,28 @@ def main():
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in cases] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    with ClockSampler() as clock:
-        t0 = time.perf_counter()
-        for s in range(args.steps):
-            for i in range(len(cases)):
-                if evict:
-                    scratch.fill_(s & 0xFF)
-                ev[s][i][0].record(stream)
-                launch(i)
-                ev[s][i][1].record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        # hold the clock sampler until it has read at least once under load
-        t_hold = time.perf_counter()
-        while not clock.samples and time.perf_counter() - t_hold < 5:
+    epoch0 = time.time()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i in range(len(cases)):
+            if evict:
+                scratch.fill_(s & 0xFF)
+            ev[s][i][0].record(stream)
+            launch(i)
+            ev[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # the timed steps are too short for the clock sampler (about one reading
+    # a second): the same steps keep running, untimed, for a few seconds and
+    # the readings over both spans describe the clock under this load
+    epoch1 = time.time()
+    if clock.proc is not None:
+        while time.time() - epoch1 < 3.0:
             for i in range(len(cases)):
                 launch(i)
             torch.cuda.synchronize()
+        epoch1 = time.time()
+    clock.stop()
 
     per_kernel_ms = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
                      for i in range(len(cases))]
@@ -261,7 +297,7 @@ def main():
     roof["traffic"] = measured_traffic(dc.name)
     roof["kernel"] = dc.name
     roof["avg_launch_ms"] = avg_ms
-    clk = clock.summary()
+    clk = clock.summary(epoch0, epoch1)
     if clk:
         # the chip runs below its 2.4 GHz peak clock when power-limited:
         # the fraction of the peak at the observed clock, for context
