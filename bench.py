@@ -32,7 +32,8 @@ PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # dense MFMA TFLOP/s (MI3
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "moe_grouped_matrix_amd", "csrc", f)
-                  for f in ("gmm_device.hpp", "gmm_big.hpp", "gmm_params.hpp", "gmm_kernels.hip")]
+                  for f in ("gmm_device.hpp", "gmm_big.hpp", "gmm_stream.hpp", "gmm_params.hpp",
+                            "gmm_kernels.hip")]
 # workloads whose weights fit in the caches between calls: each timed call
 # starts from evicted L2 / Infinity Cache (a 512 MB write outside the events)
 EVICT = {"decode_fp8w", "tiny_fp32"}

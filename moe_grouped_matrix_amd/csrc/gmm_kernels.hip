@@ -4,6 +4,7 @@
 
 #include "gmm_big.hpp"
 #include "gmm_device.hpp"
+#include "gmm_stream.hpp"
 #include "gmm_launch.hpp"
 
 namespace gmmk {
@@ -61,6 +62,26 @@ hipError_t launch_big(const Params& p, int cu_count, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <class C>
+hipError_t launch_stream(const Params& p, int cu_count, hipStream_t stream) {
+  const long long n_tiles = (p.N + C::BN - 1) / C::BN;
+  const long long m_tiles = (p.M + C::BM - 1) / C::BM + p.Ga;
+  long long grid = cu_count;  // one workgroup per CU (LDS-bound)
+  if (grid > m_tiles * n_tiles && m_tiles * n_tiles >= 8) grid = m_tiles * n_tiles;
+  if (grid >= 8) grid -= grid % 8;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(gmm_stream_kernel<C>, dim3((unsigned)grid), dim3(C::T), 0, stream, p);
+  return hipGetLastError();
+}
+
+// The weight-streaming kernel takes bf16 x e4m3 NT problems with few rows per
+// group: K in stages of 128 with at least S of them per tile, and scale
+// blocks of exactly one stage (or no scale).
+inline bool stream_fits(const Params& p) {
+  return p.K % 128 == 0 && p.K >= StreamCfg<false>::S * 128 && p.lhs_scale == nullptr &&
+         (p.rhs_scale == nullptr || p.blk == 128);
+}
+
 template <Op OP, bool NN, bool BF8, bool SC>
 hipError_t by_size(const Params& p, SizeClass sz, int cu, hipStream_t st) {
   if constexpr (OP == Op::F32) return launch_cfg<Cfg<Op::F32, NN, false, 64, 64, 2, 2, SC>>(p, cu, st);
@@ -69,6 +90,12 @@ hipError_t by_size(const Params& p, SizeClass sz, int cu, hipStream_t st) {
     if (sz == SizeClass::Big && p.K >= 5 * 32) {
       if (p.out_f32) return launch_big<BigCfg<NN, true>>(p, cu, st);
       return launch_big<BigCfg<NN, false>>(p, cu, st);
+    }
+  }
+  if constexpr (OP == Op::BF16 && BF8 && !NN) {
+    if (sz == SizeClass::Small && stream_fits(p)) {
+      if (p.out_f32) return launch_stream<StreamCfg<true>>(p, cu, st);
+      return launch_stream<StreamCfg<false>>(p, cu, st);
     }
   }
   if (sz == SizeClass::Big) return launch_cfg<typename Pick<OP, NN, BF8, SC, SizeClass::Big>::type>(p, cu, st);

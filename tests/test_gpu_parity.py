@@ -234,3 +234,44 @@ def test_host_validation_errors():
         m.gmm(lhs, rhs.to(torch.float8_e4m3fn).transpose(1, 2).contiguous(), gs, transpose_rhs=True)
     with pytest.raises(m.GmmUnsupported):
         m.gmm(lhs.float(), rhs, gs)
+
+
+STREAM_CASES = [
+    # (K, N, out dtype, bias: None | bf16 | f32, scaled, rhs_scale block)
+    (768, 328, torch.bfloat16, "bf16", True),
+    (896, 640, torch.float32, "f32", True),
+    (1024, 192, torch.bfloat16, None, False),
+    (768, 256, torch.bfloat16, "bf16", "blk256"),
+]
+
+
+@pytest.mark.parametrize("K,N,out_dtype,bias,scaled", STREAM_CASES,
+                         ids=["bf16out_bias", "f32out_f32bias", "noscale_nobias", "blk256"])
+def test_weight_streaming_kernel(K, N, out_dtype, bias, scaled):
+    """bf16 x e4m3 with few rows per group and K >= 768 runs the weight-streaming
+    kernel: every element against the oracle, with empty groups, a group
+    offset, an N tail (N not a multiple of the 64-column tile), rows outside
+    the active groups, f32 and bf16 outputs and biases, no scale, and scale
+    blocks of two K stages."""
+    import moe_grouped_matrix_amd as m
+    m.set_tile_policy(0)
+    case = workloads.decode_fp8_weight(tokens=48, experts=24, K=K, N=N, forced_empty=8,
+                                       group_offset=4, num_active=14, device="cuda")
+    if bias is None:
+        case.rhs_bias = None
+    elif bias == "f32":
+        case.rhs_bias = case.rhs_bias.float().contiguous()
+    if scaled is False:
+        case.rhs_scale = None
+    elif scaled == "blk256":
+        # per-256-K blocks: pairs of 128-K block scales merged (any positive values)
+        case.rhs_scale = case.rhs_scale[:, ::2].contiguous() * 1.5
+    case.out_dtype = out_dtype
+    print(f"stream case K={K} N={N} out={out_dtype} bias={bias} scaled={scaled} M={case.M} "
+          f"Ga={case.num_active} active_rows={case.active_rows()}", flush=True)
+    out = run_gpu(case)
+    lo, hi = active_range(case)
+    assert_zero_rows(out, lo, hi)
+    ref = reference(case)
+    compare(out.cpu()[lo:hi], ref[lo:hi], out_dtype, f"stream K={K} N={N}")
+    assert m.device_flags() == 0
