@@ -441,10 +441,13 @@ __device__ __forceinline__ void big_epilogue(const Params& p, const f32x16 (&acc
       drain(fm, it.cbase, 8);
     }
   }
-  // a half tile pads to the full tile's store count with range-dropped stores
+  // a half tile pads to the full tile's store count with range-dropped
+  // stores, each to an address of its own: the compiler deletes a store that
+  // repeats an earlier one, and every dropped one would leave the K loop's
+  // constant waits one operation short
 #pragma unroll
   for (int i = FMA * C::FN * C::ST_BLOCK; i < C::E; ++i)
-    __builtin_amdgcn_raw_buffer_store_b128(i32x4{0, 0, 0, 0}, ro, (int)0x80000000, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(i32x4{0, 0, 0, 0}, ro, (int)0x80000000, 64 * i, 0);
 }
 
 template <class C>

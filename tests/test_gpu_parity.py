@@ -237,25 +237,31 @@ def test_host_validation_errors():
 
 
 STREAM_CASES = [
-    # (K, N, out dtype, bias: None | bf16 | f32, scaled, rhs_scale block)
-    (768, 328, torch.bfloat16, "bf16", True),
-    (896, 640, torch.float32, "f32", True),
-    (1024, 192, torch.bfloat16, None, False),
-    (768, 256, torch.bfloat16, "bf16", "blk256"),
+    # (tokens, K, N, out dtype, bias: None | bf16 | f32, scaled, rhs_scale block)
+    (48, 768, 328, torch.bfloat16, "bf16", True),
+    (48, 896, 640, torch.float32, "f32", True),
+    (48, 1024, 192, torch.bfloat16, None, False),
+    (48, 768, 256, torch.bfloat16, "bf16", "blk256"),
+    (48, 640, 136, torch.bfloat16, "bf16", True),
+    (600, 1152, 264, torch.float32, "bf16", True),
 ]
 
 
-@pytest.mark.parametrize("K,N,out_dtype,bias,scaled", STREAM_CASES,
-                         ids=["bf16out_bias", "f32out_f32bias", "noscale_nobias", "blk256"])
-def test_weight_streaming_kernel(K, N, out_dtype, bias, scaled):
+@pytest.mark.parametrize("tokens,K,N,out_dtype,bias,scaled", STREAM_CASES,
+                         ids=["bf16out_bias", "f32out_f32bias", "noscale_nobias", "blk256", "k640_n136",
+                              "rows_over_32"])
+def test_weight_streaming_kernel(tokens, K, N, out_dtype, bias, scaled):
     """bf16 x e4m3 with few rows per group and K >= 768 runs the weight-streaming
     kernel: every element against the oracle, with empty groups, a group
-    offset, an N tail (N not a multiple of the 64-column tile), rows outside
-    the active groups, f32 and bf16 outputs and biases, no scale, and scale
-    blocks of two K stages."""
+    offset, N tails (N not a multiple of the 64-column tile, down to 8
+    columns past it), the fewest K stages the kernel takes (six), groups of
+    more than one 32-row tile, rows outside the active groups, f32 and bf16
+    outputs and biases, and no scale.  K = 640 (below its minimum) and scale
+    blocks of two K stages run on the general kernel, against the same
+    oracle."""
     import moe_grouped_matrix_amd as m
     m.set_tile_policy(0)
-    case = workloads.decode_fp8_weight(tokens=48, experts=24, K=K, N=N, forced_empty=8,
+    case = workloads.decode_fp8_weight(tokens=tokens, experts=24, K=K, N=N, forced_empty=8,
                                        group_offset=4, num_active=14, device="cuda")
     if bias is None:
         case.rhs_bias = None
@@ -267,7 +273,7 @@ def test_weight_streaming_kernel(K, N, out_dtype, bias, scaled):
         # per-256-K blocks: pairs of 128-K block scales merged (any positive values)
         case.rhs_scale = case.rhs_scale[:, ::2].contiguous() * 1.5
     case.out_dtype = out_dtype
-    print(f"stream case K={K} N={N} out={out_dtype} bias={bias} scaled={scaled} M={case.M} "
+    print(f"stream case tokens={tokens} K={K} N={N} out={out_dtype} bias={bias} scaled={scaled} M={case.M} "
           f"Ga={case.num_active} active_rows={case.active_rows()}", flush=True)
     out = run_gpu(case)
     lo, hi = active_range(case)
