@@ -6,7 +6,8 @@ or calls it, and it shares no code with the HIP path.
 
 The arithmetic lives in ``gmm_oracle.c`` (plain loops, fp64, k ascending);
 this module builds it with gcc, marshals torch CPU tensors into it, and holds
-the two tile-metadata definitions in ``worklist.py``.  Citations refer to the
+the two tile-metadata definitions in ``worklist.py``.  ``tgmm_reference`` is
+the weight-gradient product (lhs_g^T . rhs_g per group).  Citations refer to the
 tpu-inference 0.13.2 wheel diff page (megablox/gmm.py), the metrale
 gemm_quant.rs page and the MaxText PR page "Megablox: transposed-RHS gmm_v2
 kernel for the backward dlhs".
@@ -67,6 +68,11 @@ def _load():
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
         lib.oracle_round_bf16_array.restype = None
         lib.oracle_round_bf16_array.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.oracle_tgmm.restype = ctypes.c_int
+        lib.oracle_tgmm.argtypes = [vp, i32, i64, i64,
+                                    vp, i32, i64,
+                                    vp, i64, i64, i64,
+                                    vp, vp, i64, vp]
         lib.oracle_gmm.restype = ctypes.c_int
         lib.oracle_gmm.argtypes = [vp, i32, i64, i64,
                                    vp, i32, i64, i64, i32,
@@ -163,6 +169,48 @@ def gmm_reference(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tenso
         raise OracleError({E_ARG: "invalid arguments", E_DATA: "invalid group sizes / offset",
                            E_NOMEM: "out of memory"}.get(rc, str(rc)))
     return (out, rg) if return_row_group else out
+
+
+def tgmm_reference(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,
+                   group_offset: int = 0, num_active: Optional[int] = None,
+                   select: Optional[Sequence[Sequence[int]]] = None) -> np.ndarray:
+    """Reference values of tgmm(lhs, rhs, group_sizes) in float64: for active
+    group h (group group_offset + h), lhs_g^T . rhs_g over the group's rows,
+    zero for an empty group -- the weight gradient of gmm (gmm_oracle.c,
+    oracle_tgmm).
+
+    lhs [M,K], rhs [M,N]; group_sizes [G] int32; num_active defaults to
+    G - group_offset.  ``select`` is a list of (h, k) pairs (output rows);
+    when None every row.  Returns float64 [Ga,K,N], or [len(select),N]."""
+    lib = _load()
+    lhs, rhs, gs = _cpu(lhs), _cpu(rhs), _cpu(group_sizes)
+    if lhs.dim() != 2 or rhs.dim() != 2 or gs.dim() != 1 or gs.dtype != torch.int32:
+        raise OracleError("bad ranks / group_sizes dtype")
+    M, K = lhs.shape
+    if rhs.shape[0] != M:
+        raise OracleError("lhs and rhs must have the same rows")
+    N = rhs.shape[1]
+    G = gs.shape[0]
+    Ga = G - int(group_offset) if num_active is None else int(num_active)
+    if select is None:
+        sh = sk = None
+        out = np.zeros((Ga, K, N), dtype=np.float64)
+        n_sel = Ga * K
+    else:
+        sel = np.ascontiguousarray(np.asarray(select, dtype=np.int64).reshape(-1, 2))
+        sh = np.ascontiguousarray(sel[:, 0])
+        sk = np.ascontiguousarray(sel[:, 1])
+        n_sel = sel.shape[0]
+        out = np.zeros((n_sel, N), dtype=np.float64)
+    rc = lib.oracle_tgmm(lhs.data_ptr(), _code(lhs, "lhs"), M, K,
+                         rhs.data_ptr(), _code(rhs, "rhs"), N,
+                         gs.data_ptr(), G, int(group_offset), Ga,
+                         None if sh is None else sh.ctypes.data, None if sk is None else sk.ctypes.data,
+                         n_sel, out.ctypes.data)
+    if rc != OK:
+        raise OracleError({E_ARG: "invalid arguments", E_DATA: "invalid group sizes / offset",
+                           E_NOMEM: "out of memory"}.get(rc, str(rc)))
+    return out
 
 
 def round_to(ref: np.ndarray, dtype: torch.dtype) -> torch.Tensor:

@@ -231,3 +231,61 @@ int oracle_gmm(const void* lhs, int lhs_dtype, int64_t M, int64_t K,
   free(o);
   return OR_OK;
 }
+
+/*
+ * oracle_tgmm: reference values of the transposed grouped matmul, the weight
+ * gradient of gmm.  The Megablox metadata builder (tpu-inference wheel diff
+ * page, megablox/gmm.py, make_group_metadata, argument visit_empty_groups)
+ * keeps a tile for every empty group because this operation must still write
+ * that group's output; the MaxText PR page "transposed-RHS gmm_v2 kernel for
+ * the backward dlhs" keeps it as the weight-gradient step of gmm's custom VJP.
+ * For the forward out_g = lhs_g . W_g (W_g [K, N], rows of group g), the
+ * gradient of sum(out . rhs) with respect to W_g is lhs_g^T . rhs_g:
+ *
+ *   out[h, k, n] = sum over r in [o[g], o[g+1]) of lhs[r, k] * rhs[r, n],
+ *                  g = s + h, r ascending, in double;
+ *   out[h] = 0 when group g is empty.
+ *
+ *   lhs          [M, K] of lhs_dtype, row-major.
+ *   rhs          [M, N] of rhs_dtype, row-major.
+ *   group_sizes  [G] int32; groups s .. s+Ga-1 are active (0 <= s,
+ *                s + Ga <= G).
+ *   sel_h, sel_k NULL (every (h, k), h-major) or n_sel pairs: output row k
+ *                of active group h.
+ *   out          [n_sel, N] double (n_sel = Ga * K when no selection).
+ *
+ * Returns OR_OK, OR_E_ARG, OR_E_DATA (invalid sizes or offset), OR_E_NOMEM.
+ */
+int oracle_tgmm(const void* lhs, int lhs_dtype, int64_t M, int64_t K,
+                const void* rhs, int rhs_dtype, int64_t N,
+                const int32_t* group_sizes, int64_t G, int64_t group_offset, int64_t Ga,
+                const int64_t* sel_h, const int64_t* sel_k, int64_t n_sel, double* out) {
+  if (M < 0 || K <= 0 || N <= 0 || Ga < 0 || G < 0) return OR_E_ARG;
+  if (!dtype_ok(lhs_dtype) || !dtype_ok(rhs_dtype)) return OR_E_ARG;
+  if ((sel_h == NULL) != (sel_k == NULL)) return OR_E_ARG;
+  if (sel_h == NULL) n_sel = Ga * K;
+  for (int64_t i = 0; i < n_sel && sel_h; ++i)
+    if (sel_h[i] < 0 || sel_h[i] >= Ga || sel_k[i] < 0 || sel_k[i] >= K) return OR_E_ARG;
+  const int64_t s = group_offset;
+  if (s < 0 || s + Ga > G) return OR_E_DATA;
+
+  int64_t* o = (int64_t*)malloc(sizeof(int64_t) * (size_t)(G + 1));
+  if (!o) return OR_E_NOMEM;
+  int rc = oracle_group_offsets(group_sizes, G, M, o);
+  if (rc != OR_OK) { free(o); return rc; }
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < n_sel; ++i) {
+    const int64_t h = sel_h ? sel_h[i] : i / K;
+    const int64_t k = sel_k ? sel_k[i] : i % K;
+    const int64_t lo = o[s + h], hi = o[s + h + 1];
+    double* row = out + i * N;
+    for (int64_t n = 0; n < N; ++n) row[n] = 0.0;
+    for (int64_t r = lo; r < hi; ++r) {
+      const double a = load_elem(lhs, lhs_dtype, r * K + k);
+      for (int64_t n = 0; n < N; ++n) row[n] += a * load_elem(rhs, rhs_dtype, r * N + n);
+    }
+  }
+  free(o);
+  return OR_OK;
+}
