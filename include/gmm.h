@@ -131,6 +131,43 @@ gmm_status gmm_run(gmm_handle* h,
                    void* stream);
 
 /*
+ * gmm_tgmm_run: queue the transposed grouped matmul, the weight gradient of
+ * gmm, on `stream`.  For each active group h = g - s (g = s .. s+Ga-1),
+ *
+ *   out[h,k,n] = sum over rows r in [o[g], o[g+1]) of lhs[r,k] * rhs[r,n],
+ *
+ * accumulated in fp32 and rounded once, to nearest even, to the output type;
+ * an empty group's out[h] is all +0.0.  For the forward gmm with an NN
+ * weight W [Ga,K,N] and output gradient dout, tgmm(lhs, dout) is dW; for an
+ * NT weight [Ga,N,K], tgmm(dout, lhs) is dW.  The Megablox metadata builder
+ * keeps a tile for every empty group because this product must still write
+ * its output (tpu-inference 0.13.2 wheel diff page, megablox/gmm.py,
+ * make_group_metadata, visit_empty_groups); the MaxText PR "Megablox:
+ * transposed-RHS gmm_v2 kernel for the backward dlhs" keeps it as the
+ * weight-gradient step (drhs) of the custom VJP.
+ *
+ *   lhs          [M,K] BF16.
+ *   rhs          [M,N] BF16 (the same rows as lhs).
+ *   group_sizes  [G] I32 on the device, 1 <= G <= 1024.
+ *   group_offset NULL (s = 0) or a device pointer to one int32 s.
+ *   out          [Ga,K,N], F32 or BF16, Ga <= G.  Every element is written.
+ *                out must not overlap an input.
+ *
+ * Size limits: K % 8 == 0, N % 8 == 0, M*K*2 and M*N*2 below 2 GiB, Ga*K
+ * below 2^31.  Outside them the call returns GMM_E_UNSUPPORTED and queues
+ * nothing; shape or dtype inconsistencies return GMM_E_INVALID; a launch
+ * failure returns GMM_E_HIP.  Invalid device-resident sizes or offset are
+ * clamped and reported through gmm_device_flags, as for gmm_run.
+ */
+gmm_status gmm_tgmm_run(gmm_handle* h,
+                        const gmm_tensor* lhs,
+                        const gmm_tensor* rhs,
+                        const gmm_tensor* group_sizes,
+                        const int32_t* group_offset,
+                        const gmm_tensor* out,
+                        void* stream);
+
+/*
  * gmm_device_flags: synchronise `stream`, return the GMM_FLAG_* bits that
  * runs on this handle have set since the last call, and clear them.
  * Returns GMM_E_DEVICE_DATA when any bit was set, GMM_OK otherwise.

@@ -20,7 +20,7 @@ GMM_F32, GMM_BF16, GMM_F8E4M3FN, GMM_I32 = 0, 1, 2, 3
 GMM_OK, GMM_E_INVALID, GMM_E_UNSUPPORTED, GMM_E_HIP, GMM_E_DEVICE_DATA = 0, -1, -2, -3, -4
 FLAG_NEGATIVE_SIZE, FLAG_SIZES_EXCEED_M, FLAG_BAD_OFFSET = 0x1, 0x2, 0x4
 
-EXPORTED = ("gmm_create", "gmm_destroy", "gmm_last_error", "gmm_run", "gmm_device_flags",
+EXPORTED = ("gmm_create", "gmm_destroy", "gmm_last_error", "gmm_run", "gmm_tgmm_run", "gmm_device_flags",
             "gmm_set_tile_policy", "gmm_debug_worklist")
 
 _DTYPE = {torch.float32: GMM_F32, torch.bfloat16: GMM_BF16,
@@ -73,6 +73,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.gmm_last_error.restype = ctypes.c_char_p
             lib.gmm_run.argtypes = [vp, tp, tp, tp, tp, tp, tp, vp, ctypes.c_int, tp, vp]
             lib.gmm_run.restype = ctypes.c_int
+            lib.gmm_tgmm_run.argtypes = [vp, tp, tp, tp, vp, tp, vp]
+            lib.gmm_tgmm_run.restype = ctypes.c_int
             lib.gmm_device_flags.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
             lib.gmm_device_flags.restype = ctypes.c_int
             lib.gmm_set_tile_policy.argtypes = [vp, ctypes.c_int]
@@ -180,6 +182,38 @@ def gmm(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,
     st = stream if stream is not None else torch.cuda.current_stream(dev)
     status = lib.gmm_run(h, *[_ref(v) for v in views[:6]], off_ptr, int(bool(transpose_rhs)),
                          _ref(views[6]), ctypes.c_void_p(st.cuda_stream))
+    if keep is not None and status == GMM_OK:
+        keep.record_stream(st)
+    _raise(status, h)
+    return out
+
+
+def tgmm(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,
+         num_active: Optional[int] = None,
+         out_dtype: torch.dtype = torch.float32,
+         group_offset=None,
+         out: Optional[torch.Tensor] = None,
+         stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Transposed grouped matmul (the weight gradient of gmm) through
+    libgmm.so: out[h] = lhs_g^T . rhs_g over the rows of group g = s + h,
+    zero for an empty group.
+
+    lhs [M,K] and rhs [M,N] bf16; group_sizes int32 [G] on the device;
+    num_active Ga defaults to G minus an integer group_offset (or to G when
+    the offset is a device tensor).  Returns out [Ga,K,N] of out_dtype."""
+    lib = load()
+    dev = lhs.device
+    h = handle(dev)
+    if out is None:
+        if num_active is None:
+            s = int(group_offset) if isinstance(group_offset, int) else 0
+            num_active = group_sizes.numel() - s
+        out = torch.empty((num_active, lhs.shape[1], rhs.shape[1]), dtype=out_dtype, device=dev)
+    views = [_view(t, n) for t, n in ((lhs, "lhs"), (rhs, "rhs"), (group_sizes, "group_sizes"), (out, "out"))]
+    off_ptr, keep = _offset_ptr(group_offset, dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    status = lib.gmm_tgmm_run(h, *[_ref(v) for v in views[:3]], off_ptr, _ref(views[3]),
+                              ctypes.c_void_p(st.cuda_stream))
     if keep is not None and status == GMM_OK:
         keep.record_stream(st)
     _raise(status, h)

@@ -259,6 +259,67 @@ gmm_status gmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs,
   return GMM_OK;
 }
 
+gmm_status gmm_tgmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs,
+                        const gmm_tensor* group_sizes, const int32_t* group_offset, const gmm_tensor* out,
+                        void* stream) {
+  if (!h) return GMM_E_INVALID;
+  h->err.clear();
+  if (!lhs || !rhs || !group_sizes || !out) return fail(h, GMM_E_INVALID, "lhs, rhs, group_sizes and out are required");
+  if (lhs->ndim != 2 || rhs->ndim != 2) return fail(h, GMM_E_INVALID, "expected 2-tensors for lhs and rhs");
+  if (group_sizes->ndim != 1 || group_sizes->dtype != GMM_I32)
+    return fail(h, GMM_E_INVALID, "expected a 1-d int32 group_sizes");
+  if (out->ndim != 3) return fail(h, GMM_E_INVALID, "expected a 3-tensor [Ga,K,N] for out");
+  const long long M = lhs->shape[0], K = lhs->shape[1], N = rhs->shape[1];
+  const long long G = group_sizes->shape[0], Ga = out->shape[0];
+  if (rhs->shape[0] != M)
+    return fail(h, GMM_E_INVALID, "lhs and rhs must have the same rows: lhs " + shape_str(lhs) + ", rhs " + shape_str(rhs));
+  if (M < 0 || K <= 0 || N <= 0 || Ga < 0) return fail(h, GMM_E_INVALID, "negative or zero extent");
+  if (out->shape[1] != K || out->shape[2] != N)
+    return fail(h, GMM_E_INVALID, "out must be [Ga," + std::to_string(K) + "," + std::to_string(N) + "], got " + shape_str(out));
+  if (lhs->dtype != GMM_BF16 || rhs->dtype != GMM_BF16) {
+    if (elem_size(lhs->dtype) == 0 || elem_size(rhs->dtype) == 0 || lhs->dtype == GMM_I32 || rhs->dtype == GMM_I32)
+      return fail(h, GMM_E_INVALID, "unsupported lhs / rhs dtype");
+    return fail(h, GMM_E_UNSUPPORTED, "tgmm takes bf16 lhs and rhs");
+  }
+  if (out->dtype != GMM_F32 && out->dtype != GMM_BF16) return fail(h, GMM_E_INVALID, "out must be f32 or bf16");
+  if (G < 1) return fail(h, GMM_E_INVALID, "group_sizes must hold at least one group");
+  if (Ga > G) return fail(h, GMM_E_INVALID, "out holds more groups than group_sizes");
+  if (G > gmmk::kMaxGroups) return fail(h, GMM_E_UNSUPPORTED, "more than 1024 groups");
+  if (K % 8 || N % 8) return fail(h, GMM_E_UNSUPPORTED, "K and N must be multiples of 8");
+  if (M * K * 2 >= 0x7FFFFFF0LL || M * N * 2 >= 0x7FFFFFF0LL || Ga * K >= (1LL << 31))
+    return fail(h, GMM_E_UNSUPPORTED, "an operand beyond 2 GiB or Ga*K beyond 2^31");
+  const gmm_tensor* ins[] = {lhs, rhs, group_sizes};
+  for (const gmm_tensor* t : ins) {
+    if (numel(t) > 0 && !t->data) return fail(h, GMM_E_INVALID, "null data pointer");
+    if (!aligned16(t->data)) return fail(h, GMM_E_INVALID, "tensor data must be 16-byte aligned");
+    if (overlaps(t, out)) return fail(h, GMM_E_INVALID, "out overlaps an input");
+  }
+  if (Ga > 0 && !out->data) return fail(h, GMM_E_INVALID, "null out pointer");
+  if (!aligned16(out->data) || !aligned16(group_offset))
+    return fail(h, GMM_E_INVALID, "out and group_offset must be 16-byte aligned");
+  if (Ga == 0) return GMM_OK;
+
+  gmmk::Params p{};
+  p.lhs = lhs->data;
+  p.rhs = rhs->data;
+  p.group_sizes = static_cast<const int32_t*>(group_sizes->data);
+  p.group_offset = group_offset;
+  p.out = const_cast<void*>(out->data);
+  p.flags = h->flags;
+  p.M = (int32_t)M;
+  p.K = (int32_t)K;
+  p.N = (int32_t)N;
+  p.G = (int32_t)G;
+  p.Ga = (int32_t)Ga;
+  p.nb = 1;
+  p.blk = (int32_t)K;
+  p.out_f32 = out->dtype == GMM_F32;
+  DeviceGuard g(h->device);
+  hipError_t e = gmmk::launch_tgmm(p, h->cu_count, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(h, GMM_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return GMM_OK;
+}
+
 gmm_status gmm_device_flags(gmm_handle* h, void* stream, uint32_t* flags) {
   if (!h || !flags) return GMM_E_INVALID;
   DeviceGuard g(h->device);

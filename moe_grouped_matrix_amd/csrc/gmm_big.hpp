@@ -621,6 +621,15 @@ __global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
     kstep(full_tag, W1{}, T_{}, T_{}, F_{}, 0);  // kt = KT-3: the next tile's step 0 and bias row
     kstep(full_tag, W2{}, T_{}, F_{}, F_{}, 1);
     kstep(full_tag, W1{}, T_{}, F_{}, T_{}, 2);
+    // The weight fragments of an [G,K,N] weight come from transpose reads,
+    // whose registers are written when the data arrives; after the last tile
+    // the refills have no later use, so the compiler could give their
+    // registers to the epilogue while the reads are in flight.  Wait for
+    // them and use them here first.
+    if constexpr (C::NN) {
+      __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+      asm volatile("" ::"v"(b[0][0]), "v"(b[0][1]), "v"(b[1][0]), "v"(b[1][1]));
+    }
     // the last step's stage (the next tile's step 3 goes there after its
     // first barrier) holds the epilogue's staging slices, 4 KB per wave
     big_epilogue<C, FMA>(p, acc, cur, bias0 + par * C::BIAS_SLOT,

@@ -5,6 +5,7 @@
 #include "gmm_big.hpp"
 #include "gmm_device.hpp"
 #include "gmm_stream.hpp"
+#include "gmm_tgmm.hpp"
 #include "gmm_launch.hpp"
 
 namespace gmmk {
@@ -82,6 +83,18 @@ inline bool stream_fits(const Params& p) {
          (p.rhs_scale == nullptr || p.blk == 128);
 }
 
+// One workgroup per CU (LDS-bound), at most one per tile.
+template <class C>
+hipError_t launch_tgmm_cfg(const Params& p, int cu_count, hipStream_t stream) {
+  const long long items = (long long)p.Ga * ((p.K + C::BM - 1) / C::BM) * ((p.N + C::BN - 1) / C::BN);
+  long long grid = cu_count;
+  if (grid > items && items >= 8) grid = items;
+  if (grid >= 8) grid -= grid % 8;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(gmm_tgmm_kernel<C>, dim3((unsigned)grid), dim3(C::T), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <Op OP, bool NN, bool BF8, bool SC>
 hipError_t by_size(const Params& p, SizeClass sz, int cu, hipStream_t st) {
   if constexpr (OP == Op::F32) return launch_cfg<Cfg<Op::F32, NN, false, 64, 64, 2, 2, SC>>(p, cu, st);
@@ -133,6 +146,11 @@ hipError_t launch_gmm(const Params& p, const KernelChoice& c, int cu, hipStream_
       return by_scaled<Op::FP8, false, false>(p, c, cu, st);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_tgmm(const Params& p, int cu, hipStream_t st) {
+  if (p.out_f32) return launch_tgmm_cfg<TgCfg<true>>(p, cu, st);
+  return launch_tgmm_cfg<TgCfg<false>>(p, cu, st);
 }
 
 hipError_t launch_worklist(const Params& p, int tm, int32_t* tiles, long long capacity,

@@ -27,6 +27,9 @@ int tile_m(const KernelChoice& c);
 // Queue the gmm kernel.  Returns hipSuccess or the launch error.
 hipError_t launch_gmm(const Params& p, const KernelChoice& c, int cu_count, hipStream_t stream);
 
+// Queue the transposed grouped matmul (out [Ga,K,N]).
+hipError_t launch_tgmm(const Params& p, int cu_count, hipStream_t stream);
+
 // Queue the worklist export kernel (one workgroup).
 hipError_t launch_worklist(const Params& p, int tm, int32_t* tiles, long long capacity,
                            int32_t* count, hipStream_t stream);

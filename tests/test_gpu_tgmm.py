@@ -1,0 +1,110 @@
+"""GPU parity of the transposed grouped matmul (the weight gradient of gmm)
+against the oracle, through the C ABI (gmm_tgmm_run).
+
+Small cases compare every element: contraction tails (group sizes that are
+not multiples of the 32-row step), groups shorter than the kernel's five
+steps, empty groups (all-zero bits), K and N tails past the 256-column tiles
+(down to 8 columns), a group offset, f32 and bf16 outputs, rows outside the
+active groups (ignored), and invalid device sizes (clamped and flagged).  The
+full-size case (the forward workload's shapes) runs in the benchmark's
+launch configuration and compares sampled output rows.
+
+Tolerances are those of tests/parity.py (float32: max error 1e-4 of the
+largest reference value; bfloat16: relative Frobenius error 2e-2, globally
+and per row), and the float32 bound also per group."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import compare
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (group sizes, extra rows past the groups, K, N, out dtype, group offset, active groups)
+    ([70, 0, 33, 200, 5, 1, 130], 7, 264, 136, torch.float32, 0, None),
+    ([300, 0, 650, 17], 0, 512, 520, torch.bfloat16, 1, 3),
+    ([1000, 2000, 0, 777], 3, 256, 256, torch.float32, 0, None),
+    ([0, 0, 0], 4, 128, 64, torch.float32, 0, None),
+    ([4100, 96, 2500], 0, 1408, 704, torch.float32, 0, None),
+]
+IDS = ["tails_tiny_groups", "offset_bf16out", "exact_tiles", "all_empty", "model_shapes"]
+
+
+def _case(sizes, extra, K, N, seed):
+    g = torch.Generator().manual_seed(seed)
+    M = sum(sizes) + extra
+    lhs = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    rhs = torch.randn(M, N, generator=g).to(torch.bfloat16)
+    return lhs, rhs, torch.tensor(sizes, dtype=torch.int32)
+
+
+def _check(out, ref, sizes, s, out_dtype, what):
+    Ga, K, N = ref.shape
+    compare(out.reshape(Ga * K, N), ref.reshape(Ga * K, N), out_dtype, what)
+    for h in range(Ga):
+        if sizes[s + h] == 0:
+            assert torch.all(out[h].view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32) == 0), \
+                f"{what}: empty group {h} not all-zero bits"
+        elif out_dtype == torch.float32:
+            scale = np.abs(ref[h]).max()
+            err = np.abs(out[h].double().numpy() - ref[h]).max()
+            assert err <= 1e-4 * max(scale, 1e-30), f"{what}: group {h} max err {err} vs {scale}"
+
+
+@pytest.mark.parametrize("sizes,extra,K,N,out_dtype,s,ga", CASES, ids=IDS)
+def test_tgmm_against_oracle(sizes, extra, K, N, out_dtype, s, ga):
+    import moe_grouped_matrix_amd as m
+    lhs, rhs, gs = _case(sizes, extra, K, N, seed=len(sizes) * 1000 + K)
+    Ga = len(sizes) - s if ga is None else ga
+    print(f"tgmm case sizes={sizes} K={K} N={N} out={out_dtype} s={s} Ga={Ga}", flush=True)
+    out = m.tgmm(lhs.cuda(), rhs.cuda(), gs.cuda(), num_active=Ga, group_offset=s, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert m.device_flags() == 0
+    ref = oracle.tgmm_reference(lhs, rhs, gs, group_offset=s, num_active=Ga)
+    _check(out.cpu(), ref, sizes, s, out_dtype, f"tgmm {sizes} K={K} N={N}")
+
+
+def test_tgmm_invalid_sizes_are_clamped_and_flagged():
+    import moe_grouped_matrix_amd as m
+    sizes = [40, -3, 25]
+    lhs, rhs, _ = _case([40, 0, 25], 0, 64, 48, seed=5)
+    gs = torch.tensor(sizes, dtype=torch.int32)
+    out = m.tgmm(lhs.cuda(), rhs.cuda(), gs.cuda(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert m.device_flags() & m.FLAG_NEGATIVE_SIZE
+    ref = oracle.tgmm_reference(lhs, rhs, torch.tensor([40, 0, 25], dtype=torch.int32))
+    _check(out.cpu(), ref, [40, 0, 25], 0, torch.float32, "tgmm clamped sizes")
+
+
+def test_tgmm_full_size_sampled():
+    """The forward workload's shapes (262144 rows, 128 groups, K = N = 1408,
+    f32 out) in the benchmark's launch configuration; output rows sampled at
+    the k-tile boundaries and at random, for the largest, smallest and a
+    spread of other groups."""
+    import moe_grouped_matrix_amd as m
+    case = workloads.tgmm_bf16(device="cuda")
+    sizes = case.sizes_list()
+    print(f"tgmm full case M={case.M} K={case.K} N={case.N} Ga={case.num_active} "
+          f"sizes {min(sizes)}..{max(sizes)}", flush=True)
+    out = torch.empty((case.num_active, case.K, case.N), dtype=case.out_dtype, device="cuda")
+    m.tgmm(case.lhs, case.rhs, case.group_sizes, num_active=case.num_active, out=out)
+    torch.cuda.synchronize()
+    assert m.device_flags() == 0
+    order = np.argsort(sizes)
+    groups = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2])} |
+                    set(int(x) for x in np.random.default_rng(3).choice(len(sizes), 6, replace=False)))
+    ks = [0, 1, 127, 128, 255, 256, 1023, 1024, 1279, 1280, 1407]
+    rng = np.random.default_rng(4)
+    sel = [(h, k) for h in groups for k in ks] + [(int(h), int(k)) for h, k in
+                                                  zip(rng.integers(0, case.num_active, 24),
+                                                      rng.integers(0, case.K, 24))]
+    ref = oracle.tgmm_reference(case.lhs.cpu(), case.rhs.cpu(), case.group_sizes.cpu(),
+                                num_active=case.num_active, select=sel)
+    idx_h = torch.tensor([h for h, _ in sel], device="cuda")
+    idx_k = torch.tensor([k for _, k in sel], device="cuda")
+    got = out[idx_h, idx_k].cpu()
+    rel = compare(got, ref, case.out_dtype, f"tgmm full ({len(sel)} rows)")
+    print(f"tgmm full: {len(sel)} rows compared, error {rel:.3e}", flush=True)

@@ -56,3 +56,21 @@ def test_big_kernel_keeps_every_counted_store(kernel_asm):
         assert stores == 2 * E_FULL[out_f32], (name, stores)
         seen += 1
     assert seen == 4  # NT / NN x bf16 / f32 output
+
+
+def test_tgmm_kernel_keeps_every_counted_store(kernel_asm):
+    seen = 0
+    for name, lines in _functions(kernel_asm, r"_ZN4gmmk15gmm_tgmm_kernel"):
+        out_f32 = "true" if "TgCfgILb1E" in name else "false"
+        stores = sum(1 for ln in lines if ln.startswith("buffer_store"))
+        assert stores == 2 * E_FULL[out_f32], (name, stores)
+        seen += 1
+    assert seen == 2  # bf16 / f32 output
+
+
+def test_loop_kernels_do_not_spill(kernel_asm):
+    # a spill reload is a vector memory load: its wait would drain every
+    # direct-to-LDS load queued behind the K loop's constant counts
+    for pattern in (r"_ZN4gmmk15gmm_tgmm_kernel", r"_ZN4gmmk17gmm_stream_kernel"):
+        for name, lines in _functions(kernel_asm, pattern):
+            assert not any(ln.startswith("scratch_") for ln in lines), name

@@ -266,6 +266,71 @@ def w8a8_fp8(seed: int = 1005, device="cpu", tokens: int = 32768, experts: int =
                 meta=dict(tokens=tokens, experts=experts, top_k=top_k))
 
 
+@dataclasses.dataclass
+class TgmmCase:
+    """Inputs of the transposed grouped matmul (weight gradient):
+    out[h] = lhs_g^T . rhs_g over the rows of group g = group_offset + h."""
+    name: str
+    lhs: torch.Tensor               # [M,K]
+    rhs: torch.Tensor               # [M,N]
+    group_sizes: torch.Tensor       # int32 [G]
+    num_active: int
+    group_offset: int = 0
+    out_dtype: torch.dtype = torch.float32
+    meta: Dict = dataclasses.field(default_factory=dict)
+
+    @property
+    def M(self):
+        return self.lhs.shape[0]
+
+    @property
+    def K(self):
+        return self.lhs.shape[1]
+
+    @property
+    def N(self):
+        return self.rhs.shape[1]
+
+    def sizes_list(self):
+        return [int(x) for x in self.group_sizes.cpu().tolist()]
+
+    def active_rows(self):
+        s = self.sizes_list()
+        return sum(s[self.group_offset:self.group_offset + self.num_active])
+
+    def flops(self):
+        """2 * (active rows) * K * N."""
+        return 2 * self.active_rows() * self.K * self.N
+
+    def algorithmic_bytes(self):
+        """Active rows of both operands, every output element (empty groups
+        are written as zeros) and the group sizes."""
+        r = self.active_rows()
+        b = r * self.K * self.lhs.element_size() + r * self.N * self.rhs.element_size()
+        b += self.num_active * self.K * self.N * torch.tensor([], dtype=self.out_dtype).element_size()
+        return b + self.group_sizes.numel() * 4
+
+
+def tgmm_bf16(seed: int = 1006, device="cpu", tokens: int = 32768, experts: int = 128,
+              top_k: int = 8, K: int = 1408, N: int = 1408, sizes_seed: int = 1002) -> TgmmCase:
+    """Weight gradient of the MoE up-projection (the drhs of the forward
+    workload): lhs = the forward's activations, bf16 [tokens*top_k, K]
+    N(0, 0.02); rhs = the output gradient, bf16 [tokens*top_k, N] N(0, 1e-3)
+    (the dlhs workload's dout); the forward's router group sizes; f32 out
+    [experts, K, N]."""
+    sizes = router_group_sizes(sizes_seed, tokens, experts, top_k)
+    M = tokens * top_k
+    lhs = normal((M, K), 0.02, seed + 1, device, torch.bfloat16)
+    rhs = normal((M, N), 1e-3, seed + 2, device, torch.bfloat16)
+    return TgmmCase("tgmm_bf16", lhs, rhs, torch.from_numpy(sizes).to(device), num_active=experts,
+                    meta=dict(tokens=tokens, experts=experts, top_k=top_k))
+
+
+TGMM_FULL = {
+    "tgmm_bf16": lambda device="cpu": tgmm_bf16(device=device),
+}
+
+
 FULL = {
     "tiny_fp32": lambda device="cpu": tiny_fp32(device=device),
     "moe_fwd_bf16": lambda device="cpu": moe_forward_bf16(device=device),
