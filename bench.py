@@ -32,7 +32,7 @@ PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # dense MFMA TFLOP/s (MI3
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "moe_grouped_matrix_amd", "csrc", f)
-                  for f in ("gmm_device.hpp", "gmm_big.hpp", "gmm_stream.hpp", "gmm_params.hpp",
+                  for f in ("gmm_device.hpp", "gmm_big.hpp", "gmm_stream.hpp", "gmm_tgmm.hpp", "gmm_params.hpp",
                             "gmm_kernels.hip")]
 # workloads whose weights fit in the caches between calls: each timed call
 # starts from evicted L2 / Infinity Cache (a 512 MB write outside the events)
@@ -62,8 +62,14 @@ def measured_traffic(workload: str):
 
 def build_cases(workload: str, device):
     import workloads
+    if workload in workloads.TGMM_FULL:
+        return [workloads.TGMM_FULL[workload](device=device)]
     names = {"fwd+dlhs": ["moe_fwd_bf16", "moe_dlhs_bf16"]}.get(workload, [workload])
     return [workloads.FULL[n](device=device) for n in names]
+
+
+def is_tgmm(case) -> bool:
+    return not hasattr(case, "transpose_rhs")
 
 
 def op_peak(case):
@@ -87,6 +93,8 @@ def cpu_baseline(cases, target_s: float = 20.0):
 
     oracle.build(force=False)
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    if any(is_tgmm(c) for c in cases):
+        return cpu_baseline_tgmm(cases, target_s)
     flops_total = 0.0
     secs_total = 0.0
     descr = []
@@ -129,6 +137,37 @@ def cpu_baseline(cases, target_s: float = 20.0):
     return {"value": flops_total / secs_total / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": "; ".join(descr) + f" (fp64 oracle, {secs_total:.1f} s)"}
+
+
+def cpu_baseline_tgmm(cases, target_s: float = 20.0):
+    """Time the oracle's tgmm on a bounded sample: whole output rows (h, k)
+    of a spread of groups, each costing rows_h * N multiply-adds exactly as
+    in the full problem."""
+    import numpy as np
+
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    case = cases[0]
+    sizes = case.sizes_list()
+    lhs, rhs, gs = case.lhs.cpu(), case.rhs.cpu(), case.group_sizes.cpu()
+    groups = [h for h in range(case.num_active) if sizes[case.group_offset + h] > 0]
+    groups = groups[::max(1, len(groups) // 16)]
+    per = 2
+    for phase in ("calibrate", "calibrate", "measure"):
+        sel = [(h, (7 * j + h) % case.K) for h in groups for j in range(per)]
+        t0 = time.perf_counter()
+        oracle.tgmm_reference(lhs, rhs, gs, group_offset=case.group_offset, num_active=case.num_active,
+                              select=sel)
+        secs = time.perf_counter() - t0
+        flops = sum(2.0 * sizes[case.group_offset + h] * case.N for h, _ in sel)
+        if phase == "calibrate":
+            per = max(1, int(per * target_s / max(secs, 1e-3)))
+            if secs > 0.5 * target_s:
+                break
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{case.name}: {len(sel)} output rows (h, k) of {len(groups)} groups "
+                      f"(fp64 oracle, {secs:.1f} s)"}
 
 
 class ClockSampler:
@@ -204,7 +243,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fwd+dlhs",
                     help="fwd+dlhs (default) or one of tiny_fp32, moe_fwd_bf16, moe_dlhs_bf16, "
-                         "decode_fp8w, w8a8_fp8")
+                         "decode_fp8w, w8a8_fp8, tgmm_bf16 (the weight gradient)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -224,13 +263,17 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     cases = build_cases(args.workload, dev)
-    outs = [torch.empty((c.M, c.N), dtype=c.out_dtype, device=dev) for c in cases]
+    outs = [torch.empty((c.num_active, c.K, c.N) if is_tgmm(c) else (c.M, c.N), dtype=c.out_dtype, device=dev)
+            for c in cases]
     offs = [torch.tensor([c.group_offset], dtype=torch.int32, device=dev) if c.group_offset else None
             for c in cases]
     stream = torch.cuda.current_stream(dev)
 
     def launch(i):
         c = cases[i]
+        if is_tgmm(c):
+            gmm_amd.tgmm(c.lhs, c.rhs, c.group_sizes, num_active=c.num_active, group_offset=offs[i], out=outs[i])
+            return
         gmm_amd.gmm(c.lhs, c.rhs, c.group_sizes, rhs_scale=c.rhs_scale, rhs_bias=c.rhs_bias,
                     lhs_scale=c.lhs_scale, group_offset=offs[i], transpose_rhs=c.transpose_rhs,
                     out=outs[i])
@@ -333,7 +376,8 @@ def main():
         "data": "synthetic (seeded; router group sizes, normal values)",
         "config": {"workload": " + ".join(c.name for c in cases),
                    "shapes": [{"M": c.M, "K": c.K, "N": c.N, "G": int(c.group_sizes.numel()),
-                               "Ga": c.num_active, "transpose_rhs": c.transpose_rhs} for c in cases],
+                               "Ga": c.num_active, "transpose_rhs": getattr(c, "transpose_rhs", None),
+                               "op": "tgmm" if is_tgmm(c) else "gmm"} for c in cases],
                    "frac_of_peak": value / PEAK[op_peak(cases[0])[0]]},
         "roofline": roof,
         "detail": detail,

@@ -14,10 +14,15 @@
 #include "gmm.h"
 #include "gmm_launch.hpp"
 
+constexpr size_t kDeviceBlock = 128;
+static_assert(16 + 2 * gmmk::kQueues * sizeof(int32_t) <= kDeviceBlock, "device block");
+
 struct gmm_handle {
   int device = 0;
   int cu_count = 0;
-  uint32_t* flags = nullptr;  // device word
+  // device block: the data-error flag word at byte 0, the transposed
+  // product's work-queue counters (2 * kQueues int32) from byte 16
+  uint32_t* flags = nullptr;
   int tile_policy = 0;        // 0 auto, 1 small tiles, 2 big tiles
   std::string err;
 };
@@ -93,11 +98,11 @@ gmm_status gmm_create(gmm_handle** out, int device) {
   h->device = device;
   h->cu_count = prop.multiProcessorCount;
   DeviceGuard g(device);
-  if (hipMalloc(&h->flags, sizeof(uint32_t)) != hipSuccess) {
+  if (hipMalloc(&h->flags, kDeviceBlock) != hipSuccess) {
     delete h;
     return GMM_E_HIP;
   }
-  if (hipMemset(h->flags, 0, sizeof(uint32_t)) != hipSuccess) {
+  if (hipMemset(h->flags, 0, kDeviceBlock) != hipSuccess) {
     (void)hipFree(h->flags);
     delete h;
     return GMM_E_HIP;
@@ -306,6 +311,7 @@ gmm_status gmm_tgmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* 
   p.group_offset = group_offset;
   p.out = const_cast<void*>(out->data);
   p.flags = h->flags;
+  p.queue = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(h->flags) + 16);
   p.M = (int32_t)M;
   p.K = (int32_t)K;
   p.N = (int32_t)N;

@@ -10,6 +10,7 @@ namespace gmmk {
 enum class Op { F32, BF16, FP8 };
 
 constexpr int kMaxGroups = 1024;
+constexpr int kQueues = 8;  // one per XCD
 constexpr uint32_t kFlagNegative = 0x1u;
 constexpr uint32_t kFlagExceed = 0x2u;
 constexpr uint32_t kFlagBadOffset = 0x4u;
@@ -28,6 +29,9 @@ struct Params {
   const float* lhs_scale;       // [M, nb] or nullptr
   void* out;                    // [M, N]
   uint32_t* flags;
+  // work queues of the transposed product: kQueues tile counters followed by
+  // kQueues finished-workgroup counters, all zero between calls
+  int32_t* queue;
   int32_t M, K, N, G, Ga, nb, blk;
   int32_t bias_f32, out_f32;
 };

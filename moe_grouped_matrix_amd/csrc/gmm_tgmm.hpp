@@ -19,10 +19,14 @@
 // contraction tail) read as zeros; a tile runs at least five steps (the
 // phased loop's minimum), the extra ones reading zeros.
 //
-// Tiles go to workgroups in order of the group's row count, largest first,
-// in rounds of one tile per workgroup that alternate direction, so the
-// long contractions are spread over the workgroups and the short ones fill
-// in behind them; consecutive tiles of a group share an XCD's L2.
+// Tiles are handed out dynamically, per XCD: the active groups, largest
+// first, are dealt to eight queues (one per XCD) so that each queue gets the
+// same number of contraction steps (each to the least-loaded queue), and the
+// workgroups of an XCD take their queue's tiles in order with an atomic
+// counter, so a group's tiles share that XCD's L2 and the long contractions
+// are spread first, the short ones filling in behind.  The counters live in
+// the handle's device memory; the last workgroup of a queue to finish
+// resets its counters for the next call.
 #pragma once
 
 #include "gmm_big.hpp"
@@ -57,16 +61,55 @@ struct TgItem {
   BigItem out;     // output tile as rows h * K + k0 .. of the [Ga*K, N] output
 };
 
-// Tile L of the group order: group order[L / per], then k-tile, then n-tile.
+// Scheduling units: a group's tiles, or, for a group whose tiles are long,
+// one of the four quadrants of its tile grid (k-tiles [0, ka) or [ka, nkt),
+// n-tiles [0, na) or [na, nnt)), so that its tiles can spread over several
+// queues.  A unit is an int: the active group in bits 0..9, the quadrant in
+// bits 10 (upper k half) and 11 (upper n half), bit 12 set for a quadrant.
+constexpr int kMaxSplit = 128;                          // groups split at most
+constexpr int kMaxUnits = kMaxGroups + 3 * kMaxSplit;  // units at most
+
+struct TgGrid {
+  int nkt, nnt, ka, na;
+};
+
+// The unit of queue tile L: the last of the queue's units [*cur, u_end) whose
+// first tile (ustart, increasing along a queue) is at most L, 64 at a time
+// with a ballot.  A workgroup's tile indices only grow, so the search starts
+// from its previous unit (*cur).
+__device__ __forceinline__ int tg_find_unit(const int* ustart, int* cur, int u_end, int L, int lane) {
+  int u = *cur;
+  while (true) {
+    const int k = u + 1 + lane;
+    const bool le = k < u_end && ustart[k] <= L;
+    const int c = __popcll(__ballot(le));
+    u += c;
+    if (c < 64) break;
+  }
+  *cur = u;
+  return u;
+}
+
+// Tile L of a queue: its unit, then k-tile, then n-tile within the unit.
 template <class C>
-__device__ __forceinline__ TgItem decode_tg(const Plan& pl, const int* order, int L, int nkt, int nnt, int K,
-                                            int N, int w) {
+__device__ __forceinline__ TgItem decode_tg(const Plan& pl, const int* units, const int* ustart, int* cur,
+                                            int u_end, int L, const TgGrid& gr, int K, int N, int w, int lane) {
   TgItem it;
-  const int per = nkt * nnt;
-  const int gi = L / per, t = L % per;
-  const int h = order[gi];
-  const int kt = t / nnt, nt = t % nnt;
-  it.h = __builtin_amdgcn_readfirstlane(h);
+  const int u = tg_find_unit(ustart, cur, u_end, L, lane);
+  const int d = __builtin_amdgcn_readfirstlane(units[u]);
+  const int t = L - __builtin_amdgcn_readfirstlane(ustart[u]);
+  const int h = d & 1023;
+  int kt, nt;
+  if (d & 4096) {
+    const int k0 = (d & 1024) ? gr.ka : 0, n0 = (d & 2048) ? gr.na : 0;
+    const int bw = (d & 2048) ? gr.nnt - gr.na : gr.na;
+    kt = k0 + t / bw;
+    nt = n0 + t % bw;
+  } else {
+    kt = t / gr.nnt;
+    nt = t % gr.nnt;
+  }
+  it.h = h;
   it.rlo = __builtin_amdgcn_readfirstlane(pl.row_start[h]);
   it.nrow = __builtin_amdgcn_readfirstlane(pl.row_start[h + 1] - pl.row_start[h]);
   const int st = (it.nrow + C::BK - 1) / C::BK;
@@ -184,12 +227,154 @@ __device__ void tg_order(const Plan& pl, int* order) {
   }
 }
 
+// LDS areas.  While the tiles are scheduled, before the first load, the
+// ring holds the group order and the deal's per-unit records; past the ring
+// lie the queues' unit lists (each queue's units in order, queue after
+// queue), the first tile of each unit within its queue, scheduling words, and
+// the plan.
+template <class C>
+struct TgLds {
+  static constexpr int ORDER = 0;                        // int[kMaxGroups], in the ring
+  static constexpr int REC_UNIT = ORDER + kMaxGroups * 4;  // int[kMaxUnits], in the ring
+  static constexpr int REC_POS = REC_UNIT + kMaxUnits * 4;  // int[kMaxUnits], in the ring
+  static constexpr int REC_START = REC_POS + kMaxUnits * 4;  // int[kMaxUnits], in the ring
+  static_assert(REC_START + kMaxUnits * 4 <= C::RING, "deal records fit the ring");
+  static constexpr int UNITS = C::RING;                  // int[kMaxUnits]
+  static constexpr int USTART = UNITS + kMaxUnits * 4;   // int[kMaxUnits]
+  static constexpr int SCHED = USTART + kMaxUnits * 4;   // int[32], see the kernel
+  static constexpr int PLAN = SCHED + 128;
+  static constexpr int BYTES = PLAN + sizeof(Plan);
+  static_assert(PLAN % 16 == 0, "plan alignment");
+};
+// scheduling words: the first unit of each queue [0, kQueues], the tiles of
+// each queue, and the hand-over slot of a grabbed tile index
+constexpr int kSchedOff = 0, kSchedTiles = 12, kSchedSlot = 24;
+
+// Deal the units to nq queues, each to the queue with the least work so far
+// (the lowest index on ties), in the group order (largest first), so each
+// queue's units are in that order too.  A tile's work is its contraction
+// steps plus two for the epilogue.  A group is split into quadrants when its
+// tiles take more than a quarter of a workgroup's share of all the work (at
+// most kMaxSplit groups, the largest).  Wave 0 runs it: the greedy choice is
+// made in scalar registers, unit after unit, recording each unit's queue,
+// place in the queue and first tile; the lists are then written in parallel.
+template <class C>
+__device__ inline void tg_deal(const Plan& pl, const int* order, char* smem, int* units, int* ustart, int* sched,
+                               int nq, int P, const TgGrid& gr, int lane) {
+  using Lds = TgLds<C>;
+  int* const rec_unit = reinterpret_cast<int*>(smem + Lds::REC_UNIT);
+  int* const rec_pos = reinterpret_cast<int*>(smem + Lds::REC_POS);
+  int* const rec_start = reinterpret_cast<int*>(smem + Lds::REC_START);
+  const int ga = pl.ga;
+  const int per = gr.nnt * gr.nkt;
+  auto tile_cost = [&](int i) {
+    const int h = order[i];
+    const int st = (pl.row_start[h + 1] - pl.row_start[h] + C::BK - 1) / C::BK;
+    return (st < C::MIN_STEPS ? C::MIN_STEPS : st) + 2;
+  };
+  // all the work, and the scale that keeps the queue loads in 31 bits
+  long long total = 0;
+  for (int c = 0; c < ga; c += 64) {
+    const int cost = c + lane < ga ? tile_cost(c + lane) : 0;
+    const int n = ga - c < 64 ? ga - c : 64;
+    for (int jj = 0; jj < n; ++jj) total += __builtin_amdgcn_readlane(cost, jj);
+  }
+  total *= per;
+  int shift = 0;
+  while ((total >> shift) >= (1ll << 30)) ++shift;
+  int load[kQueues], cnt[kQueues], tiles[kQueues];
+#pragma unroll
+  for (int q = 0; q < kQueues; ++q) {
+    load[q] = q < nq ? 0 : 0x7fffffff;
+    cnt[q] = 0;
+    tiles[q] = 0;
+  }
+  int k = 0, nsplit = 0;
+  for (int c = 0; c < ga; c += 64) {
+    const int cost = c + lane < ga ? tile_cost(c + lane) : 0;
+    const int h = c + lane < ga ? order[c + lane] : 0;
+    const int n = ga - c < 64 ? ga - c : 64;
+    for (int jj = 0; jj < n; ++jj) {
+      const int cj = __builtin_amdgcn_readlane(cost, jj);
+      const int hj = __builtin_amdgcn_readlane(h, jj);
+      // a tile longer than a quarter of a workgroup's share: cost > total / (4 P)
+      const bool split = per > 1 && nsplit < kMaxSplit && 4ll * P * cj > total;
+      nsplit += split;
+      for (int qd = 0; qd < (split ? 4 : 1); ++qd) {
+        const int nk = !split ? gr.nkt : (qd & 1) ? gr.nkt - gr.ka : gr.ka;
+        const int nn = !split ? gr.nnt : (qd & 2) ? gr.nnt - gr.na : gr.na;
+        const int nt = nk * nn;
+        if (nt == 0) continue;
+        int q = 0, best = load[0];
+#pragma unroll
+        for (int t = 1; t < kQueues; ++t)
+          if (load[t] < best) {
+            best = load[t];
+            q = t;
+          }
+        const int add = (int)(((long long)cj * nt) >> shift) + 1;
+        int pos = 0, first = 0;
+#pragma unroll
+        for (int t = 0; t < kQueues; ++t) {
+          pos = t == q ? cnt[t] : pos;
+          first = t == q ? tiles[t] : first;
+          load[t] += t == q ? add : 0;
+          cnt[t] += t == q ? 1 : 0;
+          tiles[t] += t == q ? nt : 0;
+        }
+        if (lane == 0) {
+          rec_unit[k] = hj | (split ? 4096 | qd << 10 : 0);
+          rec_pos[k] = q | pos << 4;
+          rec_start[k] = first;
+        }
+        ++k;
+      }
+    }
+  }
+  int base[kQueues];
+  int acc = 0;
+#pragma unroll
+  for (int q = 0; q < kQueues; ++q) {
+    base[q] = acc;
+    if (lane == 0) {
+      sched[kSchedOff + q] = acc;
+      sched[kSchedTiles + q] = tiles[q];
+    }
+    acc += cnt[q];
+  }
+  if (lane == 0) sched[kSchedOff + kQueues] = acc;
+  for (int i = lane; i < k; i += 64) {
+    const int qp = rec_pos[i];
+    const int q = qp & 15;
+    int b = 0;
+#pragma unroll
+    for (int t = 0; t < kQueues; ++t) b = t == q ? base[t] : b;
+    units[b + (qp >> 4)] = rec_unit[i];
+    ustart[b + (qp >> 4)] = rec_start[i];
+  }
+}
+
+// atomicAdd(counter, 1) as one instruction of a whole wave that takes part
+// (`live`): a buffer atomic over the counter's four bytes, so only lane 0 is
+// in range (the other lanes' adds are dropped) and returns the old value.  A
+// wave that does not take part issues the same instruction over zero bytes:
+// every lane is dropped, but the wave still counts one memory operation, so
+// the waits after it are the same in every wave, with no branch around it.
+__device__ __forceinline__ int tg_grab_wave(int* counter, int lane, bool live) {
+  const __amdgpu_buffer_rsrc_t r = uniform_rsrc(reinterpret_cast<const char*>(counter), live ? 4 : 0);
+  return __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, r, lane * 4, 0, 0);
+}
+
 template <class C>
 __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
-  // one LDS array: the ring, the group order and the plan
-  __shared__ __attribute__((aligned(1024))) char smem[C::RING + kMaxGroups * 4 + sizeof(Plan)];
-  int* const order = reinterpret_cast<int*>(smem + C::RING);
-  Plan& pl = *reinterpret_cast<Plan*>(smem + C::RING + kMaxGroups * 4);
+  using Lds = TgLds<C>;
+  // one LDS array: the ring, the scheduling tables and the plan
+  __shared__ __attribute__((aligned(1024))) char smem[Lds::BYTES];
+  int* const order = reinterpret_cast<int*>(smem + Lds::ORDER);
+  int* const units = reinterpret_cast<int*>(smem + Lds::UNITS);
+  int* const ustart = reinterpret_cast<int*>(smem + Lds::USTART);
+  int* const sched = reinterpret_cast<int*>(smem + Lds::SCHED);
+  Plan& pl = *reinterpret_cast<Plan*>(smem + Lds::PLAN);
   if (threadIdx.x == 0) pl.flags = 0;
   __syncthreads();
   build_plan<C::T>(p, pl, C::BM);
@@ -203,8 +388,23 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
   const int K = p.K, N = p.N;
   const int P = gridDim.x;
   const int slot = xcd_slot(blockIdx.x, P);
-  const int nkt = (K + C::BM - 1) / C::BM, nnt = (N + C::BN - 1) / C::BN;
-  const int n_items = __builtin_amdgcn_readfirstlane(pl.ga) * nkt * nnt;
+  TgGrid gr;
+  gr.nkt = (K + C::BM - 1) / C::BM;
+  gr.nnt = (N + C::BN - 1) / C::BN;
+  gr.ka = (gr.nkt + 1) / 2;
+  gr.na = (gr.nnt + 1) / 2;
+  // queues: one per XCD (workgroup b runs on XCD b % 8) when the grid
+  // divides evenly and there are groups enough to deal, else one
+  const int nq = P % kQueues == 0 && pl.ga >= 2 * kQueues ? kQueues : 1;
+  const int x = blockIdx.x % nq;
+  if (w == 0) tg_deal<C>(pl, order, smem, units, ustart, sched, nq, P, gr, lane);
+  __syncthreads();
+  // this queue's units [ucur, u_end) and tiles [0, n_items)
+  int ucur = __builtin_amdgcn_readfirstlane(sched[kSchedOff + x]);
+  const int u_end = __builtin_amdgcn_readfirstlane(sched[kSchedOff + x + 1]);
+  const int n_items = __builtin_amdgcn_readfirstlane(sched[kSchedTiles + x]);
+  int* const counter = p.queue + x;
+  const int W = P / nq, j = blockIdx.x / nq;  // workgroups of the queue, this one's place
   // Output groups the plan dropped (a group offset past G - Ga, which is
   // flagged) are zero.  K * N is a multiple of 64, so 16-byte stores tile it.
   {
@@ -213,15 +413,34 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
     for (long long off = b0 + ((long long)slot * C::T + tid) * 16; off < b1; off += (long long)P * C::T * 16)
       *reinterpret_cast<i32x4*>(o + off) = i32x4{0, 0, 0, 0};
   }
-  // this workgroup's tile of round r (rounds alternate direction)
-  auto item_of = [&](int r) { return r * P + ((r & 1) ? P - 1 - slot : slot); };
-  int r = 0;
-  if (item_of(0) >= n_items) return;
+  // The last workgroup of the queue to get here resets its counters; every
+  // index this workgroup grabbed has returned by then (each was used).
+  auto finish = [&]() {
+    if (tid == 0) {
+      const int prev = atomicAdd(p.queue + kQueues + x, 1);
+      if (prev == W - 1) {
+        atomicExch(counter, 0);
+        atomicExch(p.queue + kQueues + x, 0);
+      }
+    }
+  };
 
-  TgItem cur = decode_tg<C>(pl, order, item_of(0), nkt, nnt, K, N, w);
-  bool last_item = item_of(1) >= n_items;
+  // Tile indices: the queue's first two rounds are fixed, workgroup j of the
+  // queue's W taking tiles j and 2W-1-j (had each grabbed its first two, the
+  // first workgroups would take two of the longest tiles each); afterwards
+  // each tile grabs the index of the tile after next during its first steps
+  // (so the next tile is known before its loads start), from 2W on.
+  int L_cur = j;
+  int L_nxt = 2 * W - 1 - j;
+  if (L_cur >= n_items) {
+    finish();
+    return;
+  }
+
+  TgItem cur = decode_tg<C>(pl, units, ustart, &ucur, u_end, L_cur, gr, K, N, w, lane);
+  bool last_item = L_nxt >= n_items;
   TgItem nxt = cur;
-  if (!last_item) nxt = decode_tg<C>(pl, order, item_of(1), nkt, nnt, K, N, w);
+  if (!last_item) nxt = decode_tg<C>(pl, units, ustart, &ucur, u_end, L_nxt, gr, K, N, w, lane);
   TgDma dcur = tg_dma<C>(p, cur, true);
   TgDma dnxt = tg_dma<C>(p, nxt, !last_item);
   const TgOff off = tg_offsets(K, N, w, lane);
@@ -283,11 +502,13 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
 
   f32x16 acc[C::FM][C::FN];
   int stage = 0;
+  int L_new = 0;  // the grabbed index handed over during the current tile
 
   // One contraction step s (as the big kernel's K step, without a bias
   // row): step s+1's operands are complete once at most WAIT newer
   // operations are outstanding -- step s+2's four loads and, in a tile's
-  // first two steps, the previous tile's E stores.  The barrier frees the
+  // first two steps, the previous tile's E stores (and in the second, the
+  // tile-index grab issued after the first).  The barrier frees the
   // stage step s-1 used, which takes step s+3 (this tile's step kd, or the
   // next tile's when NEXT); fragments are refilled with step s+1's right
   // after their last use.
@@ -335,7 +556,10 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  using W0 = std::integral_constant<int, C::DMA_STEP + C::E>;  // first two steps of a tile
+  // a tile's first two steps: the previous tile's E stores are also
+  // outstanding, and in the second step the grab too
+  using W0 = std::integral_constant<int, C::DMA_STEP + C::E>;
+  using W0G = std::integral_constant<int, C::DMA_STEP + C::E + 1>;
   using W1 = std::integral_constant<int, C::DMA_STEP>;
   // One tile of cur.steps >= 5 steps.
   auto ktile = [&](auto full_tag) __attribute__((always_inline)) {
@@ -343,15 +567,23 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
     constexpr int FMA = FULL ? C::FM : C::FM / 2;
     const int KT = cur.steps;
     kstep(full_tag, W0{}, F_{}, F_{}, 3);
-    kstep(full_tag, W0{}, F_{}, F_{}, 4);
+    // the grab of the tile after next, by wave 0 unless this tile has no
+    // successor: exactly one counted operation in every wave
+    const int g = tg_grab_wave(counter, lane, w == 0 && !last_item);
+    kstep(full_tag, W0G{}, F_{}, F_{}, 4);
     for (int kt = 2; kt + 3 < KT; ++kt) kstep(full_tag, W1{}, F_{}, F_{}, kt + 3);
     kstep(full_tag, W1{}, T_{}, F_{}, 0);  // kt = KT-3: the next tile's step 0
+    // the grab has returned (this step's wait left only the loads of the
+    // step before outstanding); hand it to every wave, which reads it after
+    // the last step's barrier
+    if (w == 0 && lane == 0 && !last_item) sched[kSchedSlot] = g;
     kstep(full_tag, W1{}, T_{}, F_{}, 1);
     kstep(full_tag, W1{}, T_{}, T_{}, 2);
     // every refill has landed before the epilogue takes registers of its own
     __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
     hold(0);
     hold(1);
+    L_new = 2 * W + __builtin_amdgcn_readfirstlane(sched[kSchedSlot]);
     // the last step's stage holds the epilogue's staging slices, 4 KB per wave
     big_epilogue<C, FMA>(p, acc, cur.out, smem, smem + ((stage + 3) & (C::S - 1)) * C::STAGE + w * 4096, kh, r32,
                          lane);
@@ -359,23 +591,24 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
 
   while (true) {
 #pragma unroll
-    for (int x = 0; x < C::FM; ++x)
+    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-      for (int y = 0; y < C::FN; ++y)
+      for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-        for (int z = 0; z < 16; ++z) acc[x][y][z] = 0.f;
+        for (int z = 0; z < 16; ++z) acc[i][j][z] = 0.f;
     if (!cur.out.half)
       ktile(std::true_type{});
     else
       ktile(std::false_type{});
     if (last_item) break;
-    ++r;
-    last_item = item_of(r + 1) >= n_items;
+    L_nxt = L_new;
+    last_item = L_nxt >= n_items;
     cur = nxt;
     dcur = dnxt;
-    if (!last_item) nxt = decode_tg<C>(pl, order, item_of(r + 1), nkt, nnt, K, N, w);
+    if (!last_item) nxt = decode_tg<C>(pl, units, ustart, &ucur, u_end, L_nxt, gr, K, N, w, lane);
     dnxt = tg_dma<C>(p, nxt, !last_item);
   }
+  finish();
 }
 
 }  // namespace gmmk

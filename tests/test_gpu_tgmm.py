@@ -5,7 +5,9 @@ Small cases compare every element: contraction tails (group sizes that are
 not multiples of the 32-row step), groups shorter than the kernel's five
 steps, empty groups (all-zero bits), K and N tails past the 256-column tiles
 (down to 8 columns), a group offset, f32 and bf16 outputs, rows outside the
-active groups (ignored), and invalid device sizes (clamped and flagged).  The
+active groups (ignored), invalid device sizes (clamped and flagged), and
+both tile schedules (one work queue, and one per XCD over two calls in a
+row).  The
 full-size case (the forward workload's shapes) runs in the benchmark's
 launch configuration and compares sampled output rows.
 
@@ -65,6 +67,27 @@ def test_tgmm_against_oracle(sizes, extra, K, N, out_dtype, s, ga):
     assert m.device_flags() == 0
     ref = oracle.tgmm_reference(lhs, rhs, gs, group_offset=s, num_active=Ga)
     _check(out.cpu(), ref, sizes, s, out_dtype, f"tgmm {sizes} K={K} N={N}")
+
+
+def test_tgmm_work_queues_back_to_back():
+    """Enough groups for one work queue per XCD (20 and 17 groups over 40 and
+    34 tiles, so 40 and 32 workgroups): two calls in a row on the same handle,
+    the second smaller, check that the tiles are all handed out and that the
+    last workgroup of every queue leaves its counters at zero for the next
+    call."""
+    import moe_grouped_matrix_amd as m
+    rng = np.random.default_rng(7)
+    for n_groups, K, N in ((20, 256, 264), (17, 200, 264)):
+        sizes = [int(v) for v in rng.integers(0, 300, n_groups)]
+        sizes[3] = 0
+        sizes[11] = 0
+        lhs, rhs, gs = _case(sizes, 5, K, N, seed=n_groups)
+        print(f"tgmm queues case groups={n_groups} K={K} N={N}", flush=True)
+        out = m.tgmm(lhs.cuda(), rhs.cuda(), gs.cuda(), out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert m.device_flags() == 0
+        ref = oracle.tgmm_reference(lhs, rhs, gs)
+        _check(out.cpu(), ref, sizes, 0, torch.float32, f"tgmm queues {n_groups} groups")
 
 
 def test_tgmm_invalid_sizes_are_clamped_and_flagged():
