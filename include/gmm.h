@@ -131,6 +131,38 @@ gmm_status gmm_run(gmm_handle* h,
                    void* stream);
 
 /*
+ * gmm_run_existing_out: gmm_run, except that the rows outside the active
+ * groups (rows before the first active group's, and from the end of the last
+ * active group's on) are those of existing_out instead of zeros.  This is
+ * the existing_out argument of gmm() on the tpu-inference wheel diff pages
+ * (megablox/gmm.py): the kernel starts each output tile from existing_out
+ * and stores only its group's rows over it, and no zero fill follows.  With
+ * expert shards it merges one shard's rows into an output the other shards
+ * have written.
+ *
+ *   existing_out [M,N], the dtype of out (as the pages require of the
+ *                preferred element type).  Either out itself (the active
+ *                rows are written in place, the others are not touched) or
+ *                a buffer that does not overlap out (the other rows are
+ *                copied from it).  Read-only; it may overlap an input.
+ *   Every other argument, limit and error is as for gmm_run; existing_out
+ *   NULL returns GMM_E_INVALID (gmm_run is that call), as does an
+ *   existing_out of another shape or dtype, or one that partly overlaps out.
+ */
+gmm_status gmm_run_existing_out(gmm_handle* h,
+                                const gmm_tensor* lhs,
+                                const gmm_tensor* rhs,
+                                const gmm_tensor* group_sizes,
+                                const gmm_tensor* rhs_scale,
+                                const gmm_tensor* rhs_bias,
+                                const gmm_tensor* lhs_scale,
+                                const int32_t* group_offset,
+                                int transpose_rhs,
+                                const gmm_tensor* existing_out,
+                                const gmm_tensor* out,
+                                void* stream);
+
+/*
  * gmm_tgmm_run: queue the transposed grouped matmul, the weight gradient of
  * gmm, on `stream`.  For each active group h = g - s (g = s .. s+Ga-1),
  *

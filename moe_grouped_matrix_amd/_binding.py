@@ -20,8 +20,8 @@ GMM_F32, GMM_BF16, GMM_F8E4M3FN, GMM_I32 = 0, 1, 2, 3
 GMM_OK, GMM_E_INVALID, GMM_E_UNSUPPORTED, GMM_E_HIP, GMM_E_DEVICE_DATA = 0, -1, -2, -3, -4
 FLAG_NEGATIVE_SIZE, FLAG_SIZES_EXCEED_M, FLAG_BAD_OFFSET = 0x1, 0x2, 0x4
 
-EXPORTED = ("gmm_create", "gmm_destroy", "gmm_last_error", "gmm_run", "gmm_tgmm_run", "gmm_device_flags",
-            "gmm_set_tile_policy", "gmm_debug_worklist")
+EXPORTED = ("gmm_create", "gmm_destroy", "gmm_last_error", "gmm_run", "gmm_run_existing_out", "gmm_tgmm_run",
+            "gmm_device_flags", "gmm_set_tile_policy", "gmm_debug_worklist")
 
 _DTYPE = {torch.float32: GMM_F32, torch.bfloat16: GMM_BF16,
           torch.float8_e4m3fn: GMM_F8E4M3FN, torch.int32: GMM_I32}
@@ -73,6 +73,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.gmm_last_error.restype = ctypes.c_char_p
             lib.gmm_run.argtypes = [vp, tp, tp, tp, tp, tp, tp, vp, ctypes.c_int, tp, vp]
             lib.gmm_run.restype = ctypes.c_int
+            lib.gmm_run_existing_out.argtypes = [vp, tp, tp, tp, tp, tp, tp, vp, ctypes.c_int, tp, tp, vp]
+            lib.gmm_run_existing_out.restype = ctypes.c_int
             lib.gmm_tgmm_run.argtypes = [vp, tp, tp, tp, vp, tp, vp]
             lib.gmm_tgmm_run.restype = ctypes.c_int
             lib.gmm_device_flags.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
@@ -159,6 +161,7 @@ def gmm(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,
         lhs_scale: Optional[torch.Tensor] = None,
         group_offset=None,
         transpose_rhs: bool = False,
+        existing_out: Optional[torch.Tensor] = None,
         out: Optional[torch.Tensor] = None,
         stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
     """Grouped matmul on the GPU through libgmm.so.
@@ -167,21 +170,29 @@ def gmm(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,
     group_sizes int32 [G] on the device; rhs_scale f32 [Ga,nb,1,N];
     rhs_bias [Ga,1,N]; lhs_scale f32 [M,nb]; group_offset an int or a
     one-element int32 device tensor.  Returns out [M,N] of out_dtype (the
-    float32 default follows the Megablox gmm)."""
+    float32 default follows the Megablox gmm).  With existing_out [M,N] the
+    rows outside the active groups are its rows instead of zeros
+    (gmm_run_existing_out); without out the result is written into
+    existing_out itself."""
     lib = load()
     dev = lhs.device
     h = handle(dev)
     M = lhs.shape[0] if lhs.dim() >= 1 else 0
     N = rhs.shape[2] if transpose_rhs else (rhs.shape[1] if rhs.dim() == 3 else 0)
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+        out = existing_out if existing_out is not None else torch.empty((M, N), dtype=out_dtype, device=dev)
     views = [_view(t, n) for t, n in ((lhs, "lhs"), (rhs, "rhs"), (group_sizes, "group_sizes"),
                                       (rhs_scale, "rhs_scale"), (rhs_bias, "rhs_bias"),
                                       (lhs_scale, "lhs_scale"), (out, "out"))]
     off_ptr, keep = _offset_ptr(group_offset, dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev)
-    status = lib.gmm_run(h, *[_ref(v) for v in views[:6]], off_ptr, int(bool(transpose_rhs)),
-                         _ref(views[6]), ctypes.c_void_p(st.cuda_stream))
+    if existing_out is None:
+        status = lib.gmm_run(h, *[_ref(v) for v in views[:6]], off_ptr, int(bool(transpose_rhs)),
+                             _ref(views[6]), ctypes.c_void_p(st.cuda_stream))
+    else:
+        ex = _view(existing_out, "existing_out")
+        status = lib.gmm_run_existing_out(h, *[_ref(v) for v in views[:6]], off_ptr, int(bool(transpose_rhs)),
+                                          _ref(ex), _ref(views[6]), ctypes.c_void_p(st.cuda_stream))
     if keep is not None and status == GMM_OK:
         keep.record_stream(st)
     _raise(status, h)

@@ -132,11 +132,14 @@ gmm_status gmm_set_tile_policy(gmm_handle* h, int policy) {
   return GMM_OK;
 }
 
-gmm_status gmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs,
-                   const gmm_tensor* group_sizes, const gmm_tensor* rhs_scale,
-                   const gmm_tensor* rhs_bias, const gmm_tensor* lhs_scale,
-                   const int32_t* group_offset, int transpose_rhs, const gmm_tensor* out,
-                   void* stream) {
+}  // extern "C"
+
+namespace {
+
+gmm_status run_gmm(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs, const gmm_tensor* group_sizes,
+                   const gmm_tensor* rhs_scale, const gmm_tensor* rhs_bias, const gmm_tensor* lhs_scale,
+                   const int32_t* group_offset, int transpose_rhs, const gmm_tensor* existing_out,
+                   const gmm_tensor* out, void* stream) {
   if (!h) return GMM_E_INVALID;
   h->err.clear();
   if (!lhs || !rhs || !group_sizes || !out) return fail(h, GMM_E_INVALID, "lhs, rhs, group_sizes and out are required");
@@ -229,6 +232,21 @@ gmm_status gmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs,
   if (M > 0 && !out->data) return fail(h, GMM_E_INVALID, "null out pointer");
   if (!aligned16(out->data) || !aligned16(group_offset))
     return fail(h, GMM_E_INVALID, "out and group_offset must be 16-byte aligned");
+  int32_t fill = gmmk::kFillZero;
+  if (existing_out) {
+    if (existing_out->ndim != 2 || existing_out->shape[0] != M || existing_out->shape[1] != N)
+      return fail(h, GMM_E_INVALID, "existing_out must be [M,N] like out, got " + shape_str(existing_out));
+    if (existing_out->dtype != out->dtype)
+      return fail(h, GMM_E_INVALID, "existing_out dtype must match the output dtype");
+    if (M > 0 && !existing_out->data) return fail(h, GMM_E_INVALID, "null existing_out pointer");
+    if (!aligned16(existing_out->data)) return fail(h, GMM_E_INVALID, "existing_out must be 16-byte aligned");
+    if (existing_out->data == out->data)
+      fill = gmmk::kFillKeep;
+    else if (overlaps(existing_out, out))
+      return fail(h, GMM_E_INVALID, "existing_out must be out itself or not overlap it");
+    else
+      fill = gmmk::kFillCopy;
+  }
   if (M == 0) return GMM_OK;
 
   if (h->tile_policy == 1)
@@ -247,6 +265,8 @@ gmm_status gmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs,
   p.rhs_bias = rhs_bias ? rhs_bias->data : nullptr;
   p.lhs_scale = lhs_scale ? static_cast<const float*>(lhs_scale->data) : nullptr;
   p.out = const_cast<void*>(out->data);
+  p.existing = existing_out ? existing_out->data : nullptr;
+  p.fill = fill;
   p.flags = h->flags;
   p.M = (int32_t)M;
   p.K = (int32_t)K;
@@ -262,6 +282,31 @@ gmm_status gmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs,
   hipError_t e = gmmk::launch_gmm(p, kc, h->cu_count, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(h, GMM_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return GMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gmm_status gmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs,
+                   const gmm_tensor* group_sizes, const gmm_tensor* rhs_scale,
+                   const gmm_tensor* rhs_bias, const gmm_tensor* lhs_scale,
+                   const int32_t* group_offset, int transpose_rhs, const gmm_tensor* out,
+                   void* stream) {
+  return run_gmm(h, lhs, rhs, group_sizes, rhs_scale, rhs_bias, lhs_scale, group_offset, transpose_rhs, nullptr,
+                 out, stream);
+}
+
+gmm_status gmm_run_existing_out(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs,
+                                const gmm_tensor* group_sizes, const gmm_tensor* rhs_scale,
+                                const gmm_tensor* rhs_bias, const gmm_tensor* lhs_scale,
+                                const int32_t* group_offset, int transpose_rhs,
+                                const gmm_tensor* existing_out, const gmm_tensor* out, void* stream) {
+  if (!h) return GMM_E_INVALID;
+  h->err.clear();
+  if (!existing_out) return fail(h, GMM_E_INVALID, "existing_out is required (gmm_run writes zeros instead)");
+  return run_gmm(h, lhs, rhs, group_sizes, rhs_scale, rhs_bias, lhs_scale, group_offset, transpose_rhs,
+                 existing_out, out, stream);
 }
 
 gmm_status gmm_tgmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs,

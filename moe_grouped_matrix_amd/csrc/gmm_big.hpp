@@ -469,19 +469,15 @@ __global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
   const int P = gridDim.x;
   const int slot = xcd_slot(blockIdx.x, P);
 
-  // rows outside the active groups: zero them first (grid-stride)
+  // rows outside the active groups: fill them first (grid-stride)
   {
     const long long row_bytes = (long long)N * C::es_out;
     const int lo_row = pl.row_start[0], hi_row = pl.row_start[pl.ga];
-    char* out = reinterpret_cast<char*>(p.out);
-    const i32x4 z = {0, 0, 0, 0};
-    const long long z1 = (long long)lo_row * row_bytes;
-    const long long z2b = (long long)hi_row * row_bytes, z2e = (long long)M * row_bytes;
-    const long long total = z1 + (z2e - z2b);
-    for (long long off = ((long long)slot * C::T + tid) * 16; off < total; off += (long long)P * C::T * 16) {
-      const long long o = off < z1 ? off : z2b + (off - z1);
-      *reinterpret_cast<i32x4*>(out + o) = z;
-    }
+    const long long z1 = fill_rows(p, lo_row) * row_bytes;
+    const long long z2b = (long long)hi_row * row_bytes;
+    const long long total = z1 + fill_rows(p, M - hi_row) * row_bytes;
+    for (long long off = ((long long)slot * C::T + tid) * 16; off < total; off += (long long)P * C::T * 16)
+      fill16(p, off < z1 ? off : z2b + (off - z1));
   }
 
   const int n_ntiles = (N + C::BN - 1) / C::BN;

@@ -10,7 +10,10 @@
 //   2. it then takes work items in turn: an item is an (m-tile, n-tile) pair
 //      computed with MFMA from LDS-staged, double-buffered K tiles, or a
 //      slice of the rows outside the active groups, which it zeroes
-//      (_zero_uninitialized_memory on the same page).
+//      (_zero_uninitialized_memory on the same page) or, given an existing
+//      output, copies from it or leaves alone when it is the output itself
+//      (gmm's existing_out there: each output tile starts from it and only
+//      the group's rows are stored over it).
 // The contraction, the per-block scale fold and the bias follow the kernel
 // body of gmm() on that page (_accum); the per-token lhs scale follows the
 // block-scaled W8A8 GEMM of the metrale gemm_quant.rs page
@@ -408,12 +411,24 @@ __device__ inline void mma_tile(f32x4 (&acc)[C::FM][C::FN], const char* sa, cons
   }
 }
 
+// Bytes [off, off + 16) of a row outside the active groups: zeros, or the
+// same bytes of the existing output.  (With kFillKeep nothing is written;
+// the callers then have no such bytes to fill.)
+__device__ __forceinline__ void fill16(const Params& p, long long off) {
+  i32x4 v = {0, 0, 0, 0};
+  if (p.fill == kFillCopy) v = *reinterpret_cast<const i32x4*>(reinterpret_cast<const char*>(p.existing) + off);
+  *reinterpret_cast<i32x4*>(reinterpret_cast<char*>(p.out) + off) = v;
+}
+
+// Bytes of the rows before the active ones and after them that the fill
+// writes (none when the existing output is the output itself).
+__device__ __forceinline__ long long fill_rows(const Params& p, int rows) {
+  return p.fill == kFillKeep ? 0 : (long long)rows;
+}
+
 template <class C>
-__device__ inline void zero_item(const Params& p, long long begin, long long end) {
-  char* out = reinterpret_cast<char*>(p.out);
-  const i32x4 z = {0, 0, 0, 0};
-  for (long long off = begin + (long long)threadIdx.x * 16; off < end; off += (long long)C::T * 16)
-    *reinterpret_cast<i32x4*>(out + off) = z;
+__device__ inline void fill_item(const Params& p, long long begin, long long end) {
+  for (long long off = begin + (long long)threadIdx.x * 16; off < end; off += (long long)C::T * 16) fill16(p, off);
 }
 
 template <class C>
@@ -434,8 +449,8 @@ __global__ __launch_bounds__(C::T) void gmm_kernel(Params p) {
   const int n_ntiles = (N + C::BN - 1) / C::BN;
   const long long n_gemm = (long long)pl.n_mtiles * n_ntiles;
   const int lo_row = pl.row_start[0], hi_row = pl.row_start[pl.ga];
-  const long long z1_bytes = (long long)lo_row * row_bytes;
-  const long long z2_bytes = (long long)(M - hi_row) * row_bytes;
+  const long long z1_bytes = fill_rows(p, lo_row) * row_bytes;
+  const long long z2_bytes = fill_rows(p, M - hi_row) * row_bytes;
   const long long z1 = (z1_bytes + kZeroChunk - 1) / kZeroChunk;
   const long long z2 = (z2_bytes + kZeroChunk - 1) / kZeroChunk;
   const long long n_items = n_gemm + z1 + z2;
@@ -448,14 +463,14 @@ __global__ __launch_bounds__(C::T) void gmm_kernel(Params p) {
       long long z = L - n_gemm;
       if (z < z1) {
         long long b = z * kZeroChunk;
-        zero_item<C>(p, b, b + kZeroChunk < z1_bytes ? b + kZeroChunk : z1_bytes);
+        fill_item<C>(p, b, b + kZeroChunk < z1_bytes ? b + kZeroChunk : z1_bytes);
       } else {
         z -= z1;
         long long base = (long long)hi_row * row_bytes;
         long long b = base + z * kZeroChunk;
         long long e = b + kZeroChunk;
         long long end = base + z2_bytes;
-        zero_item<C>(p, b, e < end ? e : end);
+        fill_item<C>(p, b, e < end ? e : end);
       }
       continue;
     }

@@ -14,7 +14,9 @@ constexpr int kQueues = 8;  // one per XCD
 constexpr uint32_t kFlagNegative = 0x1u;
 constexpr uint32_t kFlagExceed = 0x2u;
 constexpr uint32_t kFlagBadOffset = 0x4u;
-// Bytes of inactive rows zeroed by one work item.
+// What the rows outside the active groups receive.
+enum Fill : int32_t { kFillZero = 0, kFillCopy = 1, kFillKeep = 2 };
+// Bytes of inactive rows filled by one work item.
 constexpr int kZeroChunk = 64 * 1024;
 // dword 3 of a raw buffer resource on gfx9-family parts (32-bit data format).
 constexpr int kBufferRsrcWord3 = 0x00020000;
@@ -28,6 +30,10 @@ struct Params {
   const void* rhs_bias;         // [Ga, 1, N] or nullptr
   const float* lhs_scale;       // [M, nb] or nullptr
   void* out;                    // [M, N]
+  // rows outside the active groups: zeros (kFillZero), the rows of
+  // `existing` (kFillCopy), or left as they are (kFillKeep: existing is out)
+  const void* existing;         // [M, N] like out, or nullptr
+  int32_t fill;
   uint32_t* flags;
   // work queues of the transposed product: kQueues tile counters followed by
   // kQueues finished-workgroup counters, all zero between calls

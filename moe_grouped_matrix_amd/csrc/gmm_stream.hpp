@@ -339,20 +339,16 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
     }
   }
 
-  // rows outside the active groups: zero them last, after this workgroup's
+  // rows outside the active groups: fill them last, after this workgroup's
   // tiles (grid-stride over the whole grid)
   {
     const long long row_bytes = (long long)N * C::es_out;
     const int lo_row = pl.row_start[0], hi_row = pl.row_start[pl.ga];
-    char* out = reinterpret_cast<char*>(p.out);
-    const i32x4 z = {0, 0, 0, 0};
-    const long long z1 = (long long)lo_row * row_bytes;
-    const long long z2b = (long long)hi_row * row_bytes, z2e = (long long)M * row_bytes;
-    const long long total = z1 + (z2e - z2b);
-    for (long long o = ((long long)slot * C::T + tid) * 16; o < total; o += (long long)P * C::T * 16) {
-      const long long oo = o < z1 ? o : z2b + (o - z1);
-      *reinterpret_cast<i32x4*>(out + oo) = z;
-    }
+    const long long z1 = fill_rows(p, lo_row) * row_bytes;
+    const long long z2b = (long long)hi_row * row_bytes;
+    const long long total = z1 + fill_rows(p, M - hi_row) * row_bytes;
+    for (long long o = ((long long)slot * C::T + tid) * 16; o < total; o += (long long)P * C::T * 16)
+      fill16(p, o < z1 ? o : z2b + (o - z1));
   }
 }
 

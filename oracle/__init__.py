@@ -114,6 +114,7 @@ def gmm_reference(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tenso
                   rhs_scale: Optional[torch.Tensor] = None,
                   rhs_bias: Optional[torch.Tensor] = None,
                   lhs_scale: Optional[torch.Tensor] = None,
+                  existing_out: Optional[torch.Tensor] = None,
                   rows: Optional[Sequence[int]] = None,
                   return_row_group: bool = False):
     """Reference rows of gmm(lhs, rhs, group_sizes, ...) in float64.
@@ -122,7 +123,13 @@ def gmm_reference(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tenso
     group_sizes [G] int32; rhs_scale f32 [Ga,nb,1,N]; rhs_bias [Ga,1,N];
     lhs_scale f32 [M,nb].  ``rows`` selects output rows (all when None).
     Returns a float64 numpy array [len(rows), N] (and the group of each row,
-    -1 for none, when return_row_group)."""
+    -1 for none, when return_row_group).
+
+    existing_out [M,N] (gmm's existing_out, tpu-inference wheel diff page,
+    megablox/gmm.py): every output tile starts as existing_out and only the
+    rows of its group are stored over it, and no zero fill follows, so a row
+    of no active group is existing_out's row (its exact value) instead of
+    zero."""
     lib = _load()
     lhs, rhs, gs = _cpu(lhs), _cpu(rhs), _cpu(group_sizes)
     rhs_scale, rhs_bias, lhs_scale = _cpu(rhs_scale), _cpu(rhs_bias), _cpu(lhs_scale)
@@ -148,6 +155,10 @@ def gmm_reference(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tenso
         nb = lhs_scale.shape[1]
     if rhs_bias is not None and tuple(rhs_bias.shape) != (Ga, 1, N):
         raise OracleError("rhs_bias must be [Ga,1,N]")
+    if existing_out is not None:
+        existing_out = _cpu(existing_out)
+        if tuple(existing_out.shape) != (M, N):
+            raise OracleError("existing_out must be [M,N]")
     if rows is None:
         rows_arr = None
         n_rows = M
@@ -168,6 +179,10 @@ def gmm_reference(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tenso
     if rc != OK:
         raise OracleError({E_ARG: "invalid arguments", E_DATA: "invalid group sizes / offset",
                            E_NOMEM: "out of memory"}.get(rc, str(rc)))
+    if existing_out is not None:
+        ex = existing_out.double().numpy()
+        ex = ex if rows_arr is None else ex[rows_arr]
+        out[rg < 0] = ex[rg < 0]
     return (out, rg) if return_row_group else out
 
 
