@@ -31,18 +31,24 @@ sys.path.insert(0, ROOT)
 PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # dense MFMA TFLOP/s (MI355X)
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "moe_grouped_matrix_amd", "csrc", f)
-                  for f in ("gmm_device.hpp", "gmm_big.hpp", "gmm_stream.hpp", "gmm_tgmm.hpp", "gmm_params.hpp",
-                            "gmm_kernels.hip")]
+# the sources each workload's kernel is built from: committed counter
+# readings stay valid until one of them changes
+KERNEL_SOURCES_COMMON = ("gmm_params.hpp", "gmm_device.hpp", "gmm_kernels.hip")
+KERNEL_SOURCES = {
+    "moe_fwd_bf16": ("gmm_big.hpp",),
+    "moe_dlhs_bf16": ("gmm_big.hpp",),
+    "decode_fp8w": ("gmm_big.hpp", "gmm_stream.hpp"),
+    "tgmm_bf16": ("gmm_big.hpp", "gmm_tgmm.hpp"),
+}
 # workloads whose weights fit in the caches between calls: each timed call
 # starts from evicted L2 / Infinity Cache (a 512 MB write outside the events)
 EVICT = {"decode_fp8w", "tiny_fp32"}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(workload: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
+    for f in KERNEL_SOURCES_COMMON + KERNEL_SOURCES.get(workload, ()):
+        with open(os.path.join(ROOT, "moe_grouped_matrix_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -55,7 +61,7 @@ def measured_traffic(workload: str):
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash(workload):
         return None
     return rec.get("bytes_per_launch")
 

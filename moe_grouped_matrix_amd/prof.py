@@ -95,7 +95,7 @@ def cmd_traffic(a):
     f_scale = copy_bytes / (cf * 1024.0)
     w_scale = copy_bytes / (cw * 1024.0)
     rec = {
-        "kernel_source_hash": bench.kernel_source_hash(),
+        "kernel_source_hash": bench.kernel_source_hash(a.workload),
         "kernel": a.kernel,
         "fetch_bytes_per_launch": kf * 1024.0 * f_scale,
         "write_bytes_per_launch": kw * 1024.0 * w_scale,
