@@ -68,6 +68,10 @@ def _load():
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
         lib.oracle_round_bf16_array.restype = None
         lib.oracle_round_bf16_array.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.oracle_round_e4m3fn.restype = ctypes.c_uint8
+        lib.oracle_round_e4m3fn.argtypes = [ctypes.c_double]
+        lib.oracle_quant_fp8.restype = ctypes.c_int
+        lib.oracle_quant_fp8.argtypes = [vp, i64, i64, i64, vp, vp]
         lib.oracle_tgmm.restype = ctypes.c_int
         lib.oracle_tgmm.argtypes = [vp, i32, i64, i64,
                                     vp, i32, i64,
@@ -95,6 +99,32 @@ def round_bf16_bits(x: float) -> int:
 
 def decode_e4m3fn(code: int) -> float:
     return _load().oracle_decode_e4m3fn(code & 0xFF)
+
+
+def round_e4m3fn_code(x: float) -> int:
+    """e4m3fn code nearest to x, |x| <= 448, ties to the even mantissa."""
+    return _load().oracle_round_e4m3fn(float(x))
+
+
+def quant_fp8_reference(x: torch.Tensor, blk: int = 128):
+    """Per-token activation quantisation (per_token_group_quant_fp8, metrale
+    gemm_quant.rs page): x bf16 [M,K] -> (q float8_e4m3fn [M,K], scale f32
+    [M,K/blk]) with scale = amax/448 per block of blk (1 for an all-zero
+    block) and q the nearest e4m3fn value to clamp(x/scale, +-448), both in
+    binary32 (see oracle_quant_fp8 in gmm_oracle.c)."""
+    lib = _load()
+    x = _cpu(x)
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise OracleError("x must be a bf16 2-tensor")
+    M, K = x.shape
+    if blk <= 0 or K % blk:
+        raise OracleError("K must be a multiple of the block")
+    q = torch.empty(M, K, dtype=torch.uint8)
+    scale = torch.empty(M, K // blk, dtype=torch.float32)
+    rc = lib.oracle_quant_fp8(x.view(torch.int16).data_ptr(), M, K, blk, q.data_ptr(), scale.data_ptr())
+    if rc != OK:
+        raise OracleError("invalid arguments")
+    return q.view(torch.float8_e4m3fn), scale
 
 
 def _cpu(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:

@@ -289,3 +289,67 @@ int oracle_tgmm(const void* lhs, int lhs_dtype, int64_t M, int64_t K,
   free(o);
   return OR_OK;
 }
+
+/*
+ * Per-token activation quantisation to e4m3fn over blocks of `blk` elements
+ * of each row: the per_token_group_quant_fp8 launcher on the metrale
+ * gemm_quant.rs page (bf16 input [M,K] -> A_fp8 [M,K] e4m3 and a_scale
+ * [M,K/128] f32 over 128-element K groups; the scale is the activation
+ * scale of fp8_gemm_t_blockscaled on the same page, so x ~ q * scale).  The
+ * page gives shapes only; the arithmetic read in for both this oracle and
+ * the device kernel:
+ *   amax  = max |x| over the block (exact in binary32: x is bf16)
+ *   scale = amax / 448 in binary32, rounded to nearest (448 is the largest
+ *           finite e4m3fn value); 1 when amax is 0
+ *   q     = the e4m3fn value nearest to clamp(x / scale, -448, 448), where
+ *           x / scale is one binary32 division rounded to nearest; ties go to
+ *           the even mantissa; the sign of x is kept, so a negative value
+ *           that rounds to zero (and -0) gives the code 0x80
+ */
+
+/* e4m3fn code nearest to v, |v| <= 448 (ties to the even mantissa). */
+uint8_t oracle_round_e4m3fn(double v) {
+  const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  const double a = fabs(v);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);
+  e -= 1;                  /* a in [2^e, 2^(e+1)) */
+  if (e < -6) e = -6;      /* below 2^-6 the spacing is the subnormal one, 2^-9 */
+  const double quantum = ldexp(1.0, e - 3);
+  const double r = nearbyint(a / quantum) * quantum;  /* nearest; ties to an even multiple */
+  if (r == 0.0) return sign;
+  if (r < ldexp(1.0, -6)) return (uint8_t)(sign | (uint8_t)(r / ldexp(1.0, -9)));  /* subnormal m/8 * 2^-6 */
+  int er;
+  const double m = frexp(r, &er);                     /* r = m * 2^er, m in [0.5, 1) */
+  const int biased = er - 1 + 7;
+  const int mant = (int)(m * 16.0) - 8;               /* r / 2^(er-1) = 1 + mant/8 */
+  return (uint8_t)(sign | (uint8_t)(biased << 3) | (uint8_t)mant);
+}
+
+int oracle_quant_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t blk, uint8_t* q, float* scale) {
+  if (M < 0 || K <= 0 || blk <= 0 || K % blk) return OR_E_ARG;
+  const int64_t nb = K / blk;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < M; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint16_t* xb = x + r * K + b * blk;
+      float amax = 0.0f;
+      for (int64_t k = 0; k < blk; ++k) {
+        const float a = fabsf((float)oracle_decode_bf16(xb[k]));
+        if (a > amax) amax = a;
+      }
+      volatile float s = amax / 448.0f;
+      if (amax == 0.0f) s = 1.0f;
+      scale[r * nb + b] = s;
+      for (int64_t k = 0; k < blk; ++k) {
+        volatile float t = (float)oracle_decode_bf16(xb[k]) / s;
+        float c = t;
+        if (c > 448.0f) c = 448.0f;
+        if (c < -448.0f) c = -448.0f;
+        q[r * K + b * blk + k] = oracle_round_e4m3fn((double)c);
+      }
+    }
+  }
+  return OR_OK;
+}
