@@ -39,6 +39,7 @@ KERNEL_SOURCES = {
     "moe_dlhs_bf16": ("gmm_big.hpp",),
     "decode_fp8w": ("gmm_big.hpp", "gmm_stream.hpp"),
     "tgmm_bf16": ("gmm_big.hpp", "gmm_tgmm.hpp"),
+    "quant_fp8": ("gmm_quant.hip", "gmm_launch.hpp"),
 }
 # workloads whose weights fit in the caches between calls: each timed call
 # starts from evicted L2 / Infinity Cache (a 512 MB write outside the events)
@@ -70,16 +71,24 @@ def build_cases(workload: str, device):
     import workloads
     if workload in workloads.TGMM_FULL:
         return [workloads.TGMM_FULL[workload](device=device)]
+    if workload in workloads.QUANT_FULL:
+        return [workloads.QUANT_FULL[workload](device=device)]
     names = {"fwd+dlhs": ["moe_fwd_bf16", "moe_dlhs_bf16"]}.get(workload, [workload])
     return [workloads.FULL[n](device=device) for n in names]
 
 
 def is_tgmm(case) -> bool:
-    return not hasattr(case, "transpose_rhs")
+    return hasattr(case, "rhs") and not hasattr(case, "transpose_rhs")
+
+
+def is_quant(case) -> bool:
+    return hasattr(case, "x") and not hasattr(case, "rhs")
 
 
 def op_peak(case):
     import torch
+    if is_quant(case):
+        return "bf16", PEAK["bf16"]
     if case.lhs.dtype == torch.float8_e4m3fn:
         return "fp8", PEAK["fp8"]
     if case.lhs.dtype == torch.float32:
@@ -101,6 +110,8 @@ def cpu_baseline(cases, target_s: float = 20.0):
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     if any(is_tgmm(c) for c in cases):
         return cpu_baseline_tgmm(cases, target_s)
+    if any(is_quant(c) for c in cases):
+        return cpu_baseline_quant(cases, target_s)
     flops_total = 0.0
     secs_total = 0.0
     descr = []
@@ -176,6 +187,29 @@ def cpu_baseline_tgmm(cases, target_s: float = 20.0):
                       f"(fp64 oracle, {secs:.1f} s)"}
 
 
+def cpu_baseline_quant(cases, target_s: float = 20.0):
+    """Time the oracle's quantiser on a bounded sample of whole rows (every
+    row costs what it costs in the full problem), in algorithmic GB/s."""
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    case = cases[0]
+    rows = 4096
+    for phase in ("calibrate", "calibrate", "measure"):
+        n = min(rows, case.M)
+        x = case.x[:n].cpu()
+        t0 = time.perf_counter()
+        oracle.quant_fp8_reference(x, case.block)
+        secs = time.perf_counter() - t0
+        if phase == "calibrate":
+            rows = max(1, int(n * target_s / max(secs, 1e-3)))
+            if secs > 0.5 * target_s or n == case.M:
+                break
+    byts = n * case.K * 3 + n * (case.K // case.block) * 4
+    return {"value": byts / secs / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{case.name}: {n} of {case.M} rows (binary32 oracle, {secs:.1f} s)"}
+
+
 class ClockSampler:
     """Samples the shader clock and socket power with amd-smi (read-only
     queries) from a shell loop started as a child process before this
@@ -249,7 +283,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fwd+dlhs",
                     help="fwd+dlhs (default) or one of tiny_fp32, moe_fwd_bf16, moe_dlhs_bf16, "
-                         "decode_fp8w, w8a8_fp8, tgmm_bf16 (the weight gradient)")
+                         "decode_fp8w, w8a8_fp8, tgmm_bf16 (the weight gradient), "
+                         "quant_fp8 (the activation quantiser)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -269,14 +304,23 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     cases = build_cases(args.workload, dev)
-    outs = [torch.empty((c.num_active, c.K, c.N) if is_tgmm(c) else (c.M, c.N), dtype=c.out_dtype, device=dev)
-            for c in cases]
-    offs = [torch.tensor([c.group_offset], dtype=torch.int32, device=dev) if c.group_offset else None
+    def out_of(c):
+        if is_quant(c):
+            return (torch.empty((c.M, c.K), dtype=torch.float8_e4m3fn, device=dev),
+                    torch.empty((c.M, c.K // c.block), dtype=torch.float32, device=dev))
+        shape = (c.num_active, c.K, c.N) if is_tgmm(c) else (c.M, c.N)
+        return torch.empty(shape, dtype=c.out_dtype, device=dev)
+
+    outs = [out_of(c) for c in cases]
+    offs = [torch.tensor([c.group_offset], dtype=torch.int32, device=dev) if getattr(c, "group_offset", 0) else None
             for c in cases]
     stream = torch.cuda.current_stream(dev)
 
     def launch(i):
         c = cases[i]
+        if is_quant(c):
+            gmm_amd.quant_fp8(c.x, q=outs[i][0], scale=outs[i][1])
+            return
         if is_tgmm(c):
             gmm_amd.tgmm(c.lhs, c.rhs, c.group_sizes, num_active=c.num_active, group_offset=offs[i], out=outs[i])
             return
@@ -327,7 +371,12 @@ def main():
     # with eviction between calls the wall clock includes the scratch writes:
     # the job's rate is then taken from the kernels' own event times
     gpu_s = sum(sum(x) for x in per_kernel_ms) * 1e-3
-    value = step_flops * args.steps / (gpu_s if evict else wall) / 1e12
+    quant = all(is_quant(c) for c in cases)
+    if quant:  # an HBM-bound pass: its rate is bytes, not FLOPs
+        step_bytes = sum(c.algorithmic_bytes() for c in cases)
+        value = step_bytes * args.steps / (gpu_s if evict else wall) / 1e9
+    else:
+        value = step_flops * args.steps / (gpu_s if evict else wall) / 1e12
 
     # dominant kernel: the case with the largest total event time
     tot = [sum(x) for x in per_kernel_ms]
@@ -335,7 +384,7 @@ def main():
     dc = cases[d]
     avg_ms = statistics.mean(per_kernel_ms[d])
     kind, peak = op_peak(dc)
-    mem_bound = dc.name == "decode_fp8w"
+    mem_bound = dc.name in ("decode_fp8w", "quant_fp8")
     if mem_bound:
         achieved = dc.algorithmic_bytes() / (avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -363,12 +412,29 @@ def main():
                           "gbs_algorithmic": c.algorithmic_bytes() / (ms * 1e-3) / 1e9,
                           "active_rows": c.active_rows()}
 
-    metric = ("grouped-GEMM TFLOP/s and % MFMA peak, 128-expert bf16 fwd+dlhs"
-              if args.workload == "fwd+dlhs" else f"grouped-GEMM TFLOP/s, {args.workload}")
+    if quant:
+        metric = f"activation quantiser GB/s, {args.workload}"
+    elif args.workload == "fwd+dlhs":
+        metric = "grouped-GEMM TFLOP/s and % MFMA peak, 128-expert bf16 fwd+dlhs"
+    else:
+        metric = f"grouped-GEMM TFLOP/s, {args.workload}"
+
+    def shape_of(c):
+        if is_quant(c):
+            return {"M": c.M, "K": c.K, "block": c.block, "op": "quant_fp8"}
+        return {"M": c.M, "K": c.K, "N": c.N, "G": int(c.group_sizes.numel()), "Ga": c.num_active,
+                "transpose_rhs": getattr(c, "transpose_rhs", None), "op": "tgmm" if is_tgmm(c) else "gmm"}
+
+    if quant:
+        dtype = "bf16 -> fp8-e4m3"
+    elif any(c.rhs.dtype == torch.float8_e4m3fn and c.lhs.dtype == torch.bfloat16 for c in cases):
+        dtype = "bf16 x fp8-e4m3"
+    else:
+        dtype = {"bf16": "bf16", "fp8": "fp8-e4m3", "f32": "f32"}[op_peak(cases[0])[0]]
     line = {
         "metric": metric,
         "value": value,
-        "unit": "TFLOP/s",
+        "unit": "GB/s" if quant else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -376,15 +442,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3", "f32": "f32"}[op_peak(cases[0])[0]]
-        if not any(c.rhs.dtype == torch.float8_e4m3fn and c.lhs.dtype == torch.bfloat16 for c in cases)
-        else "bf16 x fp8-e4m3",
-        "data": "synthetic (seeded; router group sizes, normal values)",
+        "dtype": dtype,
+        "data": "synthetic (seeded; normal values)" if quant else "synthetic (seeded; router group sizes, normal values)",
         "config": {"workload": " + ".join(c.name for c in cases),
-                   "shapes": [{"M": c.M, "K": c.K, "N": c.N, "G": int(c.group_sizes.numel()),
-                               "Ga": c.num_active, "transpose_rhs": getattr(c, "transpose_rhs", None),
-                               "op": "tgmm" if is_tgmm(c) else "gmm"} for c in cases],
-                   "frac_of_peak": value / PEAK[op_peak(cases[0])[0]]},
+                   "shapes": [shape_of(c) for c in cases],
+                   "frac_of_peak": value / (HBM_PEAK_GBS if quant else PEAK[op_peak(cases[0])[0]])},
         "roofline": roof,
         "detail": detail,
     }

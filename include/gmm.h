@@ -163,6 +163,33 @@ gmm_status gmm_run_existing_out(gmm_handle* h,
                                 void* stream);
 
 /*
+ * gmm_quant_fp8_run: queue the per-token activation quantiser on `stream`:
+ * per_token_group_quant_fp8 of the metrale gemm_quant.rs page, bf16 x [M,K]
+ * to e4m3fn q [M,K] and an f32 scale per 128-element block of each row,
+ * scale [M,K/128] -- the lhs and lhs_scale that gmm_run takes for fp8 x fp8
+ * products (the page's fp8_gemm_t_blockscaled activation scale, x ~ q *
+ * scale).  The page gives the shapes only; the arithmetic is
+ *   scale[r,b] = amax / 448 over x[r, 128b .. 128b+127] in binary32
+ *                (1 when the block is all zero),
+ *   q[r,k]     = the e4m3fn value nearest to clamp(x[r,k] / scale[r,b],
+ *                -448, 448), the quotient one correctly rounded binary32
+ *                division, ties to the even mantissa, the sign kept (a
+ *                negative value that rounds to zero is 0x80).
+ *
+ *   x      [M,K] BF16, K % 128 == 0 (GMM_E_INVALID otherwise).
+ *   q      [M,K] F8E4M3FN, written.
+ *   scale  [M,K/128] F32, written.
+ *   All three on the device, 16-byte aligned, caller-owned, not overlapping
+ *   (GMM_E_INVALID otherwise).  Values outside the finite bf16 range (NaN,
+ *   infinity) are outside the contract.  A launch failure returns GMM_E_HIP.
+ */
+gmm_status gmm_quant_fp8_run(gmm_handle* h,
+                             const gmm_tensor* x,
+                             const gmm_tensor* q,
+                             const gmm_tensor* scale,
+                             void* stream);
+
+/*
  * gmm_tgmm_run: queue the transposed grouped matmul, the weight gradient of
  * gmm, on `stream`.  For each active group h = g - s (g = s .. s+Ga-1),
  *

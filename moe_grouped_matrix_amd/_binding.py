@@ -21,7 +21,7 @@ GMM_OK, GMM_E_INVALID, GMM_E_UNSUPPORTED, GMM_E_HIP, GMM_E_DEVICE_DATA = 0, -1, 
 FLAG_NEGATIVE_SIZE, FLAG_SIZES_EXCEED_M, FLAG_BAD_OFFSET = 0x1, 0x2, 0x4
 
 EXPORTED = ("gmm_create", "gmm_destroy", "gmm_last_error", "gmm_run", "gmm_run_existing_out", "gmm_tgmm_run",
-            "gmm_device_flags", "gmm_set_tile_policy", "gmm_debug_worklist")
+            "gmm_quant_fp8_run", "gmm_device_flags", "gmm_set_tile_policy", "gmm_debug_worklist")
 
 _DTYPE = {torch.float32: GMM_F32, torch.bfloat16: GMM_BF16,
           torch.float8_e4m3fn: GMM_F8E4M3FN, torch.int32: GMM_I32}
@@ -75,6 +75,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.gmm_run.restype = ctypes.c_int
             lib.gmm_run_existing_out.argtypes = [vp, tp, tp, tp, tp, tp, tp, vp, ctypes.c_int, tp, tp, vp]
             lib.gmm_run_existing_out.restype = ctypes.c_int
+            lib.gmm_quant_fp8_run.argtypes = [vp, tp, tp, tp, vp]
+            lib.gmm_quant_fp8_run.restype = ctypes.c_int
             lib.gmm_tgmm_run.argtypes = [vp, tp, tp, tp, vp, tp, vp]
             lib.gmm_tgmm_run.restype = ctypes.c_int
             lib.gmm_device_flags.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
@@ -197,6 +199,26 @@ def gmm(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,
         keep.record_stream(st)
     _raise(status, h)
     return out
+
+
+def quant_fp8(x: torch.Tensor, *, q: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,
+              stream: Optional[torch.cuda.Stream] = None):
+    """Per-token activation quantiser through libgmm.so (gmm_quant_fp8_run):
+    x bf16 [M,K] (K % 128 == 0) -> (q float8_e4m3fn [M,K], scale float32
+    [M,K/128]), x ~ q * scale per 128-element block; the pair gmm() takes as
+    lhs and lhs_scale for fp8 x fp8 products."""
+    lib = load()
+    dev = x.device
+    h = handle(dev)
+    M, K = (x.shape[0], x.shape[1]) if x.dim() == 2 else (0, 0)
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+    if scale is None:
+        scale = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    views = [_view(t, n) for t, n in ((x, "x"), (q, "q"), (scale, "scale"))]
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    _raise(lib.gmm_quant_fp8_run(h, *[_ref(v) for v in views], ctypes.c_void_p(st.cuda_stream)), h)
+    return q, scale
 
 
 def tgmm(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,

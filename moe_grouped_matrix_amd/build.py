@@ -12,7 +12,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgmm.so")
-SOURCES = [os.path.join(CSRC, "gmm_kernels.hip"), os.path.join(CSRC, "gmm_api.cpp")]
+SOURCES = [os.path.join(CSRC, "gmm_kernels.hip"), os.path.join(CSRC, "gmm_quant.hip"),
+           os.path.join(CSRC, "gmm_api.cpp")]
 
 # Packed fp32 VALU instructions are kept out of the generated code.
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

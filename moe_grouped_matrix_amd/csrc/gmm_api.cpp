@@ -309,6 +309,38 @@ gmm_status gmm_run_existing_out(gmm_handle* h, const gmm_tensor* lhs, const gmm_
                  existing_out, out, stream);
 }
 
+gmm_status gmm_quant_fp8_run(gmm_handle* h, const gmm_tensor* x, const gmm_tensor* q, const gmm_tensor* scale,
+                             void* stream) {
+  if (!h) return GMM_E_INVALID;
+  h->err.clear();
+  if (!x || !q || !scale) return fail(h, GMM_E_INVALID, "x, q and scale are required");
+  if (x->ndim != 2 || x->dtype != GMM_BF16) return fail(h, GMM_E_INVALID, "x must be a bf16 2-tensor");
+  const long long M = x->shape[0], K = x->shape[1];
+  if (M < 0 || K <= 0) return fail(h, GMM_E_INVALID, "negative or zero extent");
+  if (K % 128) return fail(h, GMM_E_INVALID, "K must be a multiple of the 128-element block");
+  if (q->ndim != 2 || q->dtype != GMM_F8E4M3FN || q->shape[0] != M || q->shape[1] != K)
+    return fail(h, GMM_E_INVALID, "q must be e4m3fn [M,K] like x, got " + shape_str(q));
+  if (scale->ndim != 2 || scale->dtype != GMM_F32 || scale->shape[0] != M || scale->shape[1] != K / 128)
+    return fail(h, GMM_E_INVALID, "scale must be f32 [M,K/128], got " + shape_str(scale));
+  const gmm_tensor* ts[] = {x, q, scale};
+  for (const gmm_tensor* t : ts) {
+    if (M > 0 && !t->data) return fail(h, GMM_E_INVALID, "null data pointer");
+    if (!aligned16(t->data)) return fail(h, GMM_E_INVALID, "tensor data must be 16-byte aligned");
+  }
+  if (overlaps(x, q) || overlaps(x, scale) || overlaps(q, scale))
+    return fail(h, GMM_E_INVALID, "x, q and scale must not overlap");
+  if (M == 0) return GMM_OK;
+  gmmk::QuantParams p{};
+  p.x = static_cast<const uint16_t*>(x->data);
+  p.q = static_cast<uint8_t*>(const_cast<void*>(q->data));
+  p.scale = static_cast<float*>(const_cast<void*>(scale->data));
+  p.blocks = M * (K / 128);
+  DeviceGuard g(h->device);
+  hipError_t e = gmmk::launch_quant_fp8(p, h->cu_count, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(h, GMM_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return GMM_OK;
+}
+
 gmm_status gmm_tgmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs,
                         const gmm_tensor* group_sizes, const int32_t* group_offset, const gmm_tensor* out,
                         void* stream) {

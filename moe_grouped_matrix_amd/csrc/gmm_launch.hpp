@@ -30,6 +30,18 @@ hipError_t launch_gmm(const Params& p, const KernelChoice& c, int cu_count, hipS
 // Queue the transposed grouped matmul (out [Ga,K,N]).
 hipError_t launch_tgmm(const Params& p, int cu_count, hipStream_t stream);
 
+// Activation quantiser arguments: x bf16 [M,K], q e4m3fn [M,K], scale f32
+// [M,K/128], blocks = M * K / 128 (K % 128 == 0).
+struct QuantParams {
+  const uint16_t* x;
+  uint8_t* q;
+  float* scale;
+  long long blocks;
+};
+
+// Queue the activation quantiser (gmm_quant.hip).
+hipError_t launch_quant_fp8(const QuantParams& p, int cu_count, hipStream_t stream);
+
 // Queue the worklist export kernel (one workgroup).
 hipError_t launch_worklist(const Params& p, int tm, int32_t* tiles, long long capacity,
                            int32_t* count, hipStream_t stream);

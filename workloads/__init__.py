@@ -326,6 +326,52 @@ def tgmm_bf16(seed: int = 1006, device="cpu", tokens: int = 32768, experts: int 
                     meta=dict(tokens=tokens, experts=experts, top_k=top_k))
 
 
+@dataclasses.dataclass
+class QuantCase:
+    """Input of the per-token activation quantiser: x bf16 [M,K], blocks of
+    ``block`` elements along each row."""
+    name: str
+    x: torch.Tensor
+    block: int = 128
+    meta: Dict = dataclasses.field(default_factory=dict)
+
+    @property
+    def M(self):
+        return self.x.shape[0]
+
+    @property
+    def K(self):
+        return self.x.shape[1]
+
+    def active_rows(self):
+        return self.M
+
+    def flops(self):
+        return 0
+
+    def algorithmic_bytes(self):
+        """x read once (2 bytes an element), the codes written once (1 byte)
+        and one f32 scale per block."""
+        return self.M * self.K * 3 + self.M * (self.K // self.block) * 4
+
+    def to(self, device):
+        return dataclasses.replace(self, x=self.x.to(device))
+
+
+def quant_fp8_act(seed: int = 1002, device="cpu", tokens: int = 32768, top_k: int = 8, K: int = 1408,
+                  std: float = 0.02) -> QuantCase:
+    """The forward workload's activations, bf16 [tokens*top_k, K] N(0,std)
+    (the same draw as moe_forward_bf16's lhs), to be quantised per token per
+    128-element block for the W8A8 product."""
+    x = normal((tokens * top_k, K), std, seed + 1, device, torch.bfloat16)
+    return QuantCase("quant_fp8", x, meta=dict(tokens=tokens, top_k=top_k))
+
+
+QUANT_FULL = {
+    "quant_fp8": lambda device="cpu": quant_fp8_act(device=device),
+}
+
+
 TGMM_FULL = {
     "tgmm_bf16": lambda device="cpu": tgmm_bf16(device=device),
 }
