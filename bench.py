@@ -42,7 +42,7 @@ KERNEL_SOURCES = {
     "quant_fp8": ("gmm_quant.hip", "gmm_launch.hpp"),
 }
 # workloads whose weights fit in the caches between calls: each timed call
-# starts from evicted L2 / Infinity Cache (a 512 MB write outside the events)
+# starts from evicted L2 / Infinity Cache (a 512 MB read outside the events)
 EVICT = {"decode_fp8w", "tiny_fp32"}
 
 
@@ -337,7 +337,10 @@ def main():
 
     # HIP events around every launch of the timed steps, on the launch stream.
     evict = args.workload in EVICT
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if evict else None
+    # eviction reads 512 MB (twice the Infinity Cache): a write would leave the
+    # caches full of dirty lines whose write-back the timed kernel then pays
+    scratch = torch.ones(512 << 18, dtype=torch.float32, device=dev) if evict else None
+    sink = torch.empty(1, dtype=torch.float32, device=dev) if evict else None
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in cases] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -346,7 +349,7 @@ def main():
     for s in range(args.steps):
         for i in range(len(cases)):
             if evict:
-                scratch.fill_(s & 0xFF)
+                torch.sum(scratch, dim=0, keepdim=True, out=sink)
             ev[s][i][0].record(stream)
             launch(i)
             ev[s][i][1].record(stream)
@@ -368,7 +371,7 @@ def main():
                      for i in range(len(cases))]
     flops = [c.flops() for c in cases]
     step_flops = sum(flops)
-    # with eviction between calls the wall clock includes the scratch writes:
+    # with eviction between calls the wall clock includes the scratch reads:
     # the job's rate is then taken from the kernels' own event times
     gpu_s = sum(sum(x) for x in per_kernel_ms) * 1e-3
     quant = all(is_quant(c) for c in cases)

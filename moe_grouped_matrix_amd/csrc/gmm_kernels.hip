@@ -65,10 +65,11 @@ hipError_t launch_big(const Params& p, int cu_count, hipStream_t stream) {
 
 template <class C>
 hipError_t launch_stream(const Params& p, int cu_count, hipStream_t stream) {
-  const long long n_tiles = (p.N + C::BN - 1) / C::BN;
-  const long long m_tiles = (p.M + C::BM - 1) / C::BM + p.Ga;
-  long long grid = cu_count;  // one workgroup per CU (LDS-bound)
-  if (grid > m_tiles * n_tiles && m_tiles * n_tiles >= 8) grid = m_tiles * n_tiles;
+  // One workgroup per CU (LDS-bound), even when there are fewer tiles:
+  // workgroups without a tile still take their share of the rows outside
+  // the active groups, which can be most of the output (an expert shard of
+  // a decode batch).
+  long long grid = cu_count;
   if (grid >= 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(gmm_stream_kernel<C>, dim3((unsigned)grid), dim3(C::T), 0, stream, p);

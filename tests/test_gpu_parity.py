@@ -247,6 +247,22 @@ STREAM_CASES = [
 ]
 
 
+def test_weight_streaming_kernel_mostly_inactive_rows():
+    """An expert shard of a decode batch: 2 of 24 experts active, so almost
+    all of the 2048 output rows lie outside the active groups and are zeroed
+    by workgroups that have no tile."""
+    import moe_grouped_matrix_amd as m
+    m.set_tile_policy(0)
+    case = workloads.decode_fp8_weight(tokens=256, experts=24, K=768, N=328, forced_empty=8,
+                                       group_offset=5, num_active=2, device="cuda")
+    print(f"stream shard M={case.M} active_rows={case.active_rows()}", flush=True)
+    out = run_gpu(case)
+    lo, hi = active_range(case)
+    assert_zero_rows(out, lo, hi)
+    compare(out.cpu()[lo:hi], reference(case)[lo:hi], case.out_dtype, "stream shard")
+    assert m.device_flags() == 0
+
+
 @pytest.mark.parametrize("tokens,K,N,out_dtype,bias,scaled", STREAM_CASES,
                          ids=["bf16out_bias", "f32out_f32bias", "noscale_nobias", "blk256", "k640_n136",
                               "rows_over_32"])
