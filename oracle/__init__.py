@@ -32,8 +32,8 @@ _SRC = os.path.join(_HERE, "gmm_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F32, BF16, E4M3FN = 0, 1, 2
-_DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: E4M3FN}
+F32, BF16, E4M3FN, E5M2 = 0, 1, 2, 3
+_DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: E4M3FN, torch.float8_e5m2: E5M2}
 
 OK, E_ARG, E_DATA, E_NOMEM = 0, -1, -4, -5
 
@@ -63,6 +63,8 @@ def _load():
         lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
         lib.oracle_decode_e4m3fn.restype = ctypes.c_double
         lib.oracle_decode_e4m3fn.argtypes = [ctypes.c_uint8]
+        lib.oracle_decode_e5m2.restype = ctypes.c_double
+        lib.oracle_decode_e5m2.argtypes = [ctypes.c_uint8]
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.oracle_round_bf16.restype = ctypes.c_uint16
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
@@ -99,6 +101,10 @@ def round_bf16_bits(x: float) -> int:
 
 def decode_e4m3fn(code: int) -> float:
     return _load().oracle_decode_e4m3fn(code & 0xFF)
+
+
+def decode_e5m2(code: int) -> float:
+    return _load().oracle_decode_e5m2(code & 0xFF)
 
 
 def round_e4m3fn_code(x: float) -> int:

@@ -43,6 +43,11 @@
  *   e4m3fn   1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent
  *            field 0 encodes subnormals m/8 * 2^-6; S.1111.111 is NaN; there
  *            are no infinities (OCP 8-bit floating point specification).
+ *   e5m2     1 sign bit, 5 exponent bits (bias 15), 2 mantissa bits; exponent
+ *            field 0 encodes subnormals m/4 * 2^-14; exponent field 31 is
+ *            infinity (m = 0) or NaN (same specification; one of the dtypes
+ *            the Megablox gmm accepts, assert_is_supported_dtype on the
+ *            tpu-inference wheel diff page).
  */
 #include <math.h>
 #include <stdint.h>
@@ -52,6 +57,7 @@
 #define OR_F32 0
 #define OR_BF16 1
 #define OR_E4M3FN 2
+#define OR_E5M2 3
 
 #define OR_OK 0
 #define OR_E_ARG (-1)
@@ -75,6 +81,19 @@ double oracle_decode_e4m3fn(uint8_t code) {
     v = ldexp((double)m / 8.0, -6);
   else
     v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -v : v;
+}
+
+double oracle_decode_e5m2(uint8_t code) {
+  int sign = (code >> 7) & 1;
+  int e = (code >> 2) & 0x1F;
+  int m = code & 0x3;
+  double v;
+  if (e == 0x1F) v = m ? NAN : INFINITY;
+  else if (e == 0)
+    v = ldexp((double)m / 4.0, -14);
+  else
+    v = ldexp(1.0 + (double)m / 4.0, e - 15);
   return sign ? -v : v;
 }
 
@@ -115,11 +134,12 @@ static double load_elem(const void* base, int dtype, int64_t idx) {
     case OR_F32: return (double)((const float*)base)[idx];
     case OR_BF16: return oracle_decode_bf16(((const uint16_t*)base)[idx]);
     case OR_E4M3FN: return oracle_decode_e4m3fn(((const uint8_t*)base)[idx]);
+    case OR_E5M2: return oracle_decode_e5m2(((const uint8_t*)base)[idx]);
     default: return NAN;
   }
 }
 
-static int dtype_ok(int d) { return d == OR_F32 || d == OR_BF16 || d == OR_E4M3FN; }
+static int dtype_ok(int d) { return d == OR_F32 || d == OR_BF16 || d == OR_E4M3FN || d == OR_E5M2; }
 
 /*
  * Group offsets o[0..G] (int64, so no overflow) from group_sizes.
