@@ -49,7 +49,8 @@ typedef enum {
   GMM_F32 = 0,       /* IEEE binary32 */
   GMM_BF16 = 1,      /* bfloat16 */
   GMM_F8E4M3FN = 2,  /* OCP e4m3fn: bias 7, max 448, no infinities */
-  GMM_I32 = 3        /* int32 (group_sizes only) */
+  GMM_I32 = 3,       /* int32 (group_sizes only) */
+  GMM_F8E5M2 = 4     /* OCP e5m2: bias 15, max 57344, with infinities and NaN */
 } gmm_dtype;
 
 typedef enum {
@@ -94,12 +95,16 @@ const char* gmm_last_error(const gmm_handle* h);
 /*
  * gmm_run: queue out = gmm(lhs, rhs, group_sizes, ...) on `stream`.
  *
- *   lhs          [M,K]; F32, BF16 or F8E4M3FN.
+ *   lhs          [M,K]; F32, BF16, F8E4M3FN or F8E5M2.
  *   rhs          [Ga,N,K] (transpose_rhs == 0) or [Ga,K,N] (== 1).
  *                Supported (lhs, rhs) pairs: (F32,F32), (BF16,BF16),
- *                (BF16,F8E4M3FN: the weight is widened exactly to bf16),
- *                (F8E4M3FN,F8E4M3FN: fp8 x fp8 products).  F8E4M3FN weights
- *                need transpose_rhs == 0.
+ *                (BF16, F8E4M3FN or F8E5M2: the weight is widened exactly
+ *                to bf16), (F8E4M3FN or F8E5M2, F8E4M3FN or F8E5M2: fp8 x
+ *                fp8 products, either format on either side; e5m2 is one of
+ *                the dtypes of the Megablox gmm's whitelist on the
+ *                tpu-inference wheel diff page).  fp8 weights need
+ *                transpose_rhs == 0.  Infinite or NaN e5m2 codes are outside
+ *                the contract.
  *   group_sizes  [G] I32 on the device, 1 <= G <= 1024.
  *   rhs_scale    NULL or F32 [Ga,nb,1,N]; K % nb == 0.
  *   rhs_bias     NULL or [Ga,1,N], F32 or BF16.

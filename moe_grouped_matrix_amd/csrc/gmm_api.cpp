@@ -62,6 +62,7 @@ int elem_size(int dtype) {
     case GMM_F32: return 4;
     case GMM_BF16: return 2;
     case GMM_F8E4M3FN: return 1;
+    case GMM_F8E5M2: return 1;
     case GMM_I32: return 4;
     default: return 0;
   }
@@ -170,11 +171,13 @@ gmm_status run_gmm(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs, 
     kc.op = gmmk::Op::F32;
   } else if (ld == GMM_BF16 && rd == GMM_BF16) {
     kc.op = gmmk::Op::BF16;
-  } else if (ld == GMM_BF16 && rd == GMM_F8E4M3FN) {
+  } else if (ld == GMM_BF16 && (rd == GMM_F8E4M3FN || rd == GMM_F8E5M2)) {
     kc.op = gmmk::Op::BF16;
     kc.b_fp8 = true;
-  } else if (ld == GMM_F8E4M3FN && rd == GMM_F8E4M3FN) {
+    kc.fmt = rd == GMM_F8E5M2 ? 2 : 0;
+  } else if ((ld == GMM_F8E4M3FN || ld == GMM_F8E5M2) && (rd == GMM_F8E4M3FN || rd == GMM_F8E5M2)) {
     kc.op = gmmk::Op::FP8;
+    kc.fmt = (ld == GMM_F8E5M2 ? 1 : 0) | (rd == GMM_F8E5M2 ? 2 : 0);
   } else {
     if (elem_size(ld) == 0 || elem_size(rd) == 0 || ld == GMM_I32 || rd == GMM_I32)
       return fail(h, GMM_E_INVALID, "unsupported lhs / rhs dtype");
@@ -182,7 +185,7 @@ gmm_status run_gmm(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs, 
   }
   kc.nn = transpose_rhs != 0;
   if (kc.nn && (kc.b_fp8 || kc.op == gmmk::Op::FP8))
-    return fail(h, GMM_E_UNSUPPORTED, "e4m3 weights are read in the [G,N,K] layout only");
+    return fail(h, GMM_E_UNSUPPORTED, "fp8 weights are read in the [G,N,K] layout only");
 
   long long nb = 1;
   if (rhs_scale) {

@@ -190,18 +190,26 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long b
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufferRsrcWord3);
 }
 
-// 8 e4m3fn bytes widened to 8 bf16 (exact: every e4m3fn value is a bf16).
-__device__ inline i32x4 e4m3x8_to_bf16x8(i32x2 v) {
+// Two fp8 values (bytes 0-1 or 2-3 of w) widened to two bf16: format F = 0
+// e4m3fn, 1 e5m2.  Exact: every finite value of either is a bf16.
+template <int F>
+__device__ __forceinline__ bf16x2 fp8x2_to_bf16x2(unsigned w, bool hi) {
+  if constexpr (F == 0)
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  else
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, false);
+}
+
+// 8 fp8 bytes of format F widened to 8 bf16.
+template <int F>
+__device__ inline i32x4 fp8x8_to_bf16x8(i32x2 v) {
   i32x4 r;
-  bf16x2 t;
-  t = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[0], 1.0f, false);
-  r[0] = __builtin_bit_cast(int, t);
-  t = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[0], 1.0f, true);
-  r[1] = __builtin_bit_cast(int, t);
-  t = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[1], 1.0f, false);
-  r[2] = __builtin_bit_cast(int, t);
-  t = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[1], 1.0f, true);
-  r[3] = __builtin_bit_cast(int, t);
+  r[0] = __builtin_bit_cast(int, fp8x2_to_bf16x2<F>((unsigned)v[0], false));
+  r[1] = __builtin_bit_cast(int, fp8x2_to_bf16x2<F>((unsigned)v[0], true));
+  r[2] = __builtin_bit_cast(int, fp8x2_to_bf16x2<F>((unsigned)v[1], false));
+  r[3] = __builtin_bit_cast(int, fp8x2_to_bf16x2<F>((unsigned)v[1], true));
   return r;
 }
 
@@ -221,12 +229,15 @@ __device__ inline int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 
 // ---------------------------------------------------------------------------
 // tile configurations
 
-template <Op OP, bool NN_, bool BFP8_, int BM_, int BN_, int WM_, int WN_, bool SCALED_>
+// FMT_: the fp8 formats, bit 0 for lhs and bit 1 for rhs (0 e4m3fn, 1 e5m2;
+// the format codes of the f8f6f4 matrix instructions).
+template <Op OP, bool NN_, bool BFP8_, int BM_, int BN_, int WM_, int WN_, bool SCALED_, int FMT_ = 0>
 struct Cfg {
   static constexpr Op op = OP;
   static constexpr bool NN = NN_;        // rhs is [Ga,K,N]
-  static constexpr bool B_FP8 = BFP8_;   // e4m3 rhs widened to bf16 operands
+  static constexpr bool B_FP8 = BFP8_;   // fp8 rhs widened to bf16 operands
   static constexpr bool SCALED = SCALED_;
+  static constexpr int FA = FMT_ & 1, FB = (FMT_ >> 1) & 1;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int T = 64 * WM * WN;
   static constexpr int ES = OP == Op::F32 ? 4 : (OP == Op::BF16 ? 2 : 1);  // operand bytes
@@ -245,7 +256,9 @@ struct Cfg {
   static_assert(B_CH >= 1 && B_CH * T == BN * 8, "B tile must split evenly");
   static_assert(!NN || (!B_FP8 && OP != Op::FP8), "NN needs f32 or bf16 weights");
   static_assert(!NN || NW == 2 || NW == 4 || NW == 8, "NN thread block width");
-  static_assert(!B_FP8 || OP == Op::BF16, "e4m3 weights widen to bf16");
+  static_assert(!B_FP8 || OP == Op::BF16, "fp8 weights widen to bf16");
+  static_assert(OP == Op::FP8 || FA == 0, "an lhs format only for fp8 x fp8");
+  static_assert(OP == Op::FP8 || B_FP8 || FB == 0, "an rhs format only for fp8 weights");
 };
 
 // ---------------------------------------------------------------------------
@@ -254,7 +267,7 @@ struct Cfg {
 template <class C>
 struct Stage {
   i32x4 a[C::A_CH];
-  // NT: B_CH chunks of operand (or e4m3 half-chunks in .x/.y when B_FP8);
+  // NT: B_CH chunks of operand (or fp8 half-chunks in .x/.y when B_FP8);
   // NN: KB rows of NW elements, packed into B_CH chunks.
   i32x4 b[C::B_CH];
 };
@@ -324,7 +337,7 @@ __device__ inline void store_tile(const C&, const Stage<C>& st, char* sa, char* 
     for (int i = 0; i < C::B_CH; ++i) {
       const int c = tid + i * C::T;
       i32x4 v = st.b[i];
-      if constexpr (C::B_FP8) v = e4m3x8_to_bf16x8(i32x2{st.b[i][0], st.b[i][1]});
+      if constexpr (C::B_FP8) v = fp8x8_to_bf16x8<C::FB>(i32x2{st.b[i][0], st.b[i][1]});
       *reinterpret_cast<i32x4*>(sb + lds_off(c >> 3, c & 7)) = v;
     }
   } else {
@@ -378,7 +391,7 @@ __device__ inline void mma_tile(f32x4 (&acc)[C::FM][C::FN], const char* sa, cons
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn)
         acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[fn], acc[fm][fn],
-                                                                       0, 0, 0, 0, 0, 0);
+                                                                       C::FA, C::FB, 0, 0, 0, 0);
     }
   } else {
 #pragma unroll

@@ -17,13 +17,13 @@ namespace {
 // partial and the running total both stay in registers.  Small: 32 x 64,
 // four waves of 32 x 16 (decode-sized groups).  F32 uses 64 x 64 tiles of
 // four 32 x 32 waves.
-template <Op OP, bool NN, bool BF8, bool SC, SizeClass SZ>
+template <Op OP, bool NN, bool BF8, bool SC, SizeClass SZ, int FMT>
 struct Pick {
-  using type = Cfg<OP, NN, BF8, 256, 128, SC ? 4 : 2, 2, SC>;
+  using type = Cfg<OP, NN, BF8, 256, 128, SC ? 4 : 2, 2, SC, FMT>;
 };
-template <Op OP, bool NN, bool BF8, bool SC>
-struct Pick<OP, NN, BF8, SC, SizeClass::Small> {
-  using type = Cfg<OP, NN, BF8, 32, 64, 1, 4, SC>;
+template <Op OP, bool NN, bool BF8, bool SC, int FMT>
+struct Pick<OP, NN, BF8, SC, SizeClass::Small, FMT> {
+  using type = Cfg<OP, NN, BF8, 32, 64, 1, 4, SC, FMT>;
 };
 
 template <class C>
@@ -96,7 +96,8 @@ hipError_t launch_tgmm_cfg(const Params& p, int cu_count, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <Op OP, bool NN, bool BF8, bool SC>
+// FMT: the fp8 formats (bit 0 lhs, bit 1 rhs; 0 e4m3fn, 1 e5m2).
+template <Op OP, bool NN, bool BF8, bool SC, int FMT>
 hipError_t by_size(const Params& p, SizeClass sz, int cu, hipStream_t st) {
   if constexpr (OP == Op::F32) return launch_cfg<Cfg<Op::F32, NN, false, 64, 64, 2, 2, SC>>(p, cu, st);
   if constexpr (OP == Op::BF16 && !BF8 && !SC) {
@@ -108,18 +109,19 @@ hipError_t by_size(const Params& p, SizeClass sz, int cu, hipStream_t st) {
   }
   if constexpr (OP == Op::BF16 && BF8 && !NN) {
     if (sz == SizeClass::Small && stream_fits(p)) {
-      if (p.out_f32) return launch_stream<StreamCfg<true>>(p, cu, st);
-      return launch_stream<StreamCfg<false>>(p, cu, st);
+      if (p.out_f32) return launch_stream<StreamCfg<true, (FMT >> 1)>>(p, cu, st);
+      return launch_stream<StreamCfg<false, (FMT >> 1)>>(p, cu, st);
     }
   }
-  if (sz == SizeClass::Big) return launch_cfg<typename Pick<OP, NN, BF8, SC, SizeClass::Big>::type>(p, cu, st);
-  return launch_cfg<typename Pick<OP, NN, BF8, SC, SizeClass::Small>::type>(p, cu, st);
+  if (sz == SizeClass::Big)
+    return launch_cfg<typename Pick<OP, NN, BF8, SC, SizeClass::Big, FMT>::type>(p, cu, st);
+  return launch_cfg<typename Pick<OP, NN, BF8, SC, SizeClass::Small, FMT>::type>(p, cu, st);
 }
 
-template <Op OP, bool NN, bool BF8>
+template <Op OP, bool NN, bool BF8, int FMT = 0>
 hipError_t by_scaled(const Params& p, const KernelChoice& c, int cu, hipStream_t st) {
-  if (c.scaled) return by_size<OP, NN, BF8, true>(p, c.size, cu, st);
-  return by_size<OP, NN, BF8, false>(p, c.size, cu, st);
+  if (c.scaled) return by_size<OP, NN, BF8, true, FMT>(p, c.size, cu, st);
+  return by_size<OP, NN, BF8, false, FMT>(p, c.size, cu, st);
 }
 
 }  // namespace
@@ -132,19 +134,27 @@ int tile_m(const KernelChoice& c) {
 hipError_t launch_gmm(const Params& p, const KernelChoice& c, int cu, hipStream_t st) {
   switch (c.op) {
     case Op::F32:
-      if (c.b_fp8) return hipErrorInvalidValue;
+      if (c.b_fp8 || c.fmt) return hipErrorInvalidValue;
       return c.nn ? by_scaled<Op::F32, true, false>(p, c, cu, st)
                   : by_scaled<Op::F32, false, false>(p, c, cu, st);
     case Op::BF16:
       if (c.b_fp8) {
-        if (c.nn) return hipErrorInvalidValue;
-        return by_scaled<Op::BF16, false, true>(p, c, cu, st);
+        if (c.nn || (c.fmt & 1)) return hipErrorInvalidValue;
+        return c.fmt ? by_scaled<Op::BF16, false, true, 2>(p, c, cu, st)
+                     : by_scaled<Op::BF16, false, true, 0>(p, c, cu, st);
       }
+      if (c.fmt) return hipErrorInvalidValue;
       return c.nn ? by_scaled<Op::BF16, true, false>(p, c, cu, st)
                   : by_scaled<Op::BF16, false, false>(p, c, cu, st);
     case Op::FP8:
       if (c.nn || c.b_fp8) return hipErrorInvalidValue;
-      return by_scaled<Op::FP8, false, false>(p, c, cu, st);
+      switch (c.fmt) {
+        case 0: return by_scaled<Op::FP8, false, false, 0>(p, c, cu, st);
+        case 1: return by_scaled<Op::FP8, false, false, 1>(p, c, cu, st);
+        case 2: return by_scaled<Op::FP8, false, false, 2>(p, c, cu, st);
+        case 3: return by_scaled<Op::FP8, false, false, 3>(p, c, cu, st);
+      }
+      return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
 }

@@ -13,7 +13,8 @@ enum class SizeClass { Small = 0, Big = 1 };
 struct KernelChoice {
   Op op;
   bool nn;      // rhs [Ga,K,N]
-  bool b_fp8;   // e4m3 rhs widened to bf16 operands
+  bool b_fp8;   // fp8 rhs widened to bf16 operands
+  int fmt;      // fp8 formats: bit 0 lhs, bit 1 rhs (0 e4m3fn, 1 e5m2)
   bool scaled;  // rhs_scale and/or lhs_scale present
   SizeClass size;
 };

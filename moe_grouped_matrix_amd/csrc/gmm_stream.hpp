@@ -28,9 +28,11 @@
 
 namespace gmmk {
 
-template <bool OUT_F32_>
+// FB_: the weight's fp8 format (0 e4m3fn, 1 e5m2).
+template <bool OUT_F32_, int FB_ = 0>
 struct StreamCfg {
   static constexpr bool OUT_F32 = OUT_F32_;
+  static constexpr int FB = FB_;
   static constexpr int BM = 32, BN = 64, BKS = 128;  // tile rows, tile columns, K per stage
   static constexpr int NWAVES = 8, T = 64 * NWAVES;
   static constexpr int W_ROW = BKS, A_ROW = BKS * 2;  // bytes per weight / lhs row in a stage
@@ -146,18 +148,9 @@ __device__ __forceinline__ void stream_stage(const StreamSrc& s, const StreamOff
   __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rb, (lds_ptr_t)(st + C::BI_OFF + w * C::SLOT), 4, bv, 0, 0, 0);
 }
 
-__device__ __forceinline__ i32x4 e4m3x8_to_bf16x8_pk(uint32_t lo, uint32_t hi) {
-  i32x4 r;
-  bf16x2 t;
-  t = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-  r[0] = __builtin_bit_cast(int, t);
-  t = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-  r[1] = __builtin_bit_cast(int, t);
-  t = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-  r[2] = __builtin_bit_cast(int, t);
-  t = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-  r[3] = __builtin_bit_cast(int, t);
-  return r;
+template <int F>
+__device__ __forceinline__ i32x4 fp8x8_to_bf16x8_pk(uint32_t lo, uint32_t hi) {
+  return fp8x8_to_bf16x8<F>(i32x2{(int)lo, (int)hi});
 }
 
 template <class C>
@@ -253,8 +246,8 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
       ring_barrier();
       stream_stage<C>(NEXT ? snxt : scur, off, kd, N, smem + ((stage + C::S - 1) % C::S) * C::STAGE, w);
       // K step jj uses bytes 8 jj .. 8 jj + 7 of the lane's weight run
-      const i32x4 bw[2] = {e4m3x8_to_bf16x8_pk((uint32_t)fw[0], (uint32_t)fw[1]),
-                           e4m3x8_to_bf16x8_pk((uint32_t)fw[2], (uint32_t)fw[3])};
+      const i32x4 bw[2] = {fp8x8_to_bf16x8_pk<C::FB>((uint32_t)fw[0], (uint32_t)fw[1]),
+                           fp8x8_to_bf16x8_pk<C::FB>((uint32_t)fw[2], (uint32_t)fw[3])};
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};

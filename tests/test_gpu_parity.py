@@ -51,8 +51,13 @@ PATHS = [
     (torch.bfloat16, torch.bfloat16, True, 64),
     (torch.bfloat16, torch.float8_e4m3fn, False, 64),
     (torch.float8_e4m3fn, torch.float8_e4m3fn, False, 128),
+    (torch.bfloat16, torch.float8_e5m2, False, 64),
+    (torch.float8_e5m2, torch.float8_e5m2, False, 128),
+    (torch.float8_e4m3fn, torch.float8_e5m2, False, 128),
+    (torch.float8_e5m2, torch.float8_e4m3fn, False, 128),
 ]
-PATH_IDS = ["f32_nt", "f32_nn", "bf16_nt", "bf16_nn", "bf16xe4m3_nt", "e4m3xe4m3_nt"]
+PATH_IDS = ["f32_nt", "f32_nn", "bf16_nt", "bf16_nn", "bf16xe4m3_nt", "e4m3xe4m3_nt",
+            "bf16xe5m2_nt", "e5m2xe5m2_nt", "e4m3xe5m2_nt", "e5m2xe4m3_nt"]
 
 
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
@@ -245,6 +250,25 @@ STREAM_CASES = [
     (48, 640, 136, torch.bfloat16, "bf16", True),
     (600, 1152, 264, torch.float32, "bf16", True),
 ]
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_weight_streaming_kernel_e5m2_weights(out_dtype):
+    """The weight-streaming kernel with e5m2 weights (the decode recipe's
+    weights re-encoded as e5m2, with their block scales and bias): every
+    element against the oracle of the same bytes."""
+    import moe_grouped_matrix_amd as m
+    m.set_tile_policy(0)
+    case = workloads.decode_fp8_weight(tokens=48, experts=24, K=768, N=328, forced_empty=8,
+                                       group_offset=4, num_active=14, device="cuda")
+    case.rhs = case.rhs.float().to(torch.float8_e5m2)
+    case.out_dtype = out_dtype
+    print(f"stream e5m2 M={case.M} active_rows={case.active_rows()} out={out_dtype}", flush=True)
+    out = run_gpu(case)
+    lo, hi = active_range(case)
+    assert_zero_rows(out, lo, hi)
+    compare(out.cpu()[lo:hi], reference(case)[lo:hi], out_dtype, "stream e5m2")
+    assert m.device_flags() == 0
 
 
 def test_weight_streaming_kernel_mostly_inactive_rows():
