@@ -72,6 +72,8 @@ def _load():
         lib.oracle_round_bf16_array.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.oracle_round_e4m3fn.restype = ctypes.c_uint8
         lib.oracle_round_e4m3fn.argtypes = [ctypes.c_double]
+        lib.oracle_widen_scales.restype = ctypes.c_int
+        lib.oracle_widen_scales.argtypes = [vp, ctypes.c_int, i64, vp]
         lib.oracle_quant_fp8.restype = ctypes.c_int
         lib.oracle_quant_fp8.argtypes = [vp, i64, i64, i64, vp, vp]
         lib.oracle_tgmm.restype = ctypes.c_int
@@ -110,6 +112,25 @@ def decode_e5m2(code: int) -> float:
 def round_e4m3fn_code(x: float) -> int:
     """e4m3fn code nearest to x, |x| <= 448, ties to the even mantissa."""
     return _load().oracle_round_e4m3fn(float(x))
+
+
+SCALE_BF16, SCALE_F32, SCALE_E8M0 = 0, 1, 2
+
+
+def widen_scales_reference(src: torch.Tensor, dtype: int) -> torch.Tensor:
+    """widen_block_scale_f32 (metrale gemm_quant.rs page): src [total] as bf16
+    (dtype 0), f32 (1) or E8M0 bytes (2, a uint8 tensor) -> f32 [total]; E8M0
+    e is 2^(e-127), with e = 0 -> 2^-127 and e = 255 -> 0.0 as the page
+    states."""
+    lib = _load()
+    src = _cpu(src).contiguous()
+    want = {SCALE_BF16: torch.bfloat16, SCALE_F32: torch.float32, SCALE_E8M0: torch.uint8}.get(dtype)
+    if want is None or src.dtype != want:
+        raise OracleError("source dtype does not match the dtype code")
+    out = torch.empty(src.numel(), dtype=torch.float32)
+    if lib.oracle_widen_scales(src.data_ptr(), dtype, src.numel(), out.data_ptr()) != OK:
+        raise OracleError("invalid arguments")
+    return out.view(src.shape)
 
 
 def quant_fp8_reference(x: torch.Tensor, blk: int = 128):

@@ -373,3 +373,30 @@ int oracle_quant_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t blk, uint8
   }
   return OR_OK;
 }
+
+/*
+ * Block-scale widening to binary32: widen_block_scale_f32 on the metrale
+ * gemm_quant.rs page, which lets the block-scaled kernels read f32 scales.
+ * The source is bf16 (dtype 0), f32 (1) or E8M0 (2).  An E8M0 byte e is
+ * 2^(e - 127), the binary32 whose bit pattern is e << 23, except as the page
+ * states for its ends: e = 0 is 2^-127 and e = 255 is 0.0.
+ */
+float oracle_widen_scale(const void* src, int dtype, int64_t i) {
+  switch (dtype) {
+    case 0: return (float)oracle_decode_bf16(((const uint16_t*)src)[i]);
+    case 1: return ((const float*)src)[i];
+    case 2: {
+      const int e = ((const uint8_t*)src)[i];
+      if (e == 0) return ldexpf(1.0f, -127);
+      if (e == 255) return 0.0f;
+      return ldexpf(1.0f, e - 127);
+    }
+    default: return NAN;
+  }
+}
+
+int oracle_widen_scales(const void* src, int dtype, int64_t n, float* dst) {
+  if (n < 0 || dtype < 0 || dtype > 2) return OR_E_ARG;
+  for (int64_t i = 0; i < n; ++i) dst[i] = oracle_widen_scale(src, dtype, i);
+  return OR_OK;
+}
