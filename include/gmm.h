@@ -50,7 +50,8 @@ typedef enum {
   GMM_BF16 = 1,      /* bfloat16 */
   GMM_F8E4M3FN = 2,  /* OCP e4m3fn: bias 7, max 448, no infinities */
   GMM_I32 = 3,       /* int32 (group_sizes only) */
-  GMM_F8E5M2 = 4     /* OCP e5m2: bias 15, max 57344, with infinities and NaN */
+  GMM_F8E5M2 = 4,    /* OCP e5m2: bias 15, max 57344, with infinities and NaN */
+  GMM_E8M0 = 5       /* 8-bit power-of-two scale byte (block scales only) */
 } gmm_dtype;
 
 typedef enum {
@@ -193,6 +194,21 @@ gmm_status gmm_quant_fp8_run(gmm_handle* h,
                              const gmm_tensor* q,
                              const gmm_tensor* scale,
                              void* stream);
+
+/*
+ * gmm_widen_scales_run: queue the widening of a block-scale tensor to f32
+ * on `stream`: widen_block_scale_f32 of the metrale gemm_quant.rs page, so
+ * that bf16 or E8M0 block scales can be passed to gmm_run (which reads f32
+ * rhs_scale and lhs_scale).
+ *   src  any shape, BF16 (widened exactly), F32 (copied) or E8M0 (a byte e
+ *        becomes the binary32 with bit pattern e << 23, i.e. 2^(e - 127);
+ *        as the page states, e = 0 becomes 2^-127 and e = 255 becomes 0.0 --
+ *        not the NaN of the OCP encoding).
+ *   dst  F32 with src's number of elements (any shape), written.
+ *   Both on the device, 16-byte aligned, caller-owned and not overlapping;
+ *   otherwise GMM_E_INVALID.  A launch failure returns GMM_E_HIP.
+ */
+gmm_status gmm_widen_scales_run(gmm_handle* h, const gmm_tensor* src, const gmm_tensor* dst, void* stream);
 
 /*
  * gmm_tgmm_run: queue the transposed grouped matmul, the weight gradient of

@@ -16,15 +16,17 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgmm.so")
 
-GMM_F32, GMM_BF16, GMM_F8E4M3FN, GMM_I32, GMM_F8E5M2 = 0, 1, 2, 3, 4
+GMM_F32, GMM_BF16, GMM_F8E4M3FN, GMM_I32, GMM_F8E5M2, GMM_E8M0 = 0, 1, 2, 3, 4, 5
 GMM_OK, GMM_E_INVALID, GMM_E_UNSUPPORTED, GMM_E_HIP, GMM_E_DEVICE_DATA = 0, -1, -2, -3, -4
 FLAG_NEGATIVE_SIZE, FLAG_SIZES_EXCEED_M, FLAG_BAD_OFFSET = 0x1, 0x2, 0x4
 
 EXPORTED = ("gmm_create", "gmm_destroy", "gmm_last_error", "gmm_run", "gmm_run_existing_out", "gmm_tgmm_run",
-            "gmm_quant_fp8_run", "gmm_device_flags", "gmm_set_tile_policy", "gmm_debug_worklist")
+            "gmm_quant_fp8_run", "gmm_widen_scales_run", "gmm_device_flags", "gmm_set_tile_policy",
+            "gmm_debug_worklist")
 
 _DTYPE = {torch.float32: GMM_F32, torch.bfloat16: GMM_BF16,
-          torch.float8_e4m3fn: GMM_F8E4M3FN, torch.float8_e5m2: GMM_F8E5M2, torch.int32: GMM_I32}
+          torch.float8_e4m3fn: GMM_F8E4M3FN, torch.float8_e5m2: GMM_F8E5M2, torch.int32: GMM_I32,
+          torch.float8_e8m0fnu: GMM_E8M0}
 
 
 class GmmError(RuntimeError):
@@ -75,6 +77,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.gmm_run.restype = ctypes.c_int
             lib.gmm_run_existing_out.argtypes = [vp, tp, tp, tp, tp, tp, tp, vp, ctypes.c_int, tp, tp, vp]
             lib.gmm_run_existing_out.restype = ctypes.c_int
+            lib.gmm_widen_scales_run.argtypes = [vp, tp, tp, vp]
+            lib.gmm_widen_scales_run.restype = ctypes.c_int
             lib.gmm_quant_fp8_run.argtypes = [vp, tp, tp, tp, vp]
             lib.gmm_quant_fp8_run.restype = ctypes.c_int
             lib.gmm_tgmm_run.argtypes = [vp, tp, tp, tp, vp, tp, vp]
@@ -198,6 +202,23 @@ def gmm(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,
     if keep is not None and status == GMM_OK:
         keep.record_stream(st)
     _raise(status, h)
+    return out
+
+
+def widen_scales(src: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+                 stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Block scales to float32 through libgmm.so (gmm_widen_scales_run):
+    src bfloat16, float32 or float8_e8m0fnu (an E8M0 byte e becomes
+    2^(e-127); e = 0 gives 2^-127 and e = 255 gives 0.0, as the metrale
+    gemm_quant.rs page states, where torch's own conversion gives NaN)."""
+    lib = load()
+    dev = src.device
+    h = handle(dev)
+    if out is None:
+        out = torch.empty(src.shape, dtype=torch.float32, device=dev)
+    views = [_view(src, "src"), _view(out, "out")]
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    _raise(lib.gmm_widen_scales_run(h, *[_ref(v) for v in views], ctypes.c_void_p(st.cuda_stream)), h)
     return out
 
 

@@ -63,6 +63,7 @@ int elem_size(int dtype) {
     case GMM_BF16: return 2;
     case GMM_F8E4M3FN: return 1;
     case GMM_F8E5M2: return 1;
+    case GMM_E8M0: return 1;
     case GMM_I32: return 4;
     default: return 0;
   }
@@ -310,6 +311,37 @@ gmm_status gmm_run_existing_out(gmm_handle* h, const gmm_tensor* lhs, const gmm_
   if (!existing_out) return fail(h, GMM_E_INVALID, "existing_out is required (gmm_run writes zeros instead)");
   return run_gmm(h, lhs, rhs, group_sizes, rhs_scale, rhs_bias, lhs_scale, group_offset, transpose_rhs,
                  existing_out, out, stream);
+}
+
+gmm_status gmm_widen_scales_run(gmm_handle* h, const gmm_tensor* src, const gmm_tensor* dst, void* stream) {
+  if (!h) return GMM_E_INVALID;
+  h->err.clear();
+  if (!src || !dst) return fail(h, GMM_E_INVALID, "src and dst are required");
+  int32_t dt;
+  switch (src->dtype) {
+    case GMM_BF16: dt = gmmk::kScaleBf16; break;
+    case GMM_F32: dt = gmmk::kScaleF32; break;
+    case GMM_E8M0: dt = gmmk::kScaleE8m0; break;
+    default: return fail(h, GMM_E_INVALID, "src must be bf16, f32 or e8m0");
+  }
+  if (dst->dtype != GMM_F32) return fail(h, GMM_E_INVALID, "dst must be f32");
+  if (src->ndim < 0 || src->ndim > 4 || dst->ndim < 0 || dst->ndim > 4)
+    return fail(h, GMM_E_INVALID, "tensors of rank 0 to 4");
+  const long long n = numel(src);
+  if (n < 0 || numel(dst) != n) return fail(h, GMM_E_INVALID, "dst must hold as many elements as src");
+  if (n > 0 && (!src->data || !dst->data)) return fail(h, GMM_E_INVALID, "null data pointer");
+  if (!aligned16(src->data) || !aligned16(dst->data)) return fail(h, GMM_E_INVALID, "tensor data must be 16-byte aligned");
+  if (overlaps(src, dst)) return fail(h, GMM_E_INVALID, "src and dst must not overlap");
+  if (n == 0) return GMM_OK;
+  gmmk::WidenParams p{};
+  p.src = src->data;
+  p.dst = static_cast<float*>(const_cast<void*>(dst->data));
+  p.n = n;
+  p.dtype = dt;
+  DeviceGuard g(h->device);
+  hipError_t e = gmmk::launch_widen_scales(p, h->cu_count, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(h, GMM_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return GMM_OK;
 }
 
 gmm_status gmm_quant_fp8_run(gmm_handle* h, const gmm_tensor* x, const gmm_tensor* q, const gmm_tensor* scale,

@@ -43,6 +43,19 @@ struct QuantParams {
 // Queue the activation quantiser (gmm_quant.hip).
 hipError_t launch_quant_fp8(const QuantParams& p, int cu_count, hipStream_t stream);
 
+// Block-scale widening arguments: src [n] of kScaleBf16 / kScaleF32 /
+// kScaleE8m0 elements, dst [n] f32.
+enum ScaleDtype : int32_t { kScaleBf16 = 0, kScaleF32 = 1, kScaleE8m0 = 2 };
+struct WidenParams {
+  const void* src;
+  float* dst;
+  long long n;
+  int32_t dtype;
+};
+
+// Queue the block-scale widening (gmm_quant.hip).
+hipError_t launch_widen_scales(const WidenParams& p, int cu_count, hipStream_t stream);
+
 // Queue the worklist export kernel (one workgroup).
 hipError_t launch_worklist(const Params& p, int tm, int32_t* tiles, long long capacity,
                            int32_t* count, hipStream_t stream);

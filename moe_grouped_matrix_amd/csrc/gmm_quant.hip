@@ -108,7 +108,36 @@ __global__ __launch_bounds__(kQuantT) void quant_fp8_kernel(QuantParams p) {
   }
 }
 
+// Block scales widened to binary32 (widen_block_scale_f32 of the metrale
+// gemm_quant.rs page): bf16 exactly, f32 as is, and an E8M0 byte e as the
+// binary32 with bit pattern e << 23 (2^(e - 127)), except 2^-127 for e = 0
+// and 0.0 for e = 255, as the page states.  Scale tensors are small; one
+// element per thread, grid-stride.
+__global__ __launch_bounds__(256) void widen_scales_kernel(WidenParams p) {
+  const long long stride = (long long)gridDim.x * 256;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < p.n; i += stride) {
+    float v;
+    if (p.dtype == kScaleBf16) {
+      v = __uint_as_float((uint32_t) reinterpret_cast<const uint16_t*>(p.src)[i] << 16);
+    } else if (p.dtype == kScaleF32) {
+      v = reinterpret_cast<const float*>(p.src)[i];
+    } else {
+      const uint32_t e = reinterpret_cast<const uint8_t*>(p.src)[i];
+      v = __uint_as_float(e == 0 ? 0x00400000u : (e == 255 ? 0u : e << 23));
+    }
+    p.dst[i] = v;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_widen_scales(const WidenParams& p, int cu_count, hipStream_t stream) {
+  long long grid = (p.n + 255) / 256;
+  if (grid > (long long)cu_count * 8) grid = (long long)cu_count * 8;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(widen_scales_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_fp8(const QuantParams& p, int cu_count, hipStream_t stream) {
   long long grid = (p.blocks + kGroupsPerWg - 1) / kGroupsPerWg;
