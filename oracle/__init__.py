@@ -32,8 +32,9 @@ _SRC = os.path.join(_HERE, "gmm_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F32, BF16, E4M3FN, E5M2 = 0, 1, 2, 3
-_DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: E4M3FN, torch.float8_e5m2: E5M2}
+F32, BF16, E4M3FN, E5M2, I8 = 0, 1, 2, 3, 4
+_DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: E4M3FN, torch.float8_e5m2: E5M2,
+               torch.int8: I8}
 
 OK, E_ARG, E_DATA, E_NOMEM = 0, -1, -4, -5
 

@@ -48,6 +48,7 @@
  *            infinity (m = 0) or NaN (same specification; one of the dtypes
  *            the Megablox gmm accepts, assert_is_supported_dtype on the
  *            tpu-inference wheel diff page).
+ *   int8     two's-complement integer, -128 .. 127 (also on that list).
  */
 #include <math.h>
 #include <stdint.h>
@@ -58,6 +59,7 @@
 #define OR_BF16 1
 #define OR_E4M3FN 2
 #define OR_E5M2 3
+#define OR_I8 4
 
 #define OR_OK 0
 #define OR_E_ARG (-1)
@@ -135,11 +137,12 @@ static double load_elem(const void* base, int dtype, int64_t idx) {
     case OR_BF16: return oracle_decode_bf16(((const uint16_t*)base)[idx]);
     case OR_E4M3FN: return oracle_decode_e4m3fn(((const uint8_t*)base)[idx]);
     case OR_E5M2: return oracle_decode_e5m2(((const uint8_t*)base)[idx]);
+    case OR_I8: return (double)((const int8_t*)base)[idx];
     default: return NAN;
   }
 }
 
-static int dtype_ok(int d) { return d == OR_F32 || d == OR_BF16 || d == OR_E4M3FN || d == OR_E5M2; }
+static int dtype_ok(int d) { return d == OR_F32 || d == OR_BF16 || d == OR_E4M3FN || d == OR_E5M2 || d == OR_I8; }
 
 /*
  * Group offsets o[0..G] (int64, so no overflow) from group_sizes.
