@@ -51,7 +51,8 @@ typedef enum {
   GMM_F8E4M3FN = 2,  /* OCP e4m3fn: bias 7, max 448, no infinities */
   GMM_I32 = 3,       /* int32 (group_sizes only) */
   GMM_F8E5M2 = 4,    /* OCP e5m2: bias 15, max 57344, with infinities and NaN */
-  GMM_E8M0 = 5       /* 8-bit power-of-two scale byte (block scales only) */
+  GMM_E8M0 = 5,      /* 8-bit power-of-two scale byte (block scales only) */
+  GMM_I8 = 6         /* two's-complement int8 */
 } gmm_dtype;
 
 typedef enum {
@@ -96,16 +97,19 @@ const char* gmm_last_error(const gmm_handle* h);
 /*
  * gmm_run: queue out = gmm(lhs, rhs, group_sizes, ...) on `stream`.
  *
- *   lhs          [M,K]; F32, BF16, F8E4M3FN or F8E5M2.
+ *   lhs          [M,K]; F32, BF16, F8E4M3FN, F8E5M2 or I8.
  *   rhs          [Ga,N,K] (transpose_rhs == 0) or [Ga,K,N] (== 1).
  *                Supported (lhs, rhs) pairs: (F32,F32), (BF16,BF16),
  *                (BF16, F8E4M3FN or F8E5M2: the weight is widened exactly
  *                to bf16), (F8E4M3FN or F8E5M2, F8E4M3FN or F8E5M2: fp8 x
  *                fp8 products, either format on either side; e5m2 is one of
  *                the dtypes of the Megablox gmm's whitelist on the
- *                tpu-inference wheel diff page).  fp8 weights need
- *                transpose_rhs == 0.  Infinite or NaN e5m2 codes are outside
- *                the contract.
+ *                tpu-inference wheel diff page), (BF16, I8: the weight is
+ *                widened exactly to bf16), (I8, I8: exact int32 products
+ *                and sums, converted to f32 per scale block, or once when
+ *                there is no scale; K, or K/nb with scales, at most 2^17).
+ *                fp8 and int8 weights need transpose_rhs == 0.  Infinite or
+ *                NaN e5m2 codes are outside the contract.
  *   group_sizes  [G] I32 on the device, 1 <= G <= 1024.
  *   rhs_scale    NULL or F32 [Ga,nb,1,N]; K % nb == 0.
  *   rhs_bias     NULL or [Ga,1,N], F32 or BF16.

@@ -16,7 +16,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgmm.so")
 
-GMM_F32, GMM_BF16, GMM_F8E4M3FN, GMM_I32, GMM_F8E5M2, GMM_E8M0 = 0, 1, 2, 3, 4, 5
+GMM_F32, GMM_BF16, GMM_F8E4M3FN, GMM_I32, GMM_F8E5M2, GMM_E8M0, GMM_I8 = 0, 1, 2, 3, 4, 5, 6
 GMM_OK, GMM_E_INVALID, GMM_E_UNSUPPORTED, GMM_E_HIP, GMM_E_DEVICE_DATA = 0, -1, -2, -3, -4
 FLAG_NEGATIVE_SIZE, FLAG_SIZES_EXCEED_M, FLAG_BAD_OFFSET = 0x1, 0x2, 0x4
 
@@ -26,7 +26,7 @@ EXPORTED = ("gmm_create", "gmm_destroy", "gmm_last_error", "gmm_run", "gmm_run_e
 
 _DTYPE = {torch.float32: GMM_F32, torch.bfloat16: GMM_BF16,
           torch.float8_e4m3fn: GMM_F8E4M3FN, torch.float8_e5m2: GMM_F8E5M2, torch.int32: GMM_I32,
-          torch.float8_e8m0fnu: GMM_E8M0}
+          torch.float8_e8m0fnu: GMM_E8M0, torch.int8: GMM_I8}
 
 
 class GmmError(RuntimeError):

@@ -64,6 +64,7 @@ int elem_size(int dtype) {
     case GMM_F8E4M3FN: return 1;
     case GMM_F8E5M2: return 1;
     case GMM_E8M0: return 1;
+    case GMM_I8: return 1;
     case GMM_I32: return 4;
     default: return 0;
   }
@@ -172,10 +173,12 @@ gmm_status run_gmm(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs, 
     kc.op = gmmk::Op::F32;
   } else if (ld == GMM_BF16 && rd == GMM_BF16) {
     kc.op = gmmk::Op::BF16;
-  } else if (ld == GMM_BF16 && (rd == GMM_F8E4M3FN || rd == GMM_F8E5M2)) {
+  } else if (ld == GMM_BF16 && (rd == GMM_F8E4M3FN || rd == GMM_F8E5M2 || rd == GMM_I8)) {
     kc.op = gmmk::Op::BF16;
     kc.b_fp8 = true;
-    kc.fmt = rd == GMM_F8E5M2 ? 2 : 0;
+    kc.fmt = rd == GMM_F8E5M2 ? 2 : (rd == GMM_I8 ? 4 : 0);
+  } else if (ld == GMM_I8 && rd == GMM_I8) {
+    kc.op = gmmk::Op::I8;
   } else if ((ld == GMM_F8E4M3FN || ld == GMM_F8E5M2) && (rd == GMM_F8E4M3FN || rd == GMM_F8E5M2)) {
     kc.op = gmmk::Op::FP8;
     kc.fmt = (ld == GMM_F8E5M2 ? 1 : 0) | (rd == GMM_F8E5M2 ? 2 : 0);
@@ -186,7 +189,8 @@ gmm_status run_gmm(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs, 
   }
   kc.nn = transpose_rhs != 0;
   if (kc.nn && (kc.b_fp8 || kc.op == gmmk::Op::FP8))
-    return fail(h, GMM_E_UNSUPPORTED, "fp8 weights are read in the [G,N,K] layout only");
+    return fail(h, GMM_E_UNSUPPORTED, "fp8 and int8 weights are read in the [G,N,K] layout only");
+  if (kc.nn && kc.op == gmmk::Op::I8) return fail(h, GMM_E_UNSUPPORTED, "int8 weights are read in the [G,N,K] layout only");
 
   long long nb = 1;
   if (rhs_scale) {
@@ -222,6 +226,8 @@ gmm_status run_gmm(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs, 
   if (K % kt) return fail(h, GMM_E_UNSUPPORTED, "K must be a multiple of " + std::to_string(kt) + " for this dtype");
   if (kc.scaled && blk % kt)
     return fail(h, GMM_E_UNSUPPORTED, "the quantisation block K/nb must be a multiple of " + std::to_string(kt));
+  if (kc.op == gmmk::Op::I8 && (kc.scaled ? blk : K) > gmmk::kMaxInt8Run)
+    return fail(h, GMM_E_UNSUPPORTED, "int8 x int8: at most 2^17 products per int32 sum (K, or K/nb with scales)");
   const long long bsb = elem_size(rd);
   if (K * N * bsb >= 0x7FFFFFF0LL || 256LL * K * elem_size(ld) >= 0x7FFFFFF0LL)
     return fail(h, GMM_E_UNSUPPORTED, "one group's weight (or a 256-row lhs tile) exceeds 2 GiB");

@@ -190,19 +190,27 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long b
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufferRsrcWord3);
 }
 
-// Two fp8 values (bytes 0-1 or 2-3 of w) widened to two bf16: format F = 0
-// e4m3fn, 1 e5m2.  Exact: every finite value of either is a bf16.
+// Two one-byte values (bytes 0-1 or 2-3 of w) widened to two bf16: format
+// F = 0 e4m3fn, 1 e5m2, 2 int8.  Exact: every finite value of each is a
+// bf16 (an int8 has at most 8 significant bits, so the low half of its
+// binary32 is zero).
 template <int F>
 __device__ __forceinline__ bf16x2 fp8x2_to_bf16x2(unsigned w, bool hi) {
-  if constexpr (F == 0)
+  if constexpr (F == 0) {
     return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
               : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-  else
+  } else if constexpr (F == 1) {
     return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, true)
               : __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, false);
+  } else {
+    const unsigned h = hi ? w >> 16 : w;
+    const float f0 = (float)(int)(int8_t)(h & 0xFF), f1 = (float)(int)(int8_t)((h >> 8) & 0xFF);
+    const unsigned bits = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+    return __builtin_bit_cast(bf16x2, bits);
+  }
 }
 
-// 8 fp8 bytes of format F widened to 8 bf16.
+// 8 one-byte values of format F widened to 8 bf16.
 template <int F>
 __device__ inline i32x4 fp8x8_to_bf16x8(i32x2 v) {
   i32x4 r;
@@ -229,15 +237,16 @@ __device__ inline int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 
 // ---------------------------------------------------------------------------
 // tile configurations
 
-// FMT_: the fp8 formats, bit 0 for lhs and bit 1 for rhs (0 e4m3fn, 1 e5m2;
-// the format codes of the f8f6f4 matrix instructions).
+// FMT_: the one-byte formats, FMT_ & 1 for lhs (0 e4m3fn, 1 e5m2: the
+// format codes of the f8f6f4 matrix instructions) and FMT_ >> 1 for rhs
+// (the same, or 2 for int8 weights widened to bf16).
 template <Op OP, bool NN_, bool BFP8_, int BM_, int BN_, int WM_, int WN_, bool SCALED_, int FMT_ = 0>
 struct Cfg {
   static constexpr Op op = OP;
   static constexpr bool NN = NN_;        // rhs is [Ga,K,N]
   static constexpr bool B_FP8 = BFP8_;   // fp8 rhs widened to bf16 operands
   static constexpr bool SCALED = SCALED_;
-  static constexpr int FA = FMT_ & 1, FB = (FMT_ >> 1) & 1;
+  static constexpr int FA = FMT_ & 1, FB = FMT_ >> 1;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int T = 64 * WM * WN;
   static constexpr int ES = OP == Op::F32 ? 4 : (OP == Op::BF16 ? 2 : 1);  // operand bytes
@@ -259,6 +268,8 @@ struct Cfg {
   static_assert(!B_FP8 || OP == Op::BF16, "fp8 weights widen to bf16");
   static_assert(OP == Op::FP8 || FA == 0, "an lhs format only for fp8 x fp8");
   static_assert(OP == Op::FP8 || B_FP8 || FB == 0, "an rhs format only for fp8 weights");
+  static_assert(OP != Op::FP8 || FB <= 1, "fp8 x fp8 formats are e4m3fn or e5m2");
+  static_assert(!NN || OP != Op::I8, "NN needs f32 or bf16 weights");
 };
 
 // ---------------------------------------------------------------------------
@@ -367,13 +378,41 @@ __device__ inline void store_tile(const C&, const Stage<C>& st, char* sa, char* 
   }
 }
 
+// The value of one accumulator element: int8 x int8 tiles accumulate exact
+// int32 sums in the same registers (their bits), the others binary32.
+template <class C>
+__device__ __forceinline__ float acc_value(float a) {
+  if constexpr (C::op == Op::I8)
+    return (float)__float_as_int(a);
+  else
+    return a;
+}
+
 // acc[fm][fn] += A(wave rows fm) * B(wave cols fn) over one 128-byte K row.
 template <class C>
 __device__ inline void mma_tile(f32x4 (&acc)[C::FM][C::FN], const char* sa, const char* sb) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w / C::WN, wn = w % C::WN;
   const int q = lane >> 4, r16 = lane & 15;
-  if constexpr (C::op == Op::FP8) {
+  if constexpr (C::op == Op::I8) {
+    // two 16x16x64 int8 products per 128-byte row: lane quarter q takes K
+    // bytes 16q .. 16q+15, then 64 + 16q .. (the same K order in A and B)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      i32x4 bfr[C::FN];
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+        bfr[fn] = *reinterpret_cast<const i32x4*>(sb + lds_off(wn * C::TN + fn * 16 + r16, q + 4 * kk));
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm) {
+        const i32x4 af = *reinterpret_cast<const i32x4*>(sa + lds_off(wm * C::TM + fm * 16 + r16, q + 4 * kk));
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+          acc[fm][fn] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bfr[fn], __builtin_bit_cast(i32x4, acc[fm][fn]), 0, 0, 0));
+      }
+    }
+  } else if constexpr (C::op == Op::FP8) {
     i32x8 bf[C::FN];
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
@@ -557,7 +596,7 @@ __global__ __launch_bounds__(C::T) void gmm_kernel(Params p) {
 #pragma unroll
             for (int fn = 0; fn < C::FN; ++fn) {
 #pragma unroll
-              for (int i = 0; i < 4; ++i) tot[fm][fn][i] += acc[fm][fn][i] * (rs[fn] * ls[fm][i]);
+              for (int i = 0; i < 4; ++i) tot[fm][fn][i] += acc_value<C>(acc[fm][fn][i]) * (rs[fn] * ls[fm][i]);
               acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
@@ -590,7 +629,7 @@ __global__ __launch_bounds__(C::T) void gmm_kernel(Params p) {
             if constexpr (C::SCALED)
               v = tot[fm][fn][i];
             else
-              v = acc[fm][fn][i];
+              v = acc_value<C>(acc[fm][fn][i]);
             v += bias;
             const long long oi = (long long)(row0 + rl) * N + col;
             if (p.out_f32)

@@ -140,8 +140,12 @@ hipError_t launch_gmm(const Params& p, const KernelChoice& c, int cu, hipStream_
     case Op::BF16:
       if (c.b_fp8) {
         if (c.nn || (c.fmt & 1)) return hipErrorInvalidValue;
-        return c.fmt ? by_scaled<Op::BF16, false, true, 2>(p, c, cu, st)
-                     : by_scaled<Op::BF16, false, true, 0>(p, c, cu, st);
+        switch (c.fmt) {
+          case 0: return by_scaled<Op::BF16, false, true, 0>(p, c, cu, st);
+          case 2: return by_scaled<Op::BF16, false, true, 2>(p, c, cu, st);
+          case 4: return by_scaled<Op::BF16, false, true, 4>(p, c, cu, st);
+        }
+        return hipErrorInvalidValue;
       }
       if (c.fmt) return hipErrorInvalidValue;
       return c.nn ? by_scaled<Op::BF16, true, false>(p, c, cu, st)
@@ -155,6 +159,9 @@ hipError_t launch_gmm(const Params& p, const KernelChoice& c, int cu, hipStream_
         case 3: return by_scaled<Op::FP8, false, false, 3>(p, c, cu, st);
       }
       return hipErrorInvalidValue;
+    case Op::I8:
+      if (c.nn || c.b_fp8 || c.fmt) return hipErrorInvalidValue;
+      return by_scaled<Op::I8, false, false, 0>(p, c, cu, st);
   }
   return hipErrorInvalidValue;
 }

@@ -14,13 +14,17 @@ struct KernelChoice {
   Op op;
   bool nn;      // rhs [Ga,K,N]
   bool b_fp8;   // fp8 rhs widened to bf16 operands
-  int fmt;      // fp8 formats: bit 0 lhs, bit 1 rhs (0 e4m3fn, 1 e5m2)
+  int fmt;      // one-byte formats: fmt & 1 lhs (0 e4m3fn, 1 e5m2), fmt >> 1 rhs (2: int8 weights)
   bool scaled;  // rhs_scale and/or lhs_scale present
   SizeClass size;
 };
 
 // K elements of one K tile for an operand type (the K granularity).
 inline int k_tile(Op op) { return op == Op::F32 ? 32 : (op == Op::BF16 ? 64 : 128); }
+
+// int8 x int8 sums are exact int32 as long as a run of int32 accumulation
+// (K, or the scale block) has at most 2^17 products of at most 2^14.
+constexpr long long kMaxInt8Run = 1LL << 17;
 
 // m-tile height the kernel uses for this choice.
 int tile_m(const KernelChoice& c);

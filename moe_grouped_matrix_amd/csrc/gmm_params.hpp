@@ -7,7 +7,7 @@
 namespace gmmk {
 
 // Operand type fed to the matrix cores.
-enum class Op { F32, BF16, FP8 };
+enum class Op { F32, BF16, FP8, I8 };
 
 constexpr int kMaxGroups = 1024;
 constexpr int kQueues = 8;  // one per XCD

@@ -55,9 +55,11 @@ PATHS = [
     (torch.float8_e5m2, torch.float8_e5m2, False, 128),
     (torch.float8_e4m3fn, torch.float8_e5m2, False, 128),
     (torch.float8_e5m2, torch.float8_e4m3fn, False, 128),
+    (torch.bfloat16, torch.int8, False, 64),
+    (torch.int8, torch.int8, False, 128),
 ]
 PATH_IDS = ["f32_nt", "f32_nn", "bf16_nt", "bf16_nn", "bf16xe4m3_nt", "e4m3xe4m3_nt",
-            "bf16xe5m2_nt", "e5m2xe5m2_nt", "e4m3xe5m2_nt", "e5m2xe4m3_nt"]
+            "bf16xe5m2_nt", "e5m2xe5m2_nt", "e4m3xe5m2_nt", "e5m2xe4m3_nt", "bf16xi8_nt", "i8xi8_nt"]
 
 
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
@@ -252,22 +254,27 @@ STREAM_CASES = [
 ]
 
 
-@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
-def test_weight_streaming_kernel_e5m2_weights(out_dtype):
-    """The weight-streaming kernel with e5m2 weights (the decode recipe's
-    weights re-encoded as e5m2, with their block scales and bias): every
-    element against the oracle of the same bytes."""
+@pytest.mark.parametrize("wdtype,out_dtype", [(torch.float8_e5m2, torch.bfloat16),
+                                              (torch.float8_e5m2, torch.float32),
+                                              (torch.int8, torch.bfloat16)],
+                         ids=["e5m2_bf16out", "e5m2_f32out", "int8_bf16out"])
+def test_weight_streaming_kernel_other_weight_formats(wdtype, out_dtype):
+    """The weight-streaming kernel with e5m2 or int8 weights (the decode
+    recipe's weights re-encoded -- int8 rounded and clamped to +-127 --
+    with their block scales and bias): every element against the oracle of
+    the same bytes."""
     import moe_grouped_matrix_amd as m
     m.set_tile_policy(0)
     case = workloads.decode_fp8_weight(tokens=48, experts=24, K=768, N=328, forced_empty=8,
                                        group_offset=4, num_active=14, device="cuda")
-    case.rhs = case.rhs.float().to(torch.float8_e5m2)
+    w = case.rhs.float()
+    case.rhs = w.round().clamp(-127, 127).to(torch.int8) if wdtype == torch.int8 else w.to(wdtype)
     case.out_dtype = out_dtype
-    print(f"stream e5m2 M={case.M} active_rows={case.active_rows()} out={out_dtype}", flush=True)
+    print(f"stream {wdtype} M={case.M} active_rows={case.active_rows()} out={out_dtype}", flush=True)
     out = run_gpu(case)
     lo, hi = active_range(case)
     assert_zero_rows(out, lo, hi)
-    compare(out.cpu()[lo:hi], reference(case)[lo:hi], out_dtype, "stream e5m2")
+    compare(out.cpu()[lo:hi], reference(case)[lo:hi], out_dtype, f"stream {wdtype}")
     assert m.device_flags() == 0
 
 
