@@ -32,7 +32,9 @@ _SRC = os.path.join(_HERE, "gmm_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F32, BF16, E4M3FN, E5M2, I8 = 0, 1, 2, 3, 4
+F32, BF16, E4M3FN, E5M2, I8, I4, U4, F4E2M1 = 0, 1, 2, 3, 4, 5, 6, 7
+# four-bit operands: packed bytes (uint8, or float4_e2m1fn_x2) named by format
+PACKED_FORMATS = {"int4": I4, "uint4": U4, "fp4_e2m1": F4E2M1}
 _DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: E4M3FN, torch.float8_e5m2: E5M2,
                torch.int8: I8}
 
@@ -66,6 +68,8 @@ def _load():
         lib.oracle_decode_e4m3fn.argtypes = [ctypes.c_uint8]
         lib.oracle_decode_e5m2.restype = ctypes.c_double
         lib.oracle_decode_e5m2.argtypes = [ctypes.c_uint8]
+        lib.oracle_decode_e2m1.restype = ctypes.c_double
+        lib.oracle_decode_e2m1.argtypes = [ctypes.c_uint8]
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.oracle_round_bf16.restype = ctypes.c_uint16
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
@@ -108,6 +112,10 @@ def decode_e4m3fn(code: int) -> float:
 
 def decode_e5m2(code: int) -> float:
     return _load().oracle_decode_e5m2(code & 0xFF)
+
+
+def decode_e2m1(nibble: int) -> float:
+    return _load().oracle_decode_e2m1(nibble & 0xF)
 
 
 def round_e4m3fn_code(x: float) -> int:
@@ -173,6 +181,7 @@ def gmm_reference(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tenso
                   rhs_bias: Optional[torch.Tensor] = None,
                   lhs_scale: Optional[torch.Tensor] = None,
                   existing_out: Optional[torch.Tensor] = None,
+                  rhs_format: Optional[str] = None,
                   rows: Optional[Sequence[int]] = None,
                   return_row_group: bool = False):
     """Reference rows of gmm(lhs, rhs, group_sizes, ...) in float64.
@@ -180,6 +189,9 @@ def gmm_reference(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tenso
     lhs [M,K]; rhs [Ga,N,K] (transpose_rhs False) or [Ga,K,N] (True);
     group_sizes [G] int32; rhs_scale f32 [Ga,nb,1,N]; rhs_bias [Ga,1,N];
     lhs_scale f32 [M,nb].  ``rows`` selects output rows (all when None).
+    rhs_format "int4", "uint4" or "fp4_e2m1": rhs holds packed bytes (uint8
+    or float4_e2m1fn_x2) [Ga,N,K/2], two elements to a byte, even elements
+    in the low nibble (only the [Ga,N,K] layout).
     Returns a float64 numpy array [len(rows), N] (and the group of each row,
     -1 for none, when return_row_group).
 
@@ -197,6 +209,12 @@ def gmm_reference(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tenso
     Ga = rhs.shape[0]
     N = rhs.shape[2] if transpose_rhs else rhs.shape[1]
     Kr = rhs.shape[1] if transpose_rhs else rhs.shape[2]
+    rhs_code = None
+    if rhs_format is not None:
+        if rhs_format not in PACKED_FORMATS or transpose_rhs or rhs.element_size() != 1:
+            raise OracleError("packed four-bit rhs: a known format, bytes, [Ga,N,K/2]")
+        rhs_code = PACKED_FORMATS[rhs_format]
+        Kr = 2 * rhs.shape[2]
     if Kr != K:
         raise OracleError("lhs / rhs contraction sizes differ")
     nb = 1
@@ -228,7 +246,7 @@ def gmm_reference(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tenso
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     rc = lib.oracle_gmm(
         ptr(lhs), _code(lhs, "lhs"), M, K,
-        ptr(rhs), _code(rhs, "rhs"), Ga, N, int(bool(transpose_rhs)),
+        ptr(rhs), _code(rhs, "rhs") if rhs_code is None else rhs_code, Ga, N, int(bool(transpose_rhs)),
         ptr(gs), gs.shape[0], int(group_offset),
         ptr(rhs_scale), ptr(rhs_bias), _code(rhs_bias, "rhs_bias") if rhs_bias is not None else 0,
         ptr(lhs_scale), nb,

@@ -49,6 +49,13 @@
  *            the Megablox gmm accepts, assert_is_supported_dtype on the
  *            tpu-inference wheel diff page).
  *   int8     two's-complement integer, -128 .. 127 (also on that list).
+ *   int4, uint4, fp4 e2m1 (also on that list): four bits, two to a byte,
+ *            element i in the low nibble of byte i/2 when i is even and in
+ *            the high nibble when odd.  int4 is two's complement (-8 .. 7),
+ *            uint4 0 .. 15; e2m1 has 1 sign, 2 exponent (bias 1) and 1
+ *            mantissa bit: exponent field 0 encodes m/2, else
+ *            (1 + m/2) * 2^(e-1), so the magnitudes are 0, 0.5, 1, 1.5, 2,
+ *            3, 4 and 6 (OCP microscaling formats specification).
  */
 #include <math.h>
 #include <stdint.h>
@@ -60,6 +67,9 @@
 #define OR_E4M3FN 2
 #define OR_E5M2 3
 #define OR_I8 4
+#define OR_I4 5
+#define OR_U4 6
+#define OR_F4E2M1 7
 
 #define OR_OK 0
 #define OR_E_ARG (-1)
@@ -131,6 +141,17 @@ void oracle_round_bf16_array(const double* x, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_round_bf16(x[i]);
 }
 
+double oracle_decode_e2m1(uint8_t nibble) {
+  const int sign = (nibble >> 3) & 1, e = (nibble >> 1) & 3, m = nibble & 1;
+  const double v = e == 0 ? m * 0.5 : (1.0 + m * 0.5) * ldexp(1.0, e - 1);
+  return sign ? -v : v;
+}
+
+static int nibble_at(const void* base, int64_t idx) {
+  const uint8_t b = ((const uint8_t*)base)[idx >> 1];
+  return (idx & 1) ? b >> 4 : b & 0xF;
+}
+
 static double load_elem(const void* base, int dtype, int64_t idx) {
   switch (dtype) {
     case OR_F32: return (double)((const float*)base)[idx];
@@ -138,11 +159,17 @@ static double load_elem(const void* base, int dtype, int64_t idx) {
     case OR_E4M3FN: return oracle_decode_e4m3fn(((const uint8_t*)base)[idx]);
     case OR_E5M2: return oracle_decode_e5m2(((const uint8_t*)base)[idx]);
     case OR_I8: return (double)((const int8_t*)base)[idx];
+    case OR_I4: {
+      const int n = nibble_at(base, idx);
+      return (double)(n >= 8 ? n - 16 : n);
+    }
+    case OR_U4: return (double)nibble_at(base, idx);
+    case OR_F4E2M1: return oracle_decode_e2m1((uint8_t)nibble_at(base, idx));
     default: return NAN;
   }
 }
 
-static int dtype_ok(int d) { return d == OR_F32 || d == OR_BF16 || d == OR_E4M3FN || d == OR_E5M2 || d == OR_I8; }
+static int dtype_ok(int d) { return d >= OR_F32 && d <= OR_F4E2M1; }
 
 /*
  * Group offsets o[0..G] (int64, so no overflow) from group_sizes.
