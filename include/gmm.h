@@ -52,7 +52,11 @@ typedef enum {
   GMM_I32 = 3,       /* int32 (group_sizes only) */
   GMM_F8E5M2 = 4,    /* OCP e5m2: bias 15, max 57344, with infinities and NaN */
   GMM_E8M0 = 5,      /* 8-bit power-of-two scale byte (block scales only) */
-  GMM_I8 = 6         /* two's-complement int8 */
+  GMM_I8 = 6,        /* two's-complement int8 */
+  GMM_I4 = 7,        /* two's-complement int4, two to a byte (element i in the low
+                        nibble of byte i/2 when i is even, the high nibble when odd) */
+  GMM_U4 = 8,        /* unsigned int4, packed as GMM_I4 */
+  GMM_F4E2M1 = 9     /* OCP fp4 e2m1 (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6), packed as GMM_I4 */
 } gmm_dtype;
 
 typedef enum {
@@ -108,8 +112,11 @@ const char* gmm_last_error(const gmm_handle* h);
  *                widened exactly to bf16), (I8, I8: exact int32 products
  *                and sums, converted to f32 per scale block, or once when
  *                there is no scale; K, or K/nb with scales, at most 2^17).
- *                fp8 and int8 weights need transpose_rhs == 0.  Infinite or
- *                NaN e5m2 codes are outside the contract.
+ *                (BF16, I4 / U4 / F4E2M1: four-bit weights, two to a byte,
+ *                widened exactly to bf16; the tensor's shape counts
+ *                elements, [Ga,N,K], and its data holds Ga*N*K/2 bytes).
+ *                fp8, int8 and four-bit weights need transpose_rhs == 0.
+ *                Infinite or NaN e5m2 codes are outside the contract.
  *   group_sizes  [G] I32 on the device, 1 <= G <= 1024.
  *   rhs_scale    NULL or F32 [Ga,nb,1,N]; K % nb == 0.
  *   rhs_bias     NULL or [Ga,1,N], F32 or BF16.

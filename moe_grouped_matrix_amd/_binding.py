@@ -17,6 +17,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgmm.so")
 
 GMM_F32, GMM_BF16, GMM_F8E4M3FN, GMM_I32, GMM_F8E5M2, GMM_E8M0, GMM_I8 = 0, 1, 2, 3, 4, 5, 6
+GMM_I4, GMM_U4, GMM_F4E2M1 = 7, 8, 9
+# four-bit weights: packed bytes (uint8, or float4_e2m1fn_x2) named by format
+PACKED_FORMATS = {"int4": GMM_I4, "uint4": GMM_U4, "fp4_e2m1": GMM_F4E2M1}
 GMM_OK, GMM_E_INVALID, GMM_E_UNSUPPORTED, GMM_E_HIP, GMM_E_DEVICE_DATA = 0, -1, -2, -3, -4
 FLAG_NEGATIVE_SIZE, FLAG_SIZES_EXCEED_M, FLAG_BAD_OFFSET = 0x1, 0x2, 0x4
 
@@ -141,6 +144,25 @@ def _view(t: Optional[torch.Tensor], name: str):
     return v
 
 
+def _view_packed(t: torch.Tensor, fmt: str, name: str):
+    """A four-bit tensor: bytes [..., K/2] (uint8 or float4_e2m1fn_x2) seen
+    by the C ABI as [..., K] elements of the named format."""
+    if fmt not in PACKED_FORMATS:
+        raise GmmInvalid(GMM_E_INVALID, f"{name}: unknown four-bit format {fmt!r}")
+    if t.dtype not in (torch.uint8, torch.float4_e2m1fn_x2):
+        raise GmmInvalid(GMM_E_INVALID, f"{name}: four-bit data comes as uint8 or float4_e2m1fn_x2 bytes")
+    if not t.is_cuda or not t.is_contiguous() or t.dim() < 1 or t.dim() > 4:
+        raise GmmInvalid(GMM_E_INVALID, f"{name} must be a contiguous device tensor of rank 1 to 4")
+    v = GmmTensor()
+    v.data = t.data_ptr() if t.numel() else None
+    v.dtype = PACKED_FORMATS[fmt]
+    v.ndim = t.dim()
+    for i, s in enumerate(t.shape):
+        v.shape[i] = s
+    v.shape[t.dim() - 1] = 2 * t.shape[-1]
+    return v
+
+
 def _ref(v):
     return ctypes.byref(v) if v is not None else None
 
@@ -168,6 +190,7 @@ def gmm(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,
         group_offset=None,
         transpose_rhs: bool = False,
         existing_out: Optional[torch.Tensor] = None,
+        rhs_format: Optional[str] = None,
         out: Optional[torch.Tensor] = None,
         stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
     """Grouped matmul on the GPU through libgmm.so.
@@ -179,7 +202,9 @@ def gmm(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,
     float32 default follows the Megablox gmm).  With existing_out [M,N] the
     rows outside the active groups are its rows instead of zeros
     (gmm_run_existing_out); without out the result is written into
-    existing_out itself."""
+    existing_out itself.  rhs_format "int4", "uint4" or "fp4_e2m1" takes rhs
+    as packed bytes [Ga,N,K/2] (uint8 or float4_e2m1fn_x2), two weights to a
+    byte, even elements in the low nibble, with a bf16 lhs."""
     lib = load()
     dev = lhs.device
     h = handle(dev)
@@ -187,9 +212,10 @@ def gmm(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,
     N = rhs.shape[2] if transpose_rhs else (rhs.shape[1] if rhs.dim() == 3 else 0)
     if out is None:
         out = existing_out if existing_out is not None else torch.empty((M, N), dtype=out_dtype, device=dev)
-    views = [_view(t, n) for t, n in ((lhs, "lhs"), (rhs, "rhs"), (group_sizes, "group_sizes"),
-                                      (rhs_scale, "rhs_scale"), (rhs_bias, "rhs_bias"),
-                                      (lhs_scale, "lhs_scale"), (out, "out"))]
+    views = [_view(t, n) if (n != "rhs" or rhs_format is None) else _view_packed(t, rhs_format, n)
+             for t, n in ((lhs, "lhs"), (rhs, "rhs"), (group_sizes, "group_sizes"),
+                          (rhs_scale, "rhs_scale"), (rhs_bias, "rhs_bias"),
+                          (lhs_scale, "lhs_scale"), (out, "out"))]
     off_ptr, keep = _offset_ptr(group_offset, dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev)
     if existing_out is None:

@@ -76,12 +76,19 @@ long long numel(const gmm_tensor* t) {
   return n;
 }
 
+bool four_bit(int dtype) { return dtype == GMM_I4 || dtype == GMM_U4 || dtype == GMM_F4E2M1; }
+
+// bytes of a tensor's data (four-bit types: two elements to a byte)
+long long tensor_bytes(const gmm_tensor* t) {
+  return four_bit(t->dtype) ? (numel(t) + 1) / 2 : numel(t) * elem_size(t->dtype);
+}
+
 bool overlaps(const gmm_tensor* a, const gmm_tensor* b) {
   if (!a || !b || !a->data || !b->data) return false;
   const char* a0 = static_cast<const char*>(a->data);
   const char* b0 = static_cast<const char*>(b->data);
-  const char* a1 = a0 + numel(a) * elem_size(a->dtype);
-  const char* b1 = b0 + numel(b) * elem_size(b->dtype);
+  const char* a1 = a0 + tensor_bytes(a);
+  const char* b1 = b0 + tensor_bytes(b);
   return a0 < b1 && b0 < a1;
 }
 
@@ -177,19 +184,24 @@ gmm_status run_gmm(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs, 
     kc.op = gmmk::Op::BF16;
     kc.b_fp8 = true;
     kc.fmt = rd == GMM_F8E5M2 ? 2 : (rd == GMM_I8 ? 4 : 0);
+  } else if (ld == GMM_BF16 && four_bit(rd)) {
+    kc.op = gmmk::Op::BF16;
+    kc.b_fp8 = true;
+    kc.fmt = rd == GMM_I4 ? 6 : (rd == GMM_U4 ? 8 : 10);
   } else if (ld == GMM_I8 && rd == GMM_I8) {
     kc.op = gmmk::Op::I8;
   } else if ((ld == GMM_F8E4M3FN || ld == GMM_F8E5M2) && (rd == GMM_F8E4M3FN || rd == GMM_F8E5M2)) {
     kc.op = gmmk::Op::FP8;
     kc.fmt = (ld == GMM_F8E5M2 ? 1 : 0) | (rd == GMM_F8E5M2 ? 2 : 0);
   } else {
-    if (elem_size(ld) == 0 || elem_size(rd) == 0 || ld == GMM_I32 || rd == GMM_I32)
+    const bool known_l = elem_size(ld) > 0 || four_bit(ld), known_r = elem_size(rd) > 0 || four_bit(rd);
+    if (!known_l || !known_r || ld == GMM_I32 || rd == GMM_I32 || ld == GMM_E8M0 || rd == GMM_E8M0)
       return fail(h, GMM_E_INVALID, "unsupported lhs / rhs dtype");
     return fail(h, GMM_E_UNSUPPORTED, "unsupported (lhs, rhs) dtype pair");
   }
   kc.nn = transpose_rhs != 0;
   if (kc.nn && (kc.b_fp8 || kc.op == gmmk::Op::FP8))
-    return fail(h, GMM_E_UNSUPPORTED, "fp8 and int8 weights are read in the [G,N,K] layout only");
+    return fail(h, GMM_E_UNSUPPORTED, "fp8, int8 and four-bit weights are read in the [G,N,K] layout only");
   if (kc.nn && kc.op == gmmk::Op::I8) return fail(h, GMM_E_UNSUPPORTED, "int8 weights are read in the [G,N,K] layout only");
 
   long long nb = 1;
@@ -228,8 +240,8 @@ gmm_status run_gmm(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs, 
     return fail(h, GMM_E_UNSUPPORTED, "the quantisation block K/nb must be a multiple of " + std::to_string(kt));
   if (kc.op == gmmk::Op::I8 && (kc.scaled ? blk : K) > gmmk::kMaxInt8Run)
     return fail(h, GMM_E_UNSUPPORTED, "int8 x int8: at most 2^17 products per int32 sum (K, or K/nb with scales)");
-  const long long bsb = elem_size(rd);
-  if (K * N * bsb >= 0x7FFFFFF0LL || 256LL * K * elem_size(ld) >= 0x7FFFFFF0LL)
+  const long long wbytes = four_bit(rd) ? K * N / 2 : K * N * elem_size(rd);
+  if (wbytes >= 0x7FFFFFF0LL || 256LL * K * elem_size(ld) >= 0x7FFFFFF0LL)
     return fail(h, GMM_E_UNSUPPORTED, "one group's weight (or a 256-row lhs tile) exceeds 2 GiB");
 
   const gmm_tensor* ins[] = {lhs, rhs, group_sizes, rhs_scale, rhs_bias, lhs_scale};

@@ -210,6 +210,31 @@ __device__ __forceinline__ bf16x2 fp8x2_to_bf16x2(unsigned w, bool hi) {
   }
 }
 
+// 8 four-bit values (the nibbles of w, the low nibble of each byte first)
+// of format F = 3 int4, 4 uint4, 5 fp4 e2m1 widened to 8 bf16 (exact: each
+// value has at most 3 significant bits).
+template <int F>
+__device__ inline i32x4 nib8_to_bf16x8(unsigned w) {
+  i32x4 r;
+  if constexpr (F == 5) {
+    r[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0));
+    r[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1));
+    r[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2));
+    r[3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int lo = (w >> (8 * j)) & 15, hi = (w >> (8 * j + 4)) & 15;
+      if constexpr (F == 3) {
+        lo = (lo ^ 8) - 8;
+        hi = (hi ^ 8) - 8;
+      }
+      r[j] = (int)((__float_as_uint((float)lo) >> 16) | (__float_as_uint((float)hi) & 0xFFFF0000u));
+    }
+  }
+  return r;
+}
+
 // 8 one-byte values of format F widened to 8 bf16.
 template <int F>
 __device__ inline i32x4 fp8x8_to_bf16x8(i32x2 v) {
@@ -237,9 +262,10 @@ __device__ inline int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 
 // ---------------------------------------------------------------------------
 // tile configurations
 
-// FMT_: the one-byte formats, FMT_ & 1 for lhs (0 e4m3fn, 1 e5m2: the
+// FMT_: the narrow formats, FMT_ & 1 for lhs (0 e4m3fn, 1 e5m2: the
 // format codes of the f8f6f4 matrix instructions) and FMT_ >> 1 for rhs
-// (the same, or 2 for int8 weights widened to bf16).
+// (the same, or for weights widened to bf16 2 int8, 3 int4, 4 uint4, 5 fp4
+// e2m1 -- the last three packed two to a byte).
 template <Op OP, bool NN_, bool BFP8_, int BM_, int BN_, int WM_, int WN_, bool SCALED_, int FMT_ = 0>
 struct Cfg {
   static constexpr Op op = OP;
@@ -259,7 +285,10 @@ struct Cfg {
   static constexpr int NW = BN * 8 / T;     // NN: n-columns per thread block
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   static constexpr int LDS = 2 * (A_BYTES + B_BYTES);
-  static constexpr int BSB = B_FP8 ? 1 : ES;  // rhs storage bytes per element
+  static constexpr int BSB = B_FP8 ? 1 : ES;  // rhs storage bytes per element (four-bit: half)
+  static constexpr bool B_NIB = B_FP8 && FB >= 3;  // four-bit weights, two to a byte
+  // bytes of `elems` consecutive rhs elements (an even count when four-bit)
+  __device__ static constexpr long long rhs_bytes(long long elems) { return B_NIB ? elems / 2 : elems * BSB; }
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
   static_assert(A_CH >= 1 && A_CH * T == BM * 8, "A tile must split evenly");
   static_assert(B_CH >= 1 && B_CH * T == BN * 8, "B tile must split evenly");
@@ -299,7 +328,10 @@ __device__ inline void load_tile(const C&, Stage<C>& st, __amdgpu_buffer_rsrc_t 
     for (int i = 0; i < C::B_CH; ++i) {
       const int c = tid + i * C::T;
       const int r = c >> 3, cc = c & 7;
-      if constexpr (C::B_FP8) {
+      if constexpr (C::B_NIB) {
+        st.b[i][0] = __builtin_amdgcn_raw_buffer_load_b32(br, r * (K / 2) + kt * 32 + cc * 4, 0, 0);
+        st.b[i][1] = 0;
+      } else if constexpr (C::B_FP8) {
         i32x2 v = __builtin_amdgcn_raw_buffer_load_b64(br, r * K + kt * 64 + cc * 8, 0, 0);
         st.b[i][0] = v[0];
         st.b[i][1] = v[1];
@@ -348,7 +380,10 @@ __device__ inline void store_tile(const C&, const Stage<C>& st, char* sa, char* 
     for (int i = 0; i < C::B_CH; ++i) {
       const int c = tid + i * C::T;
       i32x4 v = st.b[i];
-      if constexpr (C::B_FP8) v = fp8x8_to_bf16x8<C::FB>(i32x2{st.b[i][0], st.b[i][1]});
+      if constexpr (C::B_NIB)
+        v = nib8_to_bf16x8<C::FB>((unsigned)st.b[i][0]);
+      else if constexpr (C::B_FP8)
+        v = fp8x8_to_bf16x8<C::FB>(i32x2{st.b[i][0], st.b[i][1]});
       *reinterpret_cast<i32x4*>(sb + lds_off(c >> 3, c & 7)) = v;
     }
   } else {
@@ -537,12 +572,12 @@ __global__ __launch_bounds__(C::T) void gmm_kernel(Params p) {
 
     const char* lhs = reinterpret_cast<const char*>(p.lhs) + (long long)row0 * K * C::ES;
     const __amdgpu_buffer_rsrc_t ar = make_rsrc(lhs, (long long)rows * K * C::ES);
-    const char* rhs_h = reinterpret_cast<const char*>(p.rhs) + (long long)h * N * K * C::BSB;
+    const char* rhs_h = reinterpret_cast<const char*>(p.rhs) + C::rhs_bytes((long long)h * N * K);
     __amdgpu_buffer_rsrc_t br;
     if constexpr (C::NN)
-      br = make_rsrc(rhs_h, (long long)K * N * C::BSB);
+      br = make_rsrc(rhs_h, C::rhs_bytes((long long)K * N));
     else
-      br = make_rsrc(rhs_h + (long long)n0 * K * C::BSB, (long long)ncols * K * C::BSB);
+      br = make_rsrc(rhs_h + C::rhs_bytes((long long)n0 * K), C::rhs_bytes((long long)ncols * K));
 
     f32x4 acc[C::FM][C::FN];
     f32x4 tot[C::SCALED ? C::FM : 1][C::SCALED ? C::FN : 1];

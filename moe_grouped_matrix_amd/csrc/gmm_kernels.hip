@@ -107,7 +107,7 @@ hipError_t by_size(const Params& p, SizeClass sz, int cu, hipStream_t st) {
       return launch_big<BigCfg<NN, false>>(p, cu, st);
     }
   }
-  if constexpr (OP == Op::BF16 && BF8 && !NN) {
+  if constexpr (OP == Op::BF16 && BF8 && !NN && (FMT >> 1) < 3) {  // one-byte weights
     if (sz == SizeClass::Small && stream_fits(p)) {
       if (p.out_f32) return launch_stream<StreamCfg<true, (FMT >> 1)>>(p, cu, st);
       return launch_stream<StreamCfg<false, (FMT >> 1)>>(p, cu, st);
@@ -144,6 +144,9 @@ hipError_t launch_gmm(const Params& p, const KernelChoice& c, int cu, hipStream_
           case 0: return by_scaled<Op::BF16, false, true, 0>(p, c, cu, st);
           case 2: return by_scaled<Op::BF16, false, true, 2>(p, c, cu, st);
           case 4: return by_scaled<Op::BF16, false, true, 4>(p, c, cu, st);
+          case 6: return by_scaled<Op::BF16, false, true, 6>(p, c, cu, st);
+          case 8: return by_scaled<Op::BF16, false, true, 8>(p, c, cu, st);
+          case 10: return by_scaled<Op::BF16, false, true, 10>(p, c, cu, st);
         }
         return hipErrorInvalidValue;
       }

@@ -14,7 +14,8 @@ struct KernelChoice {
   Op op;
   bool nn;      // rhs [Ga,K,N]
   bool b_fp8;   // fp8 rhs widened to bf16 operands
-  int fmt;      // one-byte formats: fmt & 1 lhs (0 e4m3fn, 1 e5m2), fmt >> 1 rhs (2: int8 weights)
+  int fmt;      // narrow formats: fmt & 1 lhs (0 e4m3fn, 1 e5m2), fmt >> 1 rhs (the same, or
+                // widened weights 2 int8, 3 int4, 4 uint4, 5 fp4 e2m1)
   bool scaled;  // rhs_scale and/or lhs_scale present
   SizeClass size;
 };

@@ -102,6 +102,36 @@ def test_exact_small_integer_inputs_are_bit_exact(path, tile_policy):
                            want.view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32))
 
 
+@pytest.mark.parametrize("fmt", ["int4", "uint4", "fp4_e2m1"])
+def test_four_bit_weights_are_bit_exact(fmt, tile_policy):
+    """bf16 x packed four-bit weights (two to a byte, even elements in the
+    low nibble): small-integer activations make every product and sum exact,
+    so the outputs equal the oracle's bit for bit -- plain, and with
+    power-of-two block scales and a bias; fp4 also as float4_e2m1fn_x2."""
+    import moe_grouped_matrix_amd as m
+    g = torch.Generator().manual_seed(7)
+    sizes = [33, 0, 70, 257, 5]
+    M, K, N, nb = sum(sizes) + 7, 256, 200, 2
+    lhs = torch.randint(-3, 4, (M, K), generator=g).to(torch.bfloat16)
+    packed = torch.randint(0, 256, (len(sizes), N, K // 2), generator=g).to(torch.uint8)
+    rs = 2.0 ** torch.randint(-3, 4, (len(sizes), nb, 1, N), generator=g).to(torch.float32)
+    bias = torch.randint(-8, 9, (len(sizes), 1, N), generator=g).to(torch.bfloat16)
+    gs = torch.tensor(sizes, dtype=torch.int32)
+    print(f"four-bit {fmt} policy {tile_policy}", flush=True)
+    for out_dtype, kw in ((torch.float32, {}), (torch.bfloat16, {}),
+                          (torch.float32, dict(rhs_scale=rs, rhs_bias=bias))):
+        out = m.gmm(lhs.cuda(), packed.cuda(), gs.cuda(), rhs_format=fmt, out_dtype=out_dtype,
+                    **{k: v.cuda() for k, v in kw.items()}).cpu()
+        want = oracle.round_to(oracle.gmm_reference(lhs, packed, gs, rhs_format=fmt, **kw), out_dtype)
+        iv = torch.int16 if out_dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(out.view(iv), want.view(iv)), (fmt, out_dtype, list(kw))
+    if fmt == "fp4_e2m1":
+        out = m.gmm(lhs.cuda(), packed.view(torch.float4_e2m1fn_x2).cuda(), gs.cuda(), rhs_format=fmt).cpu()
+        assert torch.equal(out, oracle.round_to(oracle.gmm_reference(lhs, packed, gs, rhs_format=fmt),
+                                                torch.float32))
+    assert m.device_flags() == 0
+
+
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 def test_scaled_exact_inputs_are_bit_exact(path, tile_policy):
     """Power-of-two block scales, per-row scales and a bias keep the integer
