@@ -410,7 +410,9 @@ def main():
     for i, c in enumerate(cases):
         ms = statistics.median(per_kernel_ms[i])
         k, pk = op_peak(c)
-        detail[c.name] = {"median_ms": ms, "tflops": flops[i] / (ms * 1e-3) / 1e12,
+        qs = statistics.quantiles(per_kernel_ms[i], n=10) if len(per_kernel_ms[i]) > 1 else [ms] * 9
+        detail[c.name] = {"median_ms": ms, "p10_ms": qs[0], "p90_ms": qs[-1],
+                          "tflops": flops[i] / (ms * 1e-3) / 1e12,
                           "frac_peak": flops[i] / (ms * 1e-3) / 1e12 / pk,
                           "gbs_algorithmic": c.algorithmic_bytes() / (ms * 1e-3) / 1e9,
                           "active_rows": c.active_rows()}

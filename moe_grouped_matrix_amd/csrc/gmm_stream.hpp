@@ -186,11 +186,17 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
     StreamSrc scur = stream_src<C>(p, cur, true), snxt = stream_src<C>(p, nxt, !last_item);
     const StreamOff off = stream_offsets<C>(K, w, lane, bias_f32);
 
-    // prologue: stages 0 .. S-2 of the first tile, then every older memory
-    // operation is complete
+    // prologue: stages 0 .. S-2 of the first tile, then one range-dropped
+    // store in place of a previous tile's epilogue store, so that the first
+    // tile finds the same operations outstanding as every later one and the
+    // loop's constant waits hold for it too.  Only stage 0 is waited for:
+    // all workgroups ask for their first S-1 stages at once, and the last of
+    // those arrive several microseconds after the first.
 #pragma unroll
     for (int st = 0; st < C::S - 1; ++st) stream_stage<C>(scur, off, st, N, smem + st * C::STAGE, w);
-    wait_vmcnt<0>();
+    __builtin_amdgcn_raw_buffer_store_b32(0, uniform_rsrc(reinterpret_cast<const char*>(p.out), 0), (int)0x80000000,
+                                          0, 0);
+    wait_vmcnt<(C::S - 2) * C::OPS + C::E>();
     __syncthreads();
 
     // lane parts of the fragment addresses (stage-relative): weight row
