@@ -81,32 +81,39 @@ __device__ void build_plan(const Params& p, Plan& pl, int bm) {
   constexpr int EMAX = (kMaxGroups + T - 1) / T;
   const int tid = threadIdx.x;
   uint32_t flags = 0;
-  int s = p.group_offset ? p.group_offset[0] : 0;
+
+  // o[g+1] for the groups this thread owns (a contiguous run of E groups).
+  // The sizes and the offset come in through range-checked buffer loads, all
+  // issued before the first use: sizes past G (and the offset when there is
+  // none) read as 0, so no branch stands between the loads, and the plan
+  // waits for memory once instead of once per load.
+  const int E = (p.G + T - 1) / T;
+  const __amdgpu_buffer_rsrc_t rsz = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(p.group_sizes), (short)0, p.G * 4, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rof = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(p.group_offset), (short)0, p.group_offset ? 4 : 0, kBufferRsrcWord3);
+  int raw[EMAX];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) raw[e] = __builtin_amdgcn_raw_buffer_load_b32(rsz, (tid * E + e) * 4, 0, 0);
+  int s = __builtin_amdgcn_raw_buffer_load_b32(rof, 0, 0, 0);
+  long long loc[EMAX];
+  long long sum = 0;
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    // entries e >= E belong to the next thread's run
+    int x = e < E ? raw[e] : 0;
+    if (x < 0) {
+      flags |= kFlagNegative;
+      x = 0;
+    }
+    sum += x;
+    loc[e] = sum;
+  }
   if (s < 0 || s > p.G - p.Ga) {
     flags |= kFlagBadOffset;
     s = s < 0 ? 0 : (s > p.G ? p.G : s);
   }
   const int ga = p.Ga < p.G - s ? p.Ga : p.G - s;
-
-  // o[g+1] for the groups this thread owns (a contiguous run of E groups).
-  const int E = (p.G + T - 1) / T;
-  long long loc[EMAX];
-  long long sum = 0;
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-    const int g = tid * E + e;
-    long long v = 0;
-    if (e < E && g < p.G) {
-      int x = p.group_sizes[g];
-      if (x < 0) {
-        flags |= kFlagNegative;
-        x = 0;
-      }
-      v = x;
-    }
-    sum += v;
-    loc[e] = sum;
-  }
   long long total;
   const long long excl = block_excl_scan<T>(sum, pl.wave_tot, &total);
   if (total > p.M) flags |= kFlagExceed;
