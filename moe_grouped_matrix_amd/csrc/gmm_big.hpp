@@ -33,10 +33,12 @@
 
 namespace gmmk {
 
-template <bool NN_, bool OUT_F32_>
+// BIAS_: the problem has a bias (without one the epilogue adds nothing)
+template <bool NN_, bool OUT_F32_, bool BIAS_>
 struct BigCfg {
   static constexpr bool NN = NN_;
   static constexpr bool OUT_F32 = OUT_F32_;
+  static constexpr bool BIAS = BIAS_;
   static constexpr int BM = 256, BN = 256;
   static constexpr int WM = 2, WN = 4, NWAVES = WM * WN, T = 64 * NWAVES;
   static constexpr int FM = 4, FN = 2;    // 32 x 32 blocks of a full-tile wave (128 x 64)
@@ -344,15 +346,15 @@ __device__ __forceinline__ int swz_out(int r) { return (r & 7) ^ ((r >> 3) & 1);
 // staging slice so that a store writes 8 whole 128-byte row segments
 // instead of 32 scattered 32-byte ones.  Stores outside the tile's valid
 // rows and columns are dropped by the range check; a half tile pads to the
-// full tile's store count E.
-template <class C, int FMA>
+// full tile's store count E.  BIAS: add the bias row (without one, the
+// accumulators are rounded as they are).
+template <class C, int FMA, bool BIAS>
 __device__ __forceinline__ void big_epilogue(const Params& p, const f32x16 (&acc)[C::FM][C::FN], const BigItem& it,
                                              const char* bias_slot, char* stg, int kh, int r32, int lane) {
   const int N = p.N;
   char* tile = reinterpret_cast<char*>(p.out) + ((long long)it.row0 * N + it.n0) * C::es_out;
   const int nrec = ((it.rows - 1) * N + it.ncols) * C::es_out;
   const __amdgpu_buffer_rsrc_t ro = uniform_rsrc(tile, nrec);
-  const bool has_bias = p.rhs_bias != nullptr;
   const bool bias_f32 = p.bias_f32 != 0;
   const int srow = lane >> 3, schunk = lane & 7;  // store phase: row and chunk of this lane
   const int wr_row = r32 * 128;                   // write phase: this lane's staging row
@@ -399,14 +401,24 @@ __device__ __forceinline__ void big_epilogue(const Params& p, const f32x16 (&acc
       for (int fn = 0; fn < C::FN; ++fn) {
 #pragma unroll
         for (int gp = 0; gp < 4; gp += 2) {
-          float bias[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-          if (has_bias) load_bias(fn, gp, bias);
+          float v[2][4];
+#pragma unroll
+          for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[x][i] = acc[fm][fn][4 * (gp + x) + i];
+          if constexpr (BIAS) {
+            float bias[2][4];
+            load_bias(fn, gp, bias);
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v[x][i] += bias[x][i];
+          }
           int lo[4], hi[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const auto r = __builtin_amdgcn_permlane32_swap(
-                __float_as_uint(acc[fm][fn][4 * gp + i] + bias[0][i]),
-                __float_as_uint(acc[fm][fn][4 * (gp + 1) + i] + bias[1][i]), false, false);
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0][i]), __float_as_uint(v[1][i]),
+                                                            false, false);
             lo[i] = (int)r[0];
             hi[i] = (int)r[1];
           }
@@ -421,16 +433,24 @@ __device__ __forceinline__ void big_epilogue(const Params& p, const f32x16 (&acc
       for (int fn = 0; fn < C::FN; ++fn) {
 #pragma unroll
         for (int gp = 0; gp < 4; gp += 2) {
-          float bias[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-          if (has_bias) load_bias(fn, gp, bias);
+          float v[2][4];
+#pragma unroll
+          for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[x][i] = acc[fm][fn][4 * (gp + x) + i];
+          if constexpr (BIAS) {
+            float bias[2][4];
+            load_bias(fn, gp, bias);
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v[x][i] += bias[x][i];
+          }
           uint32_t x0[2], x1[2];
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
-            const int g = 4 * (gp + x);
-            x0[x] = (uint32_t)f32_to_bf16_rne(acc[fm][fn][g] + bias[x][0]) |
-                    ((uint32_t)f32_to_bf16_rne(acc[fm][fn][g + 1] + bias[x][1]) << 16);
-            x1[x] = (uint32_t)f32_to_bf16_rne(acc[fm][fn][g + 2] + bias[x][2]) |
-                    ((uint32_t)f32_to_bf16_rne(acc[fm][fn][g + 3] + bias[x][3]) << 16);
+            x0[x] = pk_bf16_rne(v[x][0], v[x][1]);
+            x1[x] = pk_bf16_rne(v[x][2], v[x][3]);
           }
           const auto r0 = __builtin_amdgcn_permlane32_swap(x0[0], x0[1], false, false);
           const auto r1 = __builtin_amdgcn_permlane32_swap(x1[0], x1[1], false, false);
@@ -628,7 +648,7 @@ __global__ __launch_bounds__(C::T) void gmm_big_kernel(Params p) {
     }
     // the last step's stage (the next tile's step 3 goes there after its
     // first barrier) holds the epilogue's staging slices, 4 KB per wave
-    big_epilogue<C, FMA>(p, acc, cur, bias0 + par * C::BIAS_SLOT,
+    big_epilogue<C, FMA, C::BIAS>(p, acc, cur, bias0 + par * C::BIAS_SLOT,
                          smem + ((stage + 3) & (C::S - 1)) * C::STAGE + w * 4096, kh, r32, lane);
   };
 

@@ -260,6 +260,15 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
+// Two values rounded the same way and packed, lo in bits 0-15: one
+// v_cvt_pk_bf16_f32 for the pair (converting each value on its own costs one
+// conversion per value plus the shifts and ors that pack them).
+__device__ __forceinline__ uint32_t pk_bf16_rne(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
 // 16-byte chunk c (0..7) of a 128-byte LDS row r is stored at chunk
 // c ^ swz(r).  Sixteen consecutive rows read at one logical chunk hit sixteen
 // distinct 16-byte bank groups, with 32 or 64 banks.

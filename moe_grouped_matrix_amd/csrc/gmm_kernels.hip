@@ -103,8 +103,10 @@ hipError_t by_size(const Params& p, SizeClass sz, int cu, hipStream_t st) {
   if constexpr (OP == Op::BF16 && !BF8 && !SC) {
     // the big kernel runs a tile in five phases of K steps of 32: K >= 160
     if (sz == SizeClass::Big && p.K >= 5 * 32) {
-      if (p.out_f32) return launch_big<BigCfg<NN, true>>(p, cu, st);
-      return launch_big<BigCfg<NN, false>>(p, cu, st);
+      const bool bias = p.rhs_bias != nullptr;
+      if (p.out_f32)
+        return bias ? launch_big<BigCfg<NN, true, true>>(p, cu, st) : launch_big<BigCfg<NN, true, false>>(p, cu, st);
+      return bias ? launch_big<BigCfg<NN, false, true>>(p, cu, st) : launch_big<BigCfg<NN, false, false>>(p, cu, st);
     }
   }
   if constexpr (OP == Op::BF16 && BF8 && !NN && (FMT >> 1) < 3) {  // one-byte weights

@@ -304,8 +304,8 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
               i32x4{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3])}, ro,
               voff, 0, 0);
         } else {
-          const uint32_t x0 = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-          const uint32_t x1 = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+          const uint32_t x0 = pk_bf16_rne(v[0], v[1]);
+          const uint32_t x1 = pk_bf16_rne(v[2], v[3]);
           __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)x0, (int)x1}, ro, voff, 0, 0);
         }
         tot[0] = f32x4{0.f, 0.f, 0.f, 0.f};

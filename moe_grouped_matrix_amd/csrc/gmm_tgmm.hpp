@@ -585,7 +585,7 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
     hold(1);
     L_new = 2 * W + __builtin_amdgcn_readfirstlane(sched[kSchedSlot]);
     // the last step's stage holds the epilogue's staging slices, 4 KB per wave
-    big_epilogue<C, FMA>(p, acc, cur.out, smem, smem + ((stage + 3) & (C::S - 1)) * C::STAGE + w * 4096, kh, r32,
+    big_epilogue<C, FMA, false>(p, acc, cur.out, smem, smem + ((stage + 3) & (C::S - 1)) * C::STAGE + w * 4096, kh, r32,
                          lane);
   };
 

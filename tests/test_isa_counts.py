@@ -55,7 +55,7 @@ def test_big_kernel_keeps_every_counted_store(kernel_asm):
         stores = sum(1 for ln in lines if ln.startswith("buffer_store"))
         assert stores == 2 * E_FULL[out_f32], (name, stores)
         seen += 1
-    assert seen == 4  # NT / NN x bf16 / f32 output
+    assert seen == 8  # NT / NN x bf16 / f32 output x with / without bias
 
 
 def test_tgmm_kernel_keeps_every_counted_store(kernel_asm):
