@@ -257,14 +257,15 @@ class ClockSampler:
             txt = fh.read()
         os.unlink(self.path)
         clk, pw = [], []
-        for block in txt.split("T")[1:]:
-            try:
-                ts = float(block.split()[0])
-            except (ValueError, IndexError):
-                continue
+        # each reading follows a line "T<epoch seconds>"
+        parts = re.split(r"^T(\d+\.\d+)\s*$", txt, flags=re.M)
+        for stamp, block in zip(parts[1::2], parts[2::2]):
+            ts = float(stamp)
             if not (t0 <= ts <= t1):
                 continue
-            c = [int(x) for x in re.findall(r"CLK:\s*(\d+) MHz", block)]
+            # the graphics clock of each XCD (GFX_0 .. GFX_7); the listing
+            # also holds memory, video and SoC clocks
+            c = [int(x) for x in re.findall(r"GFX_\d+:\s*CLK:\s*(\d+) MHz", block)]
             p = re.findall(r"SOCKET_POWER:\s*(\d+) W", block)
             if c:
                 clk.append(sum(c) / len(c))
