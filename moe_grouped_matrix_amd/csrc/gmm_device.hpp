@@ -536,7 +536,10 @@ __device__ inline void fill_item(const Params& p, long long begin, long long end
 
 template <class C>
 __global__ __launch_bounds__(C::T) void gmm_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  // operand stages, then (scaled problems) two buffers of one block's row
+  // and column scales
+  constexpr int SC_BYTES = C::SCALED ? 2 * (C::BM + C::BN) * 4 : 0;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS + SC_BYTES];
   __shared__ Plan pl;
   if (threadIdx.x == 0) pl.flags = 0;
   __syncthreads();
@@ -612,36 +615,66 @@ __global__ __launch_bounds__(C::T) void gmm_kernel(Params p) {
     Stage<C> st;
     load_tile(cfg, st, ar, br, 0, K, N, n0);
     store_tile(cfg, st, smem, smem + C::A_BYTES);
+
+    // Block scales pass through LDS one block ahead, like the operands: in
+    // the first step of block b thread i loads the row scale of tile row i
+    // and the column scale of tile column i for block b+1 before the
+    // multiply and writes them to buffer (b+1) & 1 after it; block b's fold
+    // reads buffer b & 1.  (Loading each lane's 20 scales from memory at
+    // the block's start and waiting for them at its end cost more than the
+    // multiplies.)  Rows and columns outside the tile, and an absent scale,
+    // count 1.
+    const int kt_per_blk = C::SCALED ? p.blk / C::BK : 0;
+    constexpr int SL = C::SCALED ? (C::BM + C::T - 1) / C::T : 1, SR = C::SCALED ? (C::BN + C::T - 1) / C::T : 1;
+    float* const lsc = reinterpret_cast<float*>(smem + C::LDS);  // [2][BM]
+    float* const rsc = lsc + 2 * C::BM;                          // [2][BN]
+    float sl[SL], sr[SR];
+    auto load_scales = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < SL; ++i) {
+        const int r = tid + i * C::T;
+        sl[i] = (p.lhs_scale && r < rows) ? p.lhs_scale[(long long)(row0 + r) * p.nb + b] : 1.f;
+      }
+#pragma unroll
+      for (int i = 0; i < SR; ++i) {
+        const int c = tid + i * C::T;
+        sr[i] = (p.rhs_scale && c < ncols) ? p.rhs_scale[((long long)h * p.nb + b) * N + n0 + c] : 1.f;
+      }
+    };
+    auto store_scales = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < SL; ++i)
+        if (tid + i * C::T < C::BM) lsc[buf * C::BM + tid + i * C::T] = sl[i];
+#pragma unroll
+      for (int i = 0; i < SR; ++i)
+        if (tid + i * C::T < C::BN) rsc[buf * C::BN + tid + i * C::T] = sr[i];
+    };
+    if constexpr (C::SCALED) {
+      load_scales(0);
+      store_scales(0);
+    }
     __syncthreads();
 
-    const int kt_per_blk = C::SCALED ? p.blk / C::BK : 0;
-    float rs[C::SCALED ? C::FN : 1];
-    float ls[C::SCALED ? C::FM : 1][4];
     for (int kt = 0; kt < KT; ++kt) {
       char* sa = smem + (kt & 1) * (C::A_BYTES + C::B_BYTES);
       char* sb = sa + C::A_BYTES;
+      bool next_scales = false;
       if constexpr (C::SCALED) {
-        if (kt % kt_per_blk == 0) {
-          // this block's scales, read now and used when the block ends
-          const int b = kt / kt_per_blk;
-#pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn) {
-            const int col = n0 + wn * C::TN + fn * 16 + r16;
-            rs[fn] = (p.rhs_scale && col < N) ? p.rhs_scale[((long long)h * p.nb + b) * N + col] : 1.f;
-          }
-#pragma unroll
-          for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = wm * C::TM + fm * 16 + 4 * q + i;
-              ls[fm][i] = (p.lhs_scale && r < rows) ? p.lhs_scale[(long long)(row0 + r) * p.nb + b] : 1.f;
-            }
-        }
+        next_scales = kt % kt_per_blk == 0 && kt / kt_per_blk + 1 < p.nb;
+        if (next_scales) load_scales(kt / kt_per_blk + 1);
       }
       if (kt + 1 < KT) load_tile(cfg, st, ar, br, kt + 1, K, N, n0);
       mma_tile<C>(acc, sa, sb);
       if constexpr (C::SCALED) {
         if ((kt + 1) % kt_per_blk == 0) {
+          const int bb = (kt / kt_per_blk) & 1;
+          float rs[C::FN];
+          f32x4 ls[C::FM];
+#pragma unroll
+          for (int fn = 0; fn < C::FN; ++fn) rs[fn] = rsc[bb * C::BN + wn * C::TN + fn * 16 + r16];
+#pragma unroll
+          for (int fm = 0; fm < C::FM; ++fm)
+            ls[fm] = *reinterpret_cast<const f32x4*>(lsc + bb * C::BM + wm * C::TM + fm * 16 + 4 * q);
 #pragma unroll
           for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
@@ -651,6 +684,7 @@ __global__ __launch_bounds__(C::T) void gmm_kernel(Params p) {
               acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
+        if (next_scales) store_scales((kt / kt_per_blk + 1) & 1);
       }
       if (kt + 1 < KT) {
         char* na = smem + ((kt + 1) & 1) * (C::A_BYTES + C::B_BYTES);
