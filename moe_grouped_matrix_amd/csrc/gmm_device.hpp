@@ -534,11 +534,18 @@ __device__ inline void fill_item(const Params& p, long long begin, long long end
   for (long long off = begin + (long long)threadIdx.x * 16; off < end; off += (long long)C::T * 16) fill16(p, off);
 }
 
+// Bytes of one wave's epilogue staging slice: 16 rows of TN values of up to
+// 4 bytes, each row padded by 16 bytes.  The slices of all waves fit in the
+// operand stages.
+template <class C>
+constexpr int kStageSlice = 16 * (C::TN * 4 + 16);
+
 template <class C>
 __global__ __launch_bounds__(C::T) void gmm_kernel(Params p) {
   // operand stages, then (scaled problems) two buffers of one block's row
   // and column scales
   constexpr int SC_BYTES = C::SCALED ? 2 * (C::BM + C::BN) * 4 : 0;
+  static_assert(C::T / 64 * kStageSlice<C> <= C::LDS, "epilogue staging fits the operand stages");
   __shared__ __attribute__((aligned(16))) char smem[C::LDS + SC_BYTES];
   __shared__ Plan pl;
   if (threadIdx.x == 0) pl.flags = 0;
@@ -693,37 +700,61 @@ __global__ __launch_bounds__(C::T) void gmm_kernel(Params p) {
       __syncthreads();
     }
 
-    // epilogue: bias, round, masked store
+    // epilogue: bias, round, store.  Each 16-row block of the wave's tile
+    // passes through the wave's staging slice (the operand stages are free
+    // once every wave is past the K loop's last barrier), so that each store
+    // writes a whole 16-byte chunk of an output row instead of one value.
+    // Chunks outside the tile's valid rows and columns are skipped: N is a
+    // multiple of 8 and the output 16-byte aligned, so a chunk is either
+    // all inside or all outside.
+    {
+      const int es = out_es;
+      const int pitch = C::TN * es + 16;  // staged row bytes; the extra 16 spread the rows over the banks
+      char* const stg = smem + w * kStageSlice<C>;
+      const int cpr = C::TN * es / 16;  // 16-byte chunks per staged row
+      float bias[C::FN];
 #pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn) {
-      const int cl = wn * C::TN + fn * 16 + r16;
-      const int col = n0 + cl;
-      float bias = 0.f;
-      if (p.rhs_bias && cl < ncols) {
-        const long long bi = (long long)h * N + col;
-        bias = p.bias_f32 ? reinterpret_cast<const float*>(p.rhs_bias)[bi]
-                          : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.rhs_bias)[bi]);
+      for (int fn = 0; fn < C::FN; ++fn) {
+        const int cl = wn * C::TN + fn * 16 + r16;
+        bias[fn] = 0.f;
+        if (p.rhs_bias && cl < ncols) {
+          const long long bi = (long long)h * N + n0 + cl;
+          bias[fn] = p.bias_f32 ? reinterpret_cast<const float*>(p.rhs_bias)[bi]
+                                : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.rhs_bias)[bi]);
+        }
       }
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
+      for (int fm = 0; fm < C::FM; ++fm) {
+        // lane (q, r16) holds rows 4 q + i of the block, column 16 fn + r16
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rl = wm * C::TM + fm * 16 + 4 * q + i;
-          if (rl < rows && cl < ncols) {
+        for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
             float v;
             if constexpr (C::SCALED)
               v = tot[fm][fn][i];
             else
               v = acc_value<C>(acc[fm][fn][i]);
-            v += bias;
-            const long long oi = (long long)(row0 + rl) * N + col;
+            v += bias[fn];
+            char* d = stg + (4 * q + i) * pitch + (fn * 16 + r16) * es;
             if (p.out_f32)
-              reinterpret_cast<float*>(p.out)[oi] = v;
+              *reinterpret_cast<float*>(d) = v;
             else
-              reinterpret_cast<uint16_t*>(p.out)[oi] = f32_to_bf16_rne(v);
+              *reinterpret_cast<uint16_t*>(d) = f32_to_bf16_rne(v);
           }
+        for (int c = lane; c < 16 * cpr; c += 64) {
+          const int r = c / cpr, cb = c % cpr;
+          const i32x4 d = *reinterpret_cast<const i32x4*>(stg + r * pitch + cb * 16);
+          const int rl = wm * C::TM + fm * 16 + r;
+          const int cl = wn * C::TN + cb * (16 / es);
+          if (rl < rows && cl < ncols)
+            *reinterpret_cast<i32x4*>(reinterpret_cast<char*>(p.out) +
+                                      ((long long)(row0 + rl) * N + n0 + cl) * es) = d;
         }
+      }
     }
+    // the next tile's first stage overwrites the staging slices
+    __syncthreads();
   }
 }
 
