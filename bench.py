@@ -280,7 +280,8 @@ class ClockSampler:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 50; 500 for the microsecond-scale tiny_fp32 and decode_fp8w)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fwd+dlhs",
                     help="fwd+dlhs (default) or one of tiny_fp32, moe_fwd_bf16, moe_dlhs_bf16, "
@@ -288,6 +289,8 @@ def main():
                          "quant_fp8 (the activation quantiser)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 500 if args.workload in ("tiny_fp32", "decode_fp8w") else 50
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
