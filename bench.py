@@ -96,6 +96,25 @@ def op_peak(case):
     return "bf16", PEAK["bf16"]
 
 
+def _host():
+    """The host the CPU baseline ran on: logical CPUs and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"os_cpu_count": os.cpu_count(), "cpu_model": model}
+
+
+# workloads whose CPU baseline is also timed on one thread (the microsecond-
+# scale ones, where a caller might weigh a single host core against the GPU)
+SINGLE_THREAD = {"tiny_fp32", "decode_fp8w"}
+
+
 def cpu_baseline(cases, target_s: float = 20.0):
     """Time the oracle on a bounded sample of each case: a few rows of a few
     groups, packed into a sub-problem with the same K, N and weights (every
@@ -112,13 +131,7 @@ def cpu_baseline(cases, target_s: float = 20.0):
         return cpu_baseline_tgmm(cases, target_s)
     if any(is_quant(c) for c in cases):
         return cpu_baseline_quant(cases, target_s)
-    flops_total = 0.0
-    secs_total = 0.0
-    descr = []
-    # calibrate, then size the sample to ~target_s (re-measuring while the
-    # sample ran well short of it: per-group setup dominates small samples)
-    rows_per = 16
-    for phase in ("calibrate", "calibrate", "measure"):
+    def sample(rows_per):
         flops_total = secs_total = 0.0
         descr = []
         for case in cases:
@@ -146,14 +159,33 @@ def cpu_baseline(cases, target_s: float = 20.0):
             secs_total += time.perf_counter() - t0
             flops_total += 2.0 * len(idx) * case.N * case.K
             descr.append(f"{case.name}: {len(idx)} rows of {len(groups)} groups")
+        return flops_total, secs_total, descr
+
+    # calibrate, then size the sample to ~target_s (re-measuring while the
+    # sample ran well short of it: per-group setup dominates small samples)
+    rows_per = 16
+    for phase in ("calibrate", "calibrate", "measure"):
+        flops_total, secs_total, descr = sample(rows_per)
         if phase == "calibrate":
             scale = target_s / max(secs_total, 1e-3)
             rows_per = max(1, int(rows_per * scale))
             if secs_total > 0.5 * target_s:
                 break
-    return {"value": flops_total / secs_total / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "; ".join(descr) + f" (fp64 oracle, {secs_total:.1f} s)"}
+    res = {"value": flops_total / secs_total / 1e12, "unit": "TFLOP/s", "cores": threads,
+           "kind": "oracle",
+           "sample": "; ".join(descr) + f" (fp64 oracle, {secs_total:.1f} s)"}
+    res.update(_host())
+    if all(c.name in SINGLE_THREAD for c in cases):
+        # the same kind of sample on one thread, sized for a few seconds
+        rows_1 = max(1, int(rows_per * 3.0 / max(secs_total * threads, 1e-3)))
+        oracle.set_threads(1)
+        try:
+            f1, s1, d1 = sample(rows_1)
+        finally:
+            oracle.set_threads(threads)
+        res["single_thread"] = {"value": f1 / s1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                                "sample": "; ".join(d1) + f" (fp64 oracle, {s1:.1f} s)"}
+    return res
 
 
 def cpu_baseline_tgmm(cases, target_s: float = 20.0):
@@ -182,9 +214,9 @@ def cpu_baseline_tgmm(cases, target_s: float = 20.0):
             per = max(1, int(per * target_s / max(secs, 1e-3)))
             if secs > 0.5 * target_s:
                 break
-    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{case.name}: {len(sel)} output rows (h, k) of {len(groups)} groups "
-                      f"(fp64 oracle, {secs:.1f} s)"}
+    return dict({"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                 "sample": f"{case.name}: {len(sel)} output rows (h, k) of {len(groups)} groups "
+                           f"(fp64 oracle, {secs:.1f} s)"}, **_host())
 
 
 def cpu_baseline_quant(cases, target_s: float = 20.0):
@@ -206,8 +238,8 @@ def cpu_baseline_quant(cases, target_s: float = 20.0):
             if secs > 0.5 * target_s or n == case.M:
                 break
     byts = n * case.K * 3 + n * (case.K // case.block) * 4
-    return {"value": byts / secs / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{case.name}: {n} of {case.M} rows (binary32 oracle, {secs:.1f} s)"}
+    return dict({"value": byts / secs / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+                 "sample": f"{case.name}: {n} of {case.M} rows (binary32 oracle, {secs:.1f} s)"}, **_host())
 
 
 class ClockSampler:

@@ -56,6 +56,12 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def set_threads(n: int) -> int:
+    """Threads the oracle's parallel loops use from now on (n <= 0: keep);
+    returns the count in force.  Results do not depend on it."""
+    return int(_load().oracle_set_threads(int(n)))
+
+
 def _load():
     global _lib
     if _lib is None:
@@ -63,6 +69,8 @@ def _load():
             build()
         lib = ctypes.CDLL(_LIB_PATH)
         lib.oracle_decode_bf16.restype = ctypes.c_double
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = ctypes.c_int
         lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
         lib.oracle_decode_e4m3fn.restype = ctypes.c_double
         lib.oracle_decode_e4m3fn.argtypes = [ctypes.c_uint8]

@@ -58,9 +58,19 @@
  *            3, 4 and 6 (OCP microscaling formats specification).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads the parallel loops below use (the benchmark times the oracle on
+ * one thread as well as on all of them).  n <= 0 leaves the count as it is.
+ * Returns the count in force.  No arithmetic depends on it: every output
+ * element is summed by one thread in k order. */
+int oracle_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
+}
 
 #define OR_F32 0
 #define OR_BF16 1
