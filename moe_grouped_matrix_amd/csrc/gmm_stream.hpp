@@ -197,7 +197,9 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
     __builtin_amdgcn_raw_buffer_store_b32(0, uniform_rsrc(reinterpret_cast<const char*>(p.out), 0), (int)0x80000000,
                                           0, 0);
     wait_vmcnt<(C::S - 2) * C::OPS + C::E>();
-    __syncthreads();
+    // a bare barrier, as in the loop: __syncthreads() carries a workgroup
+    // fence, which the compiler meets by draining every load in flight
+    ring_barrier();
 
     // lane parts of the fragment addresses (stage-relative): weight row
     // (output column) wn, K half wk -> 16-byte chunk 4 wk + q of the row;
