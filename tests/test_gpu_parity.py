@@ -102,6 +102,38 @@ def test_exact_small_integer_inputs_are_bit_exact(path, tile_policy):
                            want.view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32))
 
 
+@pytest.mark.parametrize("N", [392, 264])
+@pytest.mark.parametrize("T", [False, True], ids=["nt", "nn"])
+def test_big_kernel_fewest_k_steps_ragged_n_bias_or_none(N, T):
+    """The bf16 big kernel at its fewest K steps for a bf16 K (K = 192: six
+    steps of 32, one pass of the middle loop), N tails of 136 columns (full
+    tile mode) and 8 columns (half mode), row tiles of at most 128 rows, with
+    and without a bias (separate instantiations: without one nothing is
+    added), f32 and bf16 output.  Small integers make every sum exact, so the
+    output must equal the oracle's bit for bit."""
+    import moe_grouped_matrix_amd as m
+    g = torch.Generator().manual_seed(7)
+    sizes = [300, 0, 129, 40, 512, 3]
+    M, K = sum(sizes) + 5, 192
+    lhs = torch.randint(-3, 4, (M, K), generator=g).to(torch.bfloat16)
+    rhs = torch.randint(-3, 4, (len(sizes), K, N) if T else (len(sizes), N, K), generator=g).to(torch.bfloat16)
+    bias = torch.randint(-8, 9, (len(sizes), 1, N), generator=g).to(torch.bfloat16)
+    m.set_tile_policy(2)
+    try:
+        for b in (None, bias):
+            for out_dtype in (torch.float32, torch.bfloat16):
+                print(f"big kernel K={K} N={N} nn={T} bias={b is not None} out={out_dtype}", flush=True)
+                kw = {} if b is None else {"rhs_bias": b}
+                case = _case(lhs, rhs, sizes, transpose_rhs=T, out_dtype=out_dtype, **kw)
+                out = run_gpu(case).cpu()
+                want = oracle.round_to(reference(case), out_dtype)
+                iv = torch.int16 if out_dtype == torch.bfloat16 else torch.int32
+                assert torch.equal(out.view(iv), want.view(iv)), (N, T, b is not None, out_dtype)
+        assert m.device_flags() == 0
+    finally:
+        m.set_tile_policy(0)
+
+
 @pytest.mark.parametrize("fmt", ["int4", "uint4", "fp4_e2m1"])
 def test_four_bit_weights_are_bit_exact(fmt, tile_policy):
     """bf16 x packed four-bit weights (two to a byte, even elements in the
