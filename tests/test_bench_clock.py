@@ -1,7 +1,8 @@
-"""bench.py's clock sampler (host logic, CPU only): it must average the
+"""Host logic of bench.py (CPU only).  The clock sampler must average the
 graphics clock of every XCD and the socket power over the readings stamped
 inside the timed span, ignoring the memory, video and SoC clocks that the same
-amd-smi listing holds, and readings stamped outside the span."""
+amd-smi listing holds, and readings stamped outside the span.  And bench.py
+refuses to run on more than one GPU."""
 import os
 import sys
 import tempfile
@@ -42,3 +43,13 @@ def test_graphics_clocks_and_power_inside_the_span():
 
 def test_no_reading_in_the_span_gives_none():
     assert _summary(_reading(100.0, [1600] * 8, 1400), 200.0, 300.0) is None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The path runs on one GPU: --gpus 2 exits with status 2 and says so,
+    before touching a GPU."""
+    import subprocess
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
