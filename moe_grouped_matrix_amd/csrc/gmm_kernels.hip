@@ -5,6 +5,7 @@
 #include "gmm_big.hpp"
 #include "gmm_device.hpp"
 #include "gmm_stream.hpp"
+#include "gmm_w8a8.hpp"
 #include "gmm_tgmm.hpp"
 #include "gmm_launch.hpp"
 
@@ -76,6 +77,23 @@ hipError_t launch_stream(const Params& p, int cu_count, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The block-scaled fp8 x fp8 ring kernel: one workgroup per CU (its ring
+// takes most of the LDS), at most one per work item.
+template <class C>
+hipError_t launch_w8a8(const Params& p, int cu_count, hipStream_t stream) {
+  const long long n_tiles = (p.N + C::BN - 1) / C::BN;
+  const long long m_tiles = (p.M + C::BM - 1) / C::BM + p.Ga;
+  const long long row_bytes = (long long)p.N * (p.out_f32 ? 4 : 2);
+  const long long zero_items = ((long long)p.M * row_bytes + kZeroChunk - 1) / kZeroChunk + 2;
+  const long long bound = m_tiles * n_tiles + zero_items;
+  long long grid = cu_count;
+  if (grid > bound) grid = bound;
+  if (grid >= 8) grid -= grid % 8;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(gmm_w8a8_kernel<C>, dim3((unsigned)grid), dim3(C::T), 0, stream, p);
+  return hipGetLastError();
+}
+
 // The weight-streaming kernel takes bf16 x e4m3 NT problems with few rows per
 // group: K in stages of 128 with at least S of them per tile, and scale
 // blocks of exactly one stage (or no scale).
@@ -114,6 +132,10 @@ hipError_t by_size(const Params& p, SizeClass sz, int cu, hipStream_t st) {
       if (p.out_f32) return launch_stream<StreamCfg<true, (FMT >> 1)>>(p, cu, st);
       return launch_stream<StreamCfg<false, (FMT >> 1)>>(p, cu, st);
     }
+  }
+  if constexpr (OP == Op::FP8 && !NN && SC) {  // W8A8 with scale blocks of one K step
+    using CB = typename Pick<OP, NN, BF8, SC, SizeClass::Big, FMT>::type;
+    if (sz == SizeClass::Big && p.blk == CB::BK) return launch_w8a8<CB>(p, cu, st);
   }
   if (sz == SizeClass::Big)
     return launch_cfg<typename Pick<OP, NN, BF8, SC, SizeClass::Big, FMT>::type>(p, cu, st);

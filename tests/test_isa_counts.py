@@ -71,6 +71,6 @@ def test_tgmm_kernel_keeps_every_counted_store(kernel_asm):
 def test_loop_kernels_do_not_spill(kernel_asm):
     # a spill reload is a vector memory load: its wait would drain every
     # direct-to-LDS load queued behind the K loop's constant counts
-    for pattern in (r"_ZN4gmmk15gmm_tgmm_kernel", r"_ZN4gmmk17gmm_stream_kernel"):
+    for pattern in (r"_ZN4gmmk15gmm_tgmm_kernel", r"_ZN4gmmk17gmm_stream_kernel", r"_ZN4gmmk15gmm_w8a8_kernel"):
         for name, lines in _functions(kernel_asm, pattern):
             assert not any(ln.startswith("scratch_") for ln in lines), name
