@@ -33,13 +33,15 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # the sources each workload's kernel is built from: committed counter
 # readings stay valid until one of them changes
-KERNEL_SOURCES_COMMON = ("gmm_params.hpp", "gmm_device.hpp", "gmm_kernels.hip")
+KERNEL_SOURCES_COMMON = ("gmm_params.hpp", "gmm_device.hpp", "gmm_kernels.hip", "gmm_launch.hpp")
 KERNEL_SOURCES = {
+    "tiny_fp32": (),
     "moe_fwd_bf16": ("gmm_big.hpp",),
     "moe_dlhs_bf16": ("gmm_big.hpp",),
     "decode_fp8w": ("gmm_big.hpp", "gmm_stream.hpp"),
+    "w8a8_fp8": ("gmm_big.hpp", "gmm_w8a8.hpp"),
     "tgmm_bf16": ("gmm_big.hpp", "gmm_tgmm.hpp"),
-    "quant_fp8": ("gmm_quant.hip", "gmm_launch.hpp"),
+    "quant_fp8": ("gmm_quant.hip",),
 }
 # workloads whose weights fit in the caches between calls: each timed call
 # starts from evicted L2 / Infinity Cache (a 512 MB read outside the events)

@@ -86,13 +86,16 @@ typedef struct gmm_handle gmm_handle;
 
 /*
  * gmm_create: make a handle on HIP device `device` (must be gfx950).
- * Allocates one 4-byte device word for the data-error flags.
+ * Allocates a 16-byte device block for the data-error flags.  The first
+ * gmm_tgmm_run on each stream allocates that stream's 64-byte block of
+ * work-queue counters (kept until gmm_destroy); no other call allocates.
  * Returns GMM_E_UNSUPPORTED on another architecture, GMM_E_HIP on a HIP
  * failure, GMM_E_INVALID when h is NULL.
  */
 gmm_status gmm_create(gmm_handle** h, int device);
 
-/* gmm_destroy: free the handle and its flag word.  NULL is allowed. */
+/* gmm_destroy: free the handle, its flag word and its counter blocks.  Work
+ * queued with the handle must have finished.  NULL is allowed. */
 gmm_status gmm_destroy(gmm_handle* h);
 
 /* gmm_last_error: text of the last failure on h ("" when none; never NULL). */
@@ -128,7 +131,8 @@ const char* gmm_last_error(const gmm_handle* h);
  *
  * Size limits: M < 2^31; N % 8 == 0; K % 64 == 0 for BF16 products,
  * K % 128 == 0 for fp8 x fp8, K % 32 == 0 for F32, and the block length K/nb
- * must be a multiple of the same number; Ga <= G.  Outside them the call
+ * must be a multiple of the same number; Ga <= G; one group's weight, a
+ * 256-row lhs tile and a 256-row output tile each below 2 GiB.  Outside them the call
  * returns GMM_E_UNSUPPORTED and queues nothing.  Shape or dtype
  * inconsistencies return GMM_E_INVALID and queue nothing.  A launch failure
  * returns GMM_E_HIP.  Invalid device-resident values (negative sizes, a total
@@ -245,10 +249,18 @@ gmm_status gmm_widen_scales_run(gmm_handle* h, const gmm_tensor* src, const gmm_
  *                out must not overlap an input.
  *
  * Size limits: K % 8 == 0, N % 8 == 0, M*K*2 and M*N*2 below 2 GiB, Ga*K
- * below 2^31.  Outside them the call returns GMM_E_UNSUPPORTED and queues
- * nothing; shape or dtype inconsistencies return GMM_E_INVALID; a launch
- * failure returns GMM_E_HIP.  Invalid device-resident sizes or offset are
- * clamped and reported through gmm_device_flags, as for gmm_run.
+ * below 2^31, 256*N*(output element size) below 2 GiB.  Outside them the
+ * call returns GMM_E_UNSUPPORTED and queues nothing; shape or dtype
+ * inconsistencies return GMM_E_INVALID; a launch failure returns GMM_E_HIP
+ * (as does a failed allocation of a new stream's counters).  Invalid
+ * device-resident sizes or offset are clamped and reported through
+ * gmm_device_flags, as for gmm_run.
+ *
+ * Scheduling state: the kernel hands out its tiles from work-queue counters
+ * that the call's last workgroup resets.  The handle keeps one counter block
+ * per stream (allocated on the first call on that stream), so calls on one
+ * stream run one after another on their own counters and calls on different
+ * streams may overlap.
  */
 gmm_status gmm_tgmm_run(gmm_handle* h,
                         const gmm_tensor* lhs,
@@ -273,6 +285,17 @@ gmm_status gmm_device_flags(gmm_handle* h, void* stream, uint32_t* flags);
  * another value.  For tests and tuning.
  */
 gmm_status gmm_set_tile_policy(gmm_handle* h, int policy);
+
+/*
+ * gmm_set_grid_limit: launch at most `limit` workgroups for the gmm and tgmm
+ * kernels of later calls on h (0, the default, lets each kernel take its own
+ * count, normally one per compute unit).  Every kernel walks its output
+ * tiles with a grid stride, so the result does not change; with few
+ * workgroups each one runs many tiles back to back, carrying its operand
+ * pipeline from one tile into the next.  Returns GMM_E_INVALID for a
+ * negative limit.  For tests.
+ */
+gmm_status gmm_set_grid_limit(gmm_handle* h, int limit);
 
 /*
  * gmm_debug_worklist: run the device code that turns group_sizes and the

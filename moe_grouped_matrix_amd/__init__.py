@@ -5,8 +5,9 @@ libgmm.so (include/gmm.h); this package is the thin Python binding over it.
 Build the library with ``moe_grouped_matrix_amd.build.build()``."""
 from ._binding import (EXPORTED, FLAG_BAD_OFFSET, FLAG_NEGATIVE_SIZE, FLAG_SIZES_EXCEED_M,  # noqa: F401
                        LIB_PATH, GmmDeviceDataError, GmmError, GmmInvalid, GmmUnsupported,
-                       debug_worklist, device_flags, gmm, handle, load, quant_fp8, set_tile_policy, tgmm,
-                       widen_scales)
+                       debug_worklist, device_flags, gmm, handle, load, quant_fp8, set_grid_limit,
+                       set_tile_policy, tgmm, widen_scales)
 
-__all__ = ["gmm", "tgmm", "quant_fp8", "widen_scales", "device_flags", "debug_worklist", "set_tile_policy", "load", "handle",
-           "GmmError", "GmmInvalid", "GmmUnsupported", "GmmDeviceDataError", "LIB_PATH"]
+__all__ = ["gmm", "tgmm", "quant_fp8", "widen_scales", "device_flags", "debug_worklist", "set_tile_policy",
+           "set_grid_limit", "load", "handle", "GmmError", "GmmInvalid", "GmmUnsupported", "GmmDeviceDataError",
+           "LIB_PATH"]

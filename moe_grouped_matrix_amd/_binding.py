@@ -25,7 +25,7 @@ FLAG_NEGATIVE_SIZE, FLAG_SIZES_EXCEED_M, FLAG_BAD_OFFSET = 0x1, 0x2, 0x4
 
 EXPORTED = ("gmm_create", "gmm_destroy", "gmm_last_error", "gmm_run", "gmm_run_existing_out", "gmm_tgmm_run",
             "gmm_quant_fp8_run", "gmm_widen_scales_run", "gmm_device_flags", "gmm_set_tile_policy",
-            "gmm_debug_worklist")
+            "gmm_set_grid_limit", "gmm_debug_worklist")
 
 _DTYPE = {torch.float32: GMM_F32, torch.bfloat16: GMM_BF16,
           torch.float8_e4m3fn: GMM_F8E4M3FN, torch.float8_e5m2: GMM_F8E5M2, torch.int32: GMM_I32,
@@ -90,6 +90,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.gmm_device_flags.restype = ctypes.c_int
             lib.gmm_set_tile_policy.argtypes = [vp, ctypes.c_int]
             lib.gmm_set_tile_policy.restype = ctypes.c_int
+            lib.gmm_set_grid_limit.argtypes = [vp, ctypes.c_int]
+            lib.gmm_set_grid_limit.restype = ctypes.c_int
             lib.gmm_debug_worklist.argtypes = [vp, tp, vp, i64, i64, i32, vp, i64, vp, vp]
             lib.gmm_debug_worklist.restype = ctypes.c_int
             _lib = lib
@@ -317,6 +319,14 @@ def set_tile_policy(policy: int, device=None) -> None:
     lib = load()
     h = handle(device)
     _raise(lib.gmm_set_tile_policy(h, int(policy)), h)
+
+
+def set_grid_limit(limit: int, device=None) -> None:
+    """At most `limit` workgroups per gmm / tgmm launch (0 = the kernel's
+    own choice); a test hook that makes each workgroup run many tiles."""
+    lib = load()
+    h = handle(device)
+    _raise(lib.gmm_set_grid_limit(h, int(limit)), h)
 
 
 def debug_worklist(group_sizes: torch.Tensor, num_active: int, M: int, tm: int,

@@ -9,21 +9,26 @@
 
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <string>
 
 #include "gmm.h"
 #include "gmm_launch.hpp"
 
-constexpr size_t kDeviceBlock = 128;
-static_assert(16 + 2 * gmmk::kQueues * sizeof(int32_t) <= kDeviceBlock, "device block");
+constexpr size_t kDeviceBlock = 16;  // the data-error flag word
+constexpr size_t kQueueBlock = 2 * gmmk::kQueues * sizeof(int32_t);
 
 struct gmm_handle {
   int device = 0;
   int cu_count = 0;
-  // device block: the data-error flag word at byte 0, the transposed
-  // product's work-queue counters (2 * kQueues int32) from byte 16
-  uint32_t* flags = nullptr;
+  uint32_t* flags = nullptr;  // device word of data-error flags (kDeviceBlock bytes)
+  // the transposed product's work-queue counters (2 * kQueues int32, zero
+  // between calls), one block per stream: calls on one stream run in order,
+  // so each call finds its stream's counters reset by the previous one;
+  // calls on different streams never share counters
+  std::map<void*, int32_t*> queues;
   int tile_policy = 0;        // 0 auto, 1 small tiles, 2 big tiles
+  int grid_limit = 0;         // > 0: at most this many workgroups per launch
   std::string err;
 };
 
@@ -125,7 +130,9 @@ gmm_status gmm_destroy(gmm_handle* h) {
   if (!h) return GMM_OK;
   {
     DeviceGuard g(h->device);
+    // work queued on the handle's streams must not outlive the handle
     if (h->flags) (void)hipFree(h->flags);
+    for (auto& kv : h->queues) (void)hipFree(kv.second);
   }
   delete h;
   return GMM_OK;
@@ -139,6 +146,16 @@ const char* gmm_last_error(const gmm_handle* h) { return h ? h->err.c_str() : "n
 gmm_status gmm_set_tile_policy(gmm_handle* h, int policy) {
   if (!h || policy < 0 || policy > 2) return GMM_E_INVALID;
   h->tile_policy = policy;
+  return GMM_OK;
+}
+
+// Test hook: at most `limit` workgroups per launch of the gmm and tgmm
+// kernels (0 = as many as the kernel's own choice).  Every kernel walks its
+// tiles with a grid stride, so the result is unchanged; with few workgroups
+// each one runs many tiles back to back.
+gmm_status gmm_set_grid_limit(gmm_handle* h, int limit) {
+  if (!h || limit < 0) return GMM_E_INVALID;
+  h->grid_limit = limit;
   return GMM_OK;
 }
 
@@ -243,6 +260,9 @@ gmm_status run_gmm(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs, 
   const long long wbytes = four_bit(rd) ? K * N / 2 : K * N * elem_size(rd);
   if (wbytes >= 0x7FFFFFF0LL || 256LL * K * elem_size(ld) >= 0x7FFFFFF0LL)
     return fail(h, GMM_E_UNSUPPORTED, "one group's weight (or a 256-row lhs tile) exceeds 2 GiB");
+  // the epilogues address a 256-row output tile with 32-bit byte offsets
+  if (256LL * N * elem_size(out->dtype) >= 0x7FFFFFF0LL)
+    return fail(h, GMM_E_UNSUPPORTED, "a 256-row output tile exceeds 2 GiB");
 
   const gmm_tensor* ins[] = {lhs, rhs, group_sizes, rhs_scale, rhs_bias, lhs_scale};
   for (const gmm_tensor* t : ins) {
@@ -271,6 +291,7 @@ gmm_status run_gmm(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs, 
   }
   if (M == 0) return GMM_OK;
 
+  kc.grid_cap = h->grid_limit;
   if (h->tile_policy == 1)
     kc.size = gmmk::SizeClass::Small;
   else if (h->tile_policy == 2)
@@ -423,6 +444,9 @@ gmm_status gmm_tgmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* 
   if (K % 8 || N % 8) return fail(h, GMM_E_UNSUPPORTED, "K and N must be multiples of 8");
   if (M * K * 2 >= 0x7FFFFFF0LL || M * N * 2 >= 0x7FFFFFF0LL || Ga * K >= (1LL << 31))
     return fail(h, GMM_E_UNSUPPORTED, "an operand beyond 2 GiB or Ga*K beyond 2^31");
+  // the epilogue addresses a 256-row output tile with 32-bit byte offsets
+  if (256LL * N * elem_size(out->dtype) >= 0x7FFFFFF0LL)
+    return fail(h, GMM_E_UNSUPPORTED, "a 256-row output tile exceeds 2 GiB");
   const gmm_tensor* ins[] = {lhs, rhs, group_sizes};
   for (const gmm_tensor* t : ins) {
     if (numel(t) > 0 && !t->data) return fail(h, GMM_E_INVALID, "null data pointer");
@@ -434,6 +458,15 @@ gmm_status gmm_tgmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* 
     return fail(h, GMM_E_INVALID, "out and group_offset must be 16-byte aligned");
   if (Ga == 0) return GMM_OK;
 
+  DeviceGuard g(h->device);
+  int32_t*& queue = h->queues[stream];
+  if (!queue) {  // first call on this stream: its counters, zeroed
+    if (hipMalloc(&queue, kQueueBlock) != hipSuccess || hipMemset(queue, 0, kQueueBlock) != hipSuccess) {
+      if (queue) (void)hipFree(queue);
+      h->queues.erase(stream);
+      return fail(h, GMM_E_HIP, "allocating the work-queue counters failed");
+    }
+  }
   gmmk::Params p{};
   p.lhs = lhs->data;
   p.rhs = rhs->data;
@@ -441,7 +474,7 @@ gmm_status gmm_tgmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* 
   p.group_offset = group_offset;
   p.out = const_cast<void*>(out->data);
   p.flags = h->flags;
-  p.queue = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(h->flags) + 16);
+  p.queue = queue;
   p.M = (int32_t)M;
   p.K = (int32_t)K;
   p.N = (int32_t)N;
@@ -450,8 +483,7 @@ gmm_status gmm_tgmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* 
   p.nb = 1;
   p.blk = (int32_t)K;
   p.out_f32 = out->dtype == GMM_F32;
-  DeviceGuard g(h->device);
-  hipError_t e = gmmk::launch_tgmm(p, h->cu_count, static_cast<hipStream_t>(stream));
+  hipError_t e = gmmk::launch_tgmm(p, h->cu_count, h->grid_limit, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(h, GMM_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return GMM_OK;
 }

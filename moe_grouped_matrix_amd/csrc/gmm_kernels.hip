@@ -27,8 +27,13 @@ struct Pick<OP, NN, BF8, SC, SizeClass::Small, FMT> {
   using type = Cfg<OP, NN, BF8, 32, 64, 1, 4, SC, FMT>;
 };
 
+// Every kernel below walks its work items with a grid stride, so any grid
+// size is correct; a positive cap (a test hook) makes each workgroup run
+// many tiles, with the operand streams carried from one tile to the next.
+inline long long apply_cap(long long grid, int cap) { return cap > 0 && grid > cap ? cap : grid; }
+
 template <class C>
-hipError_t launch_cfg(const Params& p, int cu_count, hipStream_t stream) {
+hipError_t launch_cfg(const Params& p, int cu_count, int cap, hipStream_t stream) {
   static std::atomic<int> occ_cache{0};
   int occ = occ_cache.load();
   if (occ <= 0) {
@@ -48,24 +53,26 @@ hipError_t launch_cfg(const Params& p, int cu_count, hipStream_t stream) {
   if (grid > bound) grid = bound;
   if (grid >= 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
+  grid = apply_cap(grid, cap);
   hipLaunchKernelGGL(gmm_kernel<C>, dim3((unsigned)grid), dim3(C::T), 0, stream, p);
   return hipGetLastError();
 }
 
 template <class C>
-hipError_t launch_big(const Params& p, int cu_count, hipStream_t stream) {
+hipError_t launch_big(const Params& p, int cu_count, int cap, hipStream_t stream) {
   const long long n_tiles = (p.N + C::BN - 1) / C::BN;
   const long long m_tiles = (p.M + C::BM - 1) / C::BM + p.Ga;
   long long grid = cu_count;  // one workgroup per CU (LDS-bound)
   if (grid > m_tiles * n_tiles && m_tiles * n_tiles >= 8) grid = m_tiles * n_tiles;
   if (grid >= 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
+  grid = apply_cap(grid, cap);
   hipLaunchKernelGGL(gmm_big_kernel<C>, dim3((unsigned)grid), dim3(C::T), 0, stream, p);
   return hipGetLastError();
 }
 
 template <class C>
-hipError_t launch_stream(const Params& p, int cu_count, hipStream_t stream) {
+hipError_t launch_stream(const Params& p, int cu_count, int cap, hipStream_t stream) {
   // One workgroup per CU (LDS-bound), even when there are fewer tiles:
   // workgroups without a tile still take their share of the rows outside
   // the active groups, which can be most of the output (an expert shard of
@@ -73,6 +80,7 @@ hipError_t launch_stream(const Params& p, int cu_count, hipStream_t stream) {
   long long grid = cu_count;
   if (grid >= 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
+  grid = apply_cap(grid, cap);
   hipLaunchKernelGGL(gmm_stream_kernel<C>, dim3((unsigned)grid), dim3(C::T), 0, stream, p);
   return hipGetLastError();
 }
@@ -80,7 +88,7 @@ hipError_t launch_stream(const Params& p, int cu_count, hipStream_t stream) {
 // The block-scaled fp8 x fp8 ring kernel: one workgroup per CU (its ring
 // takes most of the LDS), at most one per work item.
 template <class C>
-hipError_t launch_w8a8(const Params& p, int cu_count, hipStream_t stream) {
+hipError_t launch_w8a8(const Params& p, int cu_count, int cap, hipStream_t stream) {
   const long long n_tiles = (p.N + C::BN - 1) / C::BN;
   const long long m_tiles = (p.M + C::BM - 1) / C::BM + p.Ga;
   const long long row_bytes = (long long)p.N * (p.out_f32 ? 4 : 2);
@@ -90,6 +98,7 @@ hipError_t launch_w8a8(const Params& p, int cu_count, hipStream_t stream) {
   if (grid > bound) grid = bound;
   if (grid >= 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
+  grid = apply_cap(grid, cap);
   hipLaunchKernelGGL(gmm_w8a8_kernel<C>, dim3((unsigned)grid), dim3(C::T), 0, stream, p);
   return hipGetLastError();
 }
@@ -104,48 +113,51 @@ inline bool stream_fits(const Params& p) {
 
 // One workgroup per CU (LDS-bound), at most one per tile.
 template <class C>
-hipError_t launch_tgmm_cfg(const Params& p, int cu_count, hipStream_t stream) {
+hipError_t launch_tgmm_cfg(const Params& p, int cu_count, int cap, hipStream_t stream) {
   const long long items = (long long)p.Ga * ((p.K + C::BM - 1) / C::BM) * ((p.N + C::BN - 1) / C::BN);
   long long grid = cu_count;
   if (grid > items && items >= 8) grid = items;
   if (grid >= 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
+  grid = apply_cap(grid, cap);
   hipLaunchKernelGGL(gmm_tgmm_kernel<C>, dim3((unsigned)grid), dim3(C::T), 0, stream, p);
   return hipGetLastError();
 }
 
 // FMT: the fp8 formats (bit 0 lhs, bit 1 rhs; 0 e4m3fn, 1 e5m2).
 template <Op OP, bool NN, bool BF8, bool SC, int FMT>
-hipError_t by_size(const Params& p, SizeClass sz, int cu, hipStream_t st) {
-  if constexpr (OP == Op::F32) return launch_cfg<Cfg<Op::F32, NN, false, 64, 64, 2, 2, SC>>(p, cu, st);
+hipError_t by_size(const Params& p, const KernelChoice& kc, int cu, hipStream_t st) {
+  const SizeClass sz = kc.size;
+  const int cap = kc.grid_cap;
+  if constexpr (OP == Op::F32) return launch_cfg<Cfg<Op::F32, NN, false, 64, 64, 2, 2, SC>>(p, cu, cap, st);
   if constexpr (OP == Op::BF16 && !BF8 && !SC) {
     // the big kernel runs a tile in five phases of K steps of 32: K >= 160
     if (sz == SizeClass::Big && p.K >= 5 * 32) {
       const bool bias = p.rhs_bias != nullptr;
       if (p.out_f32)
-        return bias ? launch_big<BigCfg<NN, true, true>>(p, cu, st) : launch_big<BigCfg<NN, true, false>>(p, cu, st);
-      return bias ? launch_big<BigCfg<NN, false, true>>(p, cu, st) : launch_big<BigCfg<NN, false, false>>(p, cu, st);
+        return bias ? launch_big<BigCfg<NN, true, true>>(p, cu, cap, st) : launch_big<BigCfg<NN, true, false>>(p, cu, cap, st);
+      return bias ? launch_big<BigCfg<NN, false, true>>(p, cu, cap, st) : launch_big<BigCfg<NN, false, false>>(p, cu, cap, st);
     }
   }
   if constexpr (OP == Op::BF16 && BF8 && !NN && (FMT >> 1) < 3) {  // one-byte weights
     if (sz == SizeClass::Small && stream_fits(p)) {
-      if (p.out_f32) return launch_stream<StreamCfg<true, (FMT >> 1)>>(p, cu, st);
-      return launch_stream<StreamCfg<false, (FMT >> 1)>>(p, cu, st);
+      if (p.out_f32) return launch_stream<StreamCfg<true, (FMT >> 1)>>(p, cu, cap, st);
+      return launch_stream<StreamCfg<false, (FMT >> 1)>>(p, cu, cap, st);
     }
   }
   if constexpr (OP == Op::FP8 && !NN && SC) {  // W8A8 with scale blocks of one K step
     using CB = typename Pick<OP, NN, BF8, SC, SizeClass::Big, FMT>::type;
-    if (sz == SizeClass::Big && p.blk == CB::BK) return launch_w8a8<CB>(p, cu, st);
+    if (sz == SizeClass::Big && p.blk == CB::BK) return launch_w8a8<CB>(p, cu, cap, st);
   }
   if (sz == SizeClass::Big)
-    return launch_cfg<typename Pick<OP, NN, BF8, SC, SizeClass::Big, FMT>::type>(p, cu, st);
-  return launch_cfg<typename Pick<OP, NN, BF8, SC, SizeClass::Small, FMT>::type>(p, cu, st);
+    return launch_cfg<typename Pick<OP, NN, BF8, SC, SizeClass::Big, FMT>::type>(p, cu, cap, st);
+  return launch_cfg<typename Pick<OP, NN, BF8, SC, SizeClass::Small, FMT>::type>(p, cu, cap, st);
 }
 
 template <Op OP, bool NN, bool BF8, int FMT = 0>
 hipError_t by_scaled(const Params& p, const KernelChoice& c, int cu, hipStream_t st) {
-  if (c.scaled) return by_size<OP, NN, BF8, true, FMT>(p, c.size, cu, st);
-  return by_size<OP, NN, BF8, false, FMT>(p, c.size, cu, st);
+  if (c.scaled) return by_size<OP, NN, BF8, true, FMT>(p, c, cu, st);
+  return by_size<OP, NN, BF8, false, FMT>(p, c, cu, st);
 }
 
 }  // namespace
@@ -193,9 +205,9 @@ hipError_t launch_gmm(const Params& p, const KernelChoice& c, int cu, hipStream_
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_tgmm(const Params& p, int cu, hipStream_t st) {
-  if (p.out_f32) return launch_tgmm_cfg<TgCfg<true>>(p, cu, st);
-  return launch_tgmm_cfg<TgCfg<false>>(p, cu, st);
+hipError_t launch_tgmm(const Params& p, int cu, int cap, hipStream_t st) {
+  if (p.out_f32) return launch_tgmm_cfg<TgCfg<true>>(p, cu, cap, st);
+  return launch_tgmm_cfg<TgCfg<false>>(p, cu, cap, st);
 }
 
 hipError_t launch_worklist(const Params& p, int tm, int32_t* tiles, long long capacity,

@@ -18,6 +18,7 @@ struct KernelChoice {
                 // widened weights 2 int8, 3 int4, 4 uint4, 5 fp4 e2m1)
   bool scaled;  // rhs_scale and/or lhs_scale present
   SizeClass size;
+  int grid_cap;  // > 0: at most this many workgroups (a test hook)
 };
 
 // K elements of one K tile for an operand type (the K granularity).
@@ -33,8 +34,9 @@ int tile_m(const KernelChoice& c);
 // Queue the gmm kernel.  Returns hipSuccess or the launch error.
 hipError_t launch_gmm(const Params& p, const KernelChoice& c, int cu_count, hipStream_t stream);
 
-// Queue the transposed grouped matmul (out [Ga,K,N]).
-hipError_t launch_tgmm(const Params& p, int cu_count, hipStream_t stream);
+// Queue the transposed grouped matmul (out [Ga,K,N]); grid_cap > 0 limits
+// the workgroups.
+hipError_t launch_tgmm(const Params& p, int cu_count, int grid_cap, hipStream_t stream);
 
 // Activation quantiser arguments: x bf16 [M,K], q e4m3fn [M,K], scale f32
 // [M,K/128], blocks = M * K / 128 (K % 128 == 0).

@@ -24,9 +24,9 @@
 // same number of contraction steps (each to the least-loaded queue), and the
 // workgroups of an XCD take their queue's tiles in order with an atomic
 // counter, so a group's tiles share that XCD's L2 and the long contractions
-// are spread first, the short ones filling in behind.  The counters live in
-// the handle's device memory; the last workgroup of a queue to finish
-// resets its counters for the next call.
+// are spread first, the short ones filling in behind.  The counters are the
+// caller's (Params::queue: a block of the handle's per stream); the last
+// workgroup of a queue to finish resets its counters for the next call.
 #pragma once
 
 #include "gmm_big.hpp"

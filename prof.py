@@ -1,12 +1,12 @@
 """Profiling helpers for the benchmark: a plain copy kernel of known size
 (to calibrate the HBM byte counters), and summaries of rocprofv3 output.
 
-  python -m moe_grouped_matrix_amd.prof copy [--mib 1024] [--reps 5]
+  python prof.py copy [--mib 1024] [--reps 5]
       an elementwise copy (int8 negation) of a known number of bytes, run under
       rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) for the scale factor
-  python -m moe_grouped_matrix_amd.prof trace DIR [--out FILE] [--cmd "..."]
+  python prof.py trace DIR [--out FILE] [--cmd "..."]
       markdown table of a rocprofv3 --kernel-trace --stats directory
-  python -m moe_grouped_matrix_amd.prof traffic --workload NAME --kernel SUBSTR
+  python prof.py traffic --workload NAME --kernel SUBSTR
       --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR [--copy-mib 1024]
       HBM bytes per launch of the kernel (FETCH_SIZE + WRITE_SIZE, each
       scaled by what the counter reads for the copy), recorded in
@@ -22,7 +22,7 @@ import os
 import statistics
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
 def _csvs(d: str, pattern: str):

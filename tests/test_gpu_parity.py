@@ -169,20 +169,20 @@ def test_scaled_exact_inputs_are_bit_exact(path, tile_policy):
     """Power-of-two block scales, per-row scales and a bias keep the integer
     arithmetic exact: bit-exact against the oracle."""
     ld, rd, T, kg = path
-    if T:
-        pytest.skip("scaled NN uses the same fold as NT; covered by the NT paths")
     g = torch.Generator().manual_seed(2)
     sizes = [40, 0, 90, 3]
     nb = 3
     M, K, N = sum(sizes) + 5, nb * (128 if kg == 128 else 2 * kg), 72
     lhs = torch.randint(-3, 4, (M, K), generator=g).to(torch.float32).to(ld)
-    rhs = torch.randint(-3, 4, (len(sizes), N, K), generator=g).to(torch.float32).to(rd)
+    shape = (len(sizes), K, N) if T else (len(sizes), N, K)
+    rhs = torch.randint(-3, 4, shape, generator=g).to(torch.float32).to(rd)
     rs = 2.0 ** torch.randint(-3, 4, (len(sizes), nb, 1, N), generator=g).to(torch.float32)
     ls = 2.0 ** torch.randint(-2, 3, (M, nb), generator=g).to(torch.float32)
     bias = torch.randint(-8, 9, (len(sizes), 1, N), generator=g).to(torch.bfloat16)
     for kw in (dict(rhs_scale=rs), dict(rhs_scale=rs, rhs_bias=bias), dict(lhs_scale=ls),
                dict(rhs_scale=rs, lhs_scale=ls, rhs_bias=bias)):
-        case = _case(lhs, rhs, sizes, out_dtype=torch.float32, **kw)
+        print(f"scaled {list(kw)} nn={T} policy {tile_policy}", flush=True)
+        case = _case(lhs, rhs, sizes, transpose_rhs=T, out_dtype=torch.float32, **kw)
         out = run_gpu(case).cpu()
         assert torch.equal(out, oracle.round_to(reference(case), torch.float32)), list(kw)
 
@@ -390,3 +390,44 @@ def test_weight_streaming_kernel(tokens, K, N, out_dtype, bias, scaled):
     ref = reference(case)
     compare(out.cpu()[lo:hi], ref[lo:hi], out_dtype, f"stream K={K} N={N}")
     assert m.device_flags() == 0
+
+
+def _fake(shape, dtype, addr=1 << 20):
+    """A tensor view that is never dereferenced: the host rejects the call
+    before anything is queued."""
+    import moe_grouped_matrix_amd._binding as b
+    v = b.GmmTensor()
+    v.data = addr
+    v.dtype = dtype
+    v.ndim = len(shape)
+    for i, s in enumerate(shape):
+        v.shape[i] = s
+    return v
+
+
+def test_output_tile_beyond_32bit_offsets_is_unsupported():
+    """The epilogues address a 256-row output tile with 32-bit byte offsets:
+    gmm_run and gmm_tgmm_run reject an N whose 256-row output tile reaches
+    2 GiB (checked on the host; nothing is launched)."""
+    import ctypes
+
+    import moe_grouped_matrix_amd._binding as b
+    lib, h = b.load(), b.handle(0)
+    K = 64
+    for out_dtype, N in ((b.GMM_F32, 2_097_152), (b.GMM_BF16, 4_194_304)):
+        lhs, rhs = _fake((1, K), b.GMM_BF16), _fake((1, N, K), b.GMM_BF16)
+        gs, out = _fake((1,), b.GMM_I32), _fake((1, N), out_dtype)
+        st = lib.gmm_run(h, ctypes.byref(lhs), ctypes.byref(rhs), ctypes.byref(gs), None, None, None, None, 0,
+                         ctypes.byref(out), None)
+        assert st == b.GMM_E_UNSUPPORTED and b"output tile" in lib.gmm_last_error(h), (out_dtype, N)
+        tl, tr, tout = _fake((16, K), b.GMM_BF16), _fake((16, N), b.GMM_BF16), _fake((1, K, N), out_dtype)
+        st = lib.gmm_tgmm_run(h, ctypes.byref(tl), ctypes.byref(tr), ctypes.byref(gs), None, ctypes.byref(tout),
+                              None)
+        assert st == b.GMM_E_UNSUPPORTED and b"output tile" in lib.gmm_last_error(h), (out_dtype, N)
+    # one column less than the limit passes the check (and then fails on the
+    # overlap of the fake tensors, still before anything is queued)
+    lhs, rhs = _fake((1, K), b.GMM_BF16), _fake((1, 4_194_296, K), b.GMM_BF16)
+    gs, out = _fake((1,), b.GMM_I32), _fake((1, 4_194_296), b.GMM_BF16)
+    st = lib.gmm_run(h, ctypes.byref(lhs), ctypes.byref(rhs), ctypes.byref(gs), None, None, None, None, 0,
+                     ctypes.byref(out), None)
+    assert st == b.GMM_E_INVALID and b"overlap" in lib.gmm_last_error(h)
