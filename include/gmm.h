@@ -271,6 +271,33 @@ gmm_status gmm_tgmm_run(gmm_handle* h,
                         void* stream);
 
 /*
+ * gmm_tgmm_run_noalloc: gmm_tgmm_run for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The same kernel and result (bit for bit); the
+ * work-queue counters live in the library's static device scratch instead
+ * of a per-stream block of the handle, so the call never allocates, also on
+ * a stream the handle has not seen.  The handle must exist (gmm_create,
+ * which looks the scratch up once per device, is the only allocating call).
+ *
+ *   Arguments, limits and errors are those of gmm_tgmm_run.  The scratch is
+ *   256 bytes per device, held until the process ends; the counters use 64
+ *   of them for every problem size, so no size is rejected for want of
+ *   scratch.  Each call first clears the counters on `stream` (a one-
+ *   workgroup kernel) and then queues the tgmm kernel.
+ *
+ *   All calls on one device share that device's scratch: two calls that
+ *   overlap in time on one GPU (different streams, or several host threads)
+ *   race on the counters and give wrong results.  Serialise them.
+ */
+gmm_status gmm_tgmm_run_noalloc(gmm_handle* h,
+                                const gmm_tensor* lhs,
+                                const gmm_tensor* rhs,
+                                const gmm_tensor* group_sizes,
+                                const int32_t* group_offset,
+                                const gmm_tensor* out,
+                                void* stream);
+
+/*
  * gmm_device_flags: synchronise `stream`, return the GMM_FLAG_* bits that
  * runs on this handle have set since the last call, and clear them.
  * Returns GMM_E_DEVICE_DATA when any bit was set, GMM_OK otherwise.

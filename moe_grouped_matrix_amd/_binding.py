@@ -24,6 +24,7 @@ GMM_OK, GMM_E_INVALID, GMM_E_UNSUPPORTED, GMM_E_HIP, GMM_E_DEVICE_DATA = 0, -1, 
 FLAG_NEGATIVE_SIZE, FLAG_SIZES_EXCEED_M, FLAG_BAD_OFFSET = 0x1, 0x2, 0x4
 
 EXPORTED = ("gmm_create", "gmm_destroy", "gmm_last_error", "gmm_run", "gmm_run_existing_out", "gmm_tgmm_run",
+            "gmm_tgmm_run_noalloc",
             "gmm_quant_fp8_run", "gmm_widen_scales_run", "gmm_device_flags", "gmm_set_tile_policy",
             "gmm_set_grid_limit", "gmm_debug_worklist")
 
@@ -86,6 +87,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.gmm_quant_fp8_run.restype = ctypes.c_int
             lib.gmm_tgmm_run.argtypes = [vp, tp, tp, tp, vp, tp, vp]
             lib.gmm_tgmm_run.restype = ctypes.c_int
+            lib.gmm_tgmm_run_noalloc.argtypes = [vp, tp, tp, tp, vp, tp, vp]
+            lib.gmm_tgmm_run_noalloc.restype = ctypes.c_int
             lib.gmm_device_flags.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
             lib.gmm_device_flags.restype = ctypes.c_int
             lib.gmm_set_tile_policy.argtypes = [vp, ctypes.c_int]
@@ -275,6 +278,7 @@ def tgmm(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,
          out_dtype: torch.dtype = torch.float32,
          group_offset=None,
          out: Optional[torch.Tensor] = None,
+         no_alloc: bool = False,
          stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
     """Transposed grouped matmul (the weight gradient of gmm) through
     libgmm.so: out[h] = lhs_g^T . rhs_g over the rows of group g = s + h,
@@ -282,7 +286,11 @@ def tgmm(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,
 
     lhs [M,K] and rhs [M,N] bf16; group_sizes int32 [G] on the device;
     num_active Ga defaults to G minus an integer group_offset (or to G when
-    the offset is a device tensor).  Returns out [Ga,K,N] of out_dtype."""
+    the offset is a device tensor).  Returns out [Ga,K,N] of out_dtype.
+    no_alloc=True calls gmm_tgmm_run_noalloc (the library's static scratch
+    instead of a per-stream counter block; calls on one GPU must not
+    overlap); pass `out` (and a tensor group_offset) to keep the call free of
+    torch allocations too."""
     lib = load()
     dev = lhs.device
     h = handle(dev)
@@ -294,8 +302,8 @@ def tgmm(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,
     views = [_view(t, n) for t, n in ((lhs, "lhs"), (rhs, "rhs"), (group_sizes, "group_sizes"), (out, "out"))]
     off_ptr, keep = _offset_ptr(group_offset, dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev)
-    status = lib.gmm_tgmm_run(h, *[_ref(v) for v in views[:3]], off_ptr, _ref(views[3]),
-                              ctypes.c_void_p(st.cuda_stream))
+    fn = lib.gmm_tgmm_run_noalloc if no_alloc else lib.gmm_tgmm_run
+    status = fn(h, *[_ref(v) for v in views[:3]], off_ptr, _ref(views[3]), ctypes.c_void_p(st.cuda_stream))
     if keep is not None and status == GMM_OK:
         keep.record_stream(st)
     _raise(status, h)

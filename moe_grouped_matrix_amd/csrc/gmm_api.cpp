@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 
 #include "gmm.h"
@@ -29,8 +30,14 @@ struct gmm_handle {
   std::map<void*, int32_t*> queues;
   int tile_policy = 0;        // 0 auto, 1 small tiles, 2 big tiles
   int grid_limit = 0;         // > 0: at most this many workgroups per launch
+  void* scratch = nullptr;    // device address of the device's static scratch
   std::string err;
 };
+
+// Device addresses of the static scratch (gmmk::static_scratch_address), one
+// per device, looked up by the first gmm_create on that device.
+static std::mutex g_scratch_mu;
+static std::map<int, void*> g_scratch;
 
 namespace {
 
@@ -121,6 +128,20 @@ gmm_status gmm_create(gmm_handle** out, int device) {
     (void)hipFree(h->flags);
     delete h;
     return GMM_E_HIP;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch.find(device);
+    if (it == g_scratch.end()) {
+      void* ptr = nullptr;
+      if (gmmk::static_scratch_address(&ptr) != hipSuccess || !ptr) {
+        (void)hipFree(h->flags);
+        delete h;
+        return GMM_E_HIP;
+      }
+      it = g_scratch.emplace(device, ptr).first;
+    }
+    h->scratch = it->second;
   }
   *out = h;
   return GMM_OK;
@@ -415,9 +436,12 @@ gmm_status gmm_quant_fp8_run(gmm_handle* h, const gmm_tensor* x, const gmm_tenso
   return GMM_OK;
 }
 
-gmm_status gmm_tgmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs,
-                        const gmm_tensor* group_sizes, const int32_t* group_offset, const gmm_tensor* out,
-                        void* stream) {
+// The transposed product: validation, then the launch with the work-queue
+// counters of the handle's block for this stream, or (no_alloc) of the
+// device's static scratch, cleared first.
+static gmm_status run_tgmm(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs,
+                           const gmm_tensor* group_sizes, const int32_t* group_offset, const gmm_tensor* out,
+                           void* stream, bool no_alloc) {
   if (!h) return GMM_E_INVALID;
   h->err.clear();
   if (!lhs || !rhs || !group_sizes || !out) return fail(h, GMM_E_INVALID, "lhs, rhs, group_sizes and out are required");
@@ -459,13 +483,24 @@ gmm_status gmm_tgmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* 
   if (Ga == 0) return GMM_OK;
 
   DeviceGuard g(h->device);
-  int32_t*& queue = h->queues[stream];
-  if (!queue) {  // first call on this stream: its counters, zeroed
-    if (hipMalloc(&queue, kQueueBlock) != hipSuccess || hipMemset(queue, 0, kQueueBlock) != hipSuccess) {
-      if (queue) (void)hipFree(queue);
-      h->queues.erase(stream);
-      return fail(h, GMM_E_HIP, "allocating the work-queue counters failed");
+  int32_t* queue = nullptr;
+  if (no_alloc) {
+    // the device's scratch keeps the last call's contents: clear the
+    // counters in stream order (a kernel, not a memset)
+    queue = static_cast<int32_t*>(h->scratch);
+    hipError_t e = gmmk::launch_clear_ints(queue, (int)(kQueueBlock / sizeof(int32_t)),
+                                           static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(h, GMM_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  } else {
+    int32_t*& q = h->queues[stream];
+    if (!q) {  // first call on this stream: its counters, zeroed
+      if (hipMalloc(&q, kQueueBlock) != hipSuccess || hipMemset(q, 0, kQueueBlock) != hipSuccess) {
+        if (q) (void)hipFree(q);
+        h->queues.erase(stream);
+        return fail(h, GMM_E_HIP, "allocating the work-queue counters failed");
+      }
     }
+    queue = q;
   }
   gmmk::Params p{};
   p.lhs = lhs->data;
@@ -486,6 +521,18 @@ gmm_status gmm_tgmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* 
   hipError_t e = gmmk::launch_tgmm(p, h->cu_count, h->grid_limit, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(h, GMM_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return GMM_OK;
+}
+
+gmm_status gmm_tgmm_run(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs,
+                        const gmm_tensor* group_sizes, const int32_t* group_offset, const gmm_tensor* out,
+                        void* stream) {
+  return run_tgmm(h, lhs, rhs, group_sizes, group_offset, out, stream, false);
+}
+
+gmm_status gmm_tgmm_run_noalloc(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs,
+                                const gmm_tensor* group_sizes, const int32_t* group_offset,
+                                const gmm_tensor* out, void* stream) {
+  return run_tgmm(h, lhs, rhs, group_sizes, group_offset, out, stream, true);
 }
 
 gmm_status gmm_device_flags(gmm_handle* h, void* stream, uint32_t* flags) {

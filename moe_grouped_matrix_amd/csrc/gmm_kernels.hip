@@ -11,6 +11,27 @@
 
 namespace gmmk {
 
+// The scratch of gmm_tgmm_run_noalloc (kStaticScratchBytes, zero at load).
+// Host code never passes `scratch` itself to a kernel: on the host the name
+// stands for a host-side shadow, not the device array.  The device address
+// comes from static_scratch_address, called once per device with that
+// device current.
+static __device__ __align__(256) int32_t scratch[kStaticScratchBytes / 4];
+
+hipError_t static_scratch_address(void** ptr) {
+  return hipGetSymbolAddress(ptr, HIP_SYMBOL(scratch));
+}
+
+__global__ void clear_ints_kernel(int32_t* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
+}
+
+hipError_t launch_clear_ints(int32_t* p, int n, hipStream_t stream) {
+  if (n < 0 || n > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(clear_ints_kernel, dim3(1), dim3(64), 0, stream, p, n);
+  return hipGetLastError();
+}
+
 namespace {
 
 // Tile shapes.  Big: 256 x 128 output tile, four waves of 128 x 64 (for

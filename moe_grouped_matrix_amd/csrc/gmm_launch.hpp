@@ -63,6 +63,18 @@ struct WidenParams {
 // Queue the block-scale widening (gmm_quant.hip).
 hipError_t launch_widen_scales(const WidenParams& p, int cu_count, hipStream_t stream);
 
+// Device scratch for callers that cannot allocate (gmm_tgmm_run_noalloc):
+// a file-scope array in gmm_kernels.hip, one copy per device, holding the
+// transposed product's work-queue counters.
+constexpr int kStaticScratchBytes = 256;
+static_assert(2 * kQueues * 4 <= kStaticScratchBytes, "work-queue counters fit the scratch");
+
+// The device address of the current device's scratch (hipGetSymbolAddress).
+hipError_t static_scratch_address(void** ptr);
+
+// Queue a one-workgroup kernel that writes n zero int32 at p (n <= 64).
+hipError_t launch_clear_ints(int32_t* p, int n, hipStream_t stream);
+
 // Queue the worklist export kernel (one workgroup).
 hipError_t launch_worklist(const Params& p, int tm, int32_t* tiles, long long capacity,
                            int32_t* count, hipStream_t stream);

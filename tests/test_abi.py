@@ -26,7 +26,7 @@ def lib_path():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["gmm_create", "gmm_destroy", "gmm_last_error", "gmm_run", "gmm_run_existing_out",
-                                  "gmm_tgmm_run", "gmm_quant_fp8_run", "gmm_widen_scales_run",
+                                  "gmm_tgmm_run", "gmm_tgmm_run_noalloc", "gmm_quant_fp8_run", "gmm_widen_scales_run",
                                   "gmm_device_flags", "gmm_set_tile_policy", "gmm_set_grid_limit",
                                   "gmm_debug_worklist"])
 
