@@ -311,6 +311,164 @@ class ClockSampler:
                 "socket_power_w": round(statistics.mean(pw)) if pw else None}
 
 
+def make_launcher(cases, dev, gmm_amd):
+    """Outputs for each case and launch(i), which queues case i's call on
+    the current stream."""
+    import torch
+
+    def out_of(c):
+        if is_quant(c):
+            return (torch.empty((c.M, c.K), dtype=torch.float8_e4m3fn, device=dev),
+                    torch.empty((c.M, c.K // c.block), dtype=torch.float32, device=dev))
+        shape = (c.num_active, c.K, c.N) if is_tgmm(c) else (c.M, c.N)
+        return torch.empty(shape, dtype=c.out_dtype, device=dev)
+
+    outs = [out_of(c) for c in cases]
+    offs = [torch.tensor([c.group_offset], dtype=torch.int32, device=dev) if getattr(c, "group_offset", 0) else None
+            for c in cases]
+
+    def launch(i):
+        c = cases[i]
+        if is_quant(c):
+            gmm_amd.quant_fp8(c.x, q=outs[i][0], scale=outs[i][1])
+            return
+        if is_tgmm(c):
+            gmm_amd.tgmm(c.lhs, c.rhs, c.group_sizes, num_active=c.num_active, group_offset=offs[i], out=outs[i])
+            return
+        gmm_amd.gmm(c.lhs, c.rhs, c.group_sizes, rhs_scale=c.rhs_scale, rhs_bias=c.rhs_bias,
+                    lhs_scale=c.lhs_scale, group_offset=offs[i], transpose_rhs=c.transpose_rhs,
+                    out=outs[i])
+
+    return launch, outs
+
+
+class Evictor:
+    """Reads 512 MB (twice the Infinity Cache) between timed calls, outside
+    the events: a write would leave the caches full of dirty lines whose
+    write-back the timed kernel then pays."""
+
+    def __init__(self, dev):
+        import torch
+        self.scratch = torch.ones(512 << 18, dtype=torch.float32, device=dev)
+        self.sink = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        import torch
+        torch.sum(self.scratch, dim=0, keepdim=True, out=self.sink)
+
+
+def time_steps(fns, steps: int, warmup: int, evict=None):
+    """Run `steps` steps of the launches in fns (one after another) after
+    `warmup` untimed ones, with a HIP event pair on the launch stream around
+    every launch.  Returns (per-launch milliseconds [len(fns)][steps], wall
+    seconds of the timed steps, epoch seconds at their start)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    epoch0 = time.time()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for i, f in enumerate(fns):
+            if evict is not None:
+                evict()
+            ev[s][i][0].record(stream)
+            f()
+            ev[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)] for i in range(len(fns))], wall, epoch0
+
+
+def summarize(case, ms):
+    """Median / p10 / p90 of one case's launch times and its rates: TFLOP/s
+    and the fraction of the dtype's MFMA peak, algorithmic GB/s and the
+    fraction of HBM peak."""
+    med = statistics.median(ms)
+    qs = statistics.quantiles(ms, n=10) if len(ms) > 1 else [med] * 9
+    d = {"median_ms": med, "p10_ms": qs[0], "p90_ms": qs[-1], "launches": len(ms)}
+    gbs = case.algorithmic_bytes() / (med * 1e-3) / 1e9
+    if not is_quant(case):
+        kind, pk = op_peak(case)
+        tf = case.flops() / (med * 1e-3) / 1e12
+        d.update({"tflops": tf, "peak_tflops": pk, "peak_dtype": kind, "frac_peak": tf / pk})
+        if hasattr(case, "active_rows"):
+            d["active_rows"] = case.active_rows()
+    d.update({"gbs_algorithmic": gbs, "algorithmic_bytes": case.algorithmic_bytes(), "frac_hbm": gbs / HBM_PEAK_GBS})
+    d["bound"] = "hbm" if case.name in MEM_BOUND else "mfma"
+    return d
+
+
+# workloads bound by HBM bandwidth (their roofline is bytes)
+MEM_BOUND = {"decode_fp8w", "quant_fp8"}
+# the other configurations, timed after the headline steps of a default run,
+# each in its own protocol: (workload, timed calls, warm-up calls)
+DETAIL_WORKLOADS = (("decode_fp8w", 500, 5), ("tiny_fp32", 500, 5), ("w8a8_fp8", 20, 3),
+                    ("tgmm_bf16", 20, 3), ("quant_fp8", 20, 3))
+
+
+def detail_workload(name, steps, warmup, dev, gmm_amd):
+    import torch
+    cases = build_cases(name, dev)
+    launch, outs = make_launcher(cases, dev, gmm_amd)
+    evict = Evictor(dev) if name in EVICT else None
+    ms, _, _ = time_steps([lambda: launch(0)], steps, warmup, evict)
+    if gmm_amd.device_flags() != 0:
+        raise RuntimeError(f"{name}: device data flags set")
+    d = summarize(cases[0], ms[0])
+    d["evicted_caches"] = evict is not None
+    d["traffic"] = measured_traffic(name)
+    del cases, outs, evict
+    torch.cuda.empty_cache()
+    return d
+
+
+def speed_gate(fwd, dlhs, steps, warmup, gmm_amd):
+    """The transposed-RHS kernel's speed test on the MaxText PR page
+    "Megablox: transposed-RHS gmm_v2 kernel for the backward dlhs" (Tests;
+    Context: the wi and wo weight-transpose copies it removes): the backward
+    dlhs reading the forward weight in place (NN) against an explicit
+    transpose copy of the weight followed by the NT product on the copy, at
+    the wi shape (the up-projection's weight [128,1408,1408]; the forward's
+    activations stand in for its output gradient) and the wo shape (the
+    down-projection's dlhs workload).  The copy is timed on its own."""
+    import torch
+    res = {}
+    for tag, lhs, w, gs in (("wi", fwd.lhs, fwd.rhs, fwd.group_sizes), ("wo", dlhs.lhs, dlhs.rhs, dlhs.group_sizes)):
+        # W as the forward stores it: the dlhs contracts its dim 1 (NN)
+        M, Kc, Nc = lhs.shape[0], w.shape[1], w.shape[2]
+        out_nn = torch.empty((M, Nc), dtype=torch.bfloat16, device=lhs.device)
+        out_nt = torch.empty_like(out_nn)
+        wt = torch.empty((w.shape[0], Nc, Kc), dtype=w.dtype, device=w.device)
+
+        def nn():
+            gmm_amd.gmm(lhs, w, gs, transpose_rhs=True, out=out_nn)
+
+        def copy():
+            wt.copy_(w.transpose(1, 2))
+
+        def nt():
+            gmm_amd.gmm(lhs, wt, gs, transpose_rhs=False, out=out_nt)
+
+        ms, _, _ = time_steps([nn, copy, nt], steps, warmup)
+        med = [statistics.median(x) for x in ms]
+        torch.cuda.synchronize()
+        res[tag] = {"weight": list(w.shape), "dlhs": [M, Nc],
+                    "nn_in_place_ms": med[0], "transpose_copy_ms": med[1], "nt_on_copy_ms": med[2],
+                    "copy_plus_nt_ms": med[1] + med[2], "speedup_vs_copy_plus_nt": (med[1] + med[2]) / med[0],
+                    "copy_bytes": 2 * w.numel() * w.element_size(),
+                    "copy_gbs": 2 * w.numel() * w.element_size() / (med[1] * 1e-3) / 1e9,
+                    "nn_equals_nt_bitwise": bool(torch.equal(out_nn, out_nt))}
+        del out_nn, out_nt, wt
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -322,6 +480,8 @@ def main():
                          "decode_fp8w, w8a8_fp8, tgmm_bf16 (the weight gradient), "
                          "quant_fp8 (the activation quantiser)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-detail", action="store_true",
+                    help="default workload only: skip the other configurations and the speed gate")
     args = ap.parse_args()
     if args.steps is None:
         args.steps = 500 if args.workload in ("tiny_fp32", "decode_fp8w") else 50
@@ -342,71 +502,25 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     cases = build_cases(args.workload, dev)
-    def out_of(c):
-        if is_quant(c):
-            return (torch.empty((c.M, c.K), dtype=torch.float8_e4m3fn, device=dev),
-                    torch.empty((c.M, c.K // c.block), dtype=torch.float32, device=dev))
-        shape = (c.num_active, c.K, c.N) if is_tgmm(c) else (c.M, c.N)
-        return torch.empty(shape, dtype=c.out_dtype, device=dev)
+    launch, outs = make_launcher(cases, dev, gmm_amd)
+    fns = [(lambda i=i: launch(i)) for i in range(len(cases))]
 
-    outs = [out_of(c) for c in cases]
-    offs = [torch.tensor([c.group_offset], dtype=torch.int32, device=dev) if getattr(c, "group_offset", 0) else None
-            for c in cases]
-    stream = torch.cuda.current_stream(dev)
-
-    def launch(i):
-        c = cases[i]
-        if is_quant(c):
-            gmm_amd.quant_fp8(c.x, q=outs[i][0], scale=outs[i][1])
-            return
-        if is_tgmm(c):
-            gmm_amd.tgmm(c.lhs, c.rhs, c.group_sizes, num_active=c.num_active, group_offset=offs[i], out=outs[i])
-            return
-        gmm_amd.gmm(c.lhs, c.rhs, c.group_sizes, rhs_scale=c.rhs_scale, rhs_bias=c.rhs_bias,
-                    lhs_scale=c.lhs_scale, group_offset=offs[i], transpose_rhs=c.transpose_rhs,
-                    out=outs[i])
-
-    for _ in range(args.warmup):
-        for i in range(len(cases)):
-            launch(i)
-    torch.cuda.synchronize()
+    evict = Evictor(dev) if args.workload in EVICT else None
+    per_kernel_ms, wall, epoch0 = time_steps(fns, args.steps, args.warmup, evict)
     if gmm_amd.device_flags() != 0:
         raise RuntimeError("device data flags set")
-
-    # HIP events around every launch of the timed steps, on the launch stream.
-    evict = args.workload in EVICT
-    # eviction reads 512 MB (twice the Infinity Cache): a write would leave the
-    # caches full of dirty lines whose write-back the timed kernel then pays
-    scratch = torch.ones(512 << 18, dtype=torch.float32, device=dev) if evict else None
-    sink = torch.empty(1, dtype=torch.float32, device=dev) if evict else None
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in cases] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    epoch0 = time.time()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        for i in range(len(cases)):
-            if evict:
-                torch.sum(scratch, dim=0, keepdim=True, out=sink)
-            ev[s][i][0].record(stream)
-            launch(i)
-            ev[s][i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     # the timed steps are too short for the clock sampler (about one reading
     # a second): the same steps keep running, untimed, for a few seconds and
     # the readings over both spans describe the clock under this load
     epoch1 = time.time()
     if clock.proc is not None:
         while time.time() - epoch1 < 3.0:
-            for i in range(len(cases)):
-                launch(i)
+            for f in fns:
+                f()
             torch.cuda.synchronize()
         epoch1 = time.time()
     clock.stop()
 
-    per_kernel_ms = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
-                     for i in range(len(cases))]
     flops = [c.flops() for c in cases]
     step_flops = sum(flops)
     # with eviction between calls the wall clock includes the scratch reads:
@@ -425,8 +539,7 @@ def main():
     dc = cases[d]
     avg_ms = statistics.mean(per_kernel_ms[d])
     kind, peak = op_peak(dc)
-    mem_bound = dc.name in ("decode_fp8w", "quant_fp8")
-    if mem_bound:
+    if dc.name in MEM_BOUND:
         achieved = dc.algorithmic_bytes() / (avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
@@ -444,16 +557,9 @@ def main():
         clk["frac_of_peak_at_sclk"] = roof["frac"] * 2400.0 / clk["sclk_mhz"] if roof["bound"] == "mfma" else None
     roof["clock"] = clk
 
-    detail = {}
-    for i, c in enumerate(cases):
-        ms = statistics.median(per_kernel_ms[i])
-        k, pk = op_peak(c)
-        qs = statistics.quantiles(per_kernel_ms[i], n=10) if len(per_kernel_ms[i]) > 1 else [ms] * 9
-        detail[c.name] = {"median_ms": ms, "p10_ms": qs[0], "p90_ms": qs[-1],
-                          "tflops": flops[i] / (ms * 1e-3) / 1e12,
-                          "frac_peak": flops[i] / (ms * 1e-3) / 1e12 / pk,
-                          "gbs_algorithmic": c.algorithmic_bytes() / (ms * 1e-3) / 1e9,
-                          "active_rows": c.active_rows()}
+    detail = {c.name: summarize(c, per_kernel_ms[i]) for i, c in enumerate(cases)}
+    if args.workload == "fwd+dlhs" and not args.no_detail:
+        detail["p4_speed_gate"] = speed_gate(cases[0], cases[1], 20, 3, gmm_amd)
 
     if quant:
         metric = f"activation quantiser GB/s, {args.workload}"
@@ -497,6 +603,12 @@ def main():
         line["cpu_baseline"] = cpu_baseline(cases)
     else:
         line["cpu_baseline"] = None
+    if args.workload == "fwd+dlhs" and not args.no_detail:
+        # the other configurations, after the headline's inputs are freed
+        del cases, outs, fns, launch
+        torch.cuda.empty_cache()
+        for name, steps, warm in DETAIL_WORKLOADS:
+            detail[name] = detail_workload(name, steps, warm, dev, gmm_amd)
     print(json.dumps(line), flush=True)
 
 
