@@ -190,6 +190,7 @@ def gmm_reference(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tenso
                   lhs_scale: Optional[torch.Tensor] = None,
                   existing_out: Optional[torch.Tensor] = None,
                   rhs_format: Optional[str] = None,
+                  lhs_format: Optional[str] = None,
                   rows: Optional[Sequence[int]] = None,
                   return_row_group: bool = False):
     """Reference rows of gmm(lhs, rhs, group_sizes, ...) in float64.
@@ -199,7 +200,8 @@ def gmm_reference(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tenso
     lhs_scale f32 [M,nb].  ``rows`` selects output rows (all when None).
     rhs_format "int4", "uint4" or "fp4_e2m1": rhs holds packed bytes (uint8
     or float4_e2m1fn_x2) [Ga,N,K/2], two elements to a byte, even elements
-    in the low nibble (only the [Ga,N,K] layout).
+    in the low nibble (only the [Ga,N,K] layout).  lhs_format the same for
+    packed four-bit activations: lhs bytes [M,K/2] hold the [M,K] elements.
     Returns a float64 numpy array [len(rows), N] (and the group of each row,
     -1 for none, when return_row_group).
 
@@ -214,6 +216,12 @@ def gmm_reference(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tenso
     if lhs.dim() != 2 or rhs.dim() != 3 or gs.dim() != 1 or gs.dtype != torch.int32:
         raise OracleError("bad ranks / group_sizes dtype")
     M, K = lhs.shape
+    lhs_code = None
+    if lhs_format is not None:
+        if lhs_format not in PACKED_FORMATS or lhs.element_size() != 1:
+            raise OracleError("packed four-bit lhs: a known format, bytes, [M,K/2]")
+        lhs_code = PACKED_FORMATS[lhs_format]
+        K = 2 * lhs.shape[1]
     Ga = rhs.shape[0]
     N = rhs.shape[2] if transpose_rhs else rhs.shape[1]
     Kr = rhs.shape[1] if transpose_rhs else rhs.shape[2]
@@ -253,7 +261,7 @@ def gmm_reference(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tenso
     rg = np.zeros((n_rows,), dtype=np.int64)
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     rc = lib.oracle_gmm(
-        ptr(lhs), _code(lhs, "lhs"), M, K,
+        ptr(lhs), _code(lhs, "lhs") if lhs_code is None else lhs_code, M, K,
         ptr(rhs), _code(rhs, "rhs") if rhs_code is None else rhs_code, Ga, N, int(bool(transpose_rhs)),
         ptr(gs), gs.shape[0], int(group_offset),
         ptr(rhs_scale), ptr(rhs_bias), _code(rhs_bias, "rhs_bias") if rhs_bias is not None else 0,
