@@ -104,7 +104,9 @@ const char* gmm_last_error(const gmm_handle* h);
 /*
  * gmm_run: queue out = gmm(lhs, rhs, group_sizes, ...) on `stream`.
  *
- *   lhs          [M,K]; F32, BF16, F8E4M3FN, F8E5M2 or I8.
+ *   lhs          [M,K]; F32, BF16, F8E4M3FN, F8E5M2, I8, or the four-bit I4,
+ *                U4 and F4E2M1 (two to a byte; the shape counts elements, the
+ *                data holds M*K/2 bytes).
  *   rhs          [Ga,N,K] (transpose_rhs == 0) or [Ga,K,N] (== 1).
  *                Supported (lhs, rhs) pairs: (F32,F32), (BF16,BF16),
  *                (BF16, F8E4M3FN or F8E5M2: the weight is widened exactly
@@ -118,6 +120,13 @@ const char* gmm_last_error(const gmm_handle* h);
  *                (BF16, I4 / U4 / F4E2M1: four-bit weights, two to a byte,
  *                widened exactly to bf16; the tensor's shape counts
  *                elements, [Ga,N,K], and its data holds Ga*N*K/2 bytes).
+ *                Four-bit activations (the Megablox gmm's dtype list holds
+ *                for lhs as for rhs): (I8 / I4 / U4, I8 / I4 / U4: int8
+ *                products, four-bit values widened exactly to int8, exact
+ *                int32 sums as for (I8, I8)), and (F8E4M3FN / F8E5M2 /
+ *                F4E2M1, F8E4M3FN / F8E5M2 / F4E2M1: products on the
+ *                f8f6f4 matrix instruction with each side in its own
+ *                format, fp4 e2m1 read packed).  K % 128 == 0 for these.
  *                fp8, int8 and four-bit weights need transpose_rhs == 0.
  *                Infinite or NaN e5m2 codes are outside the contract.
  *   group_sizes  [G] I32 on the device, 1 <= G <= 1024.

@@ -196,6 +196,7 @@ def gmm(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,
         transpose_rhs: bool = False,
         existing_out: Optional[torch.Tensor] = None,
         rhs_format: Optional[str] = None,
+        lhs_format: Optional[str] = None,
         out: Optional[torch.Tensor] = None,
         stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
     """Grouped matmul on the GPU through libgmm.so.
@@ -209,7 +210,11 @@ def gmm(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,
     (gmm_run_existing_out); without out the result is written into
     existing_out itself.  rhs_format "int4", "uint4" or "fp4_e2m1" takes rhs
     as packed bytes [Ga,N,K/2] (uint8 or float4_e2m1fn_x2), two weights to a
-    byte, even elements in the low nibble, with a bf16 lhs."""
+    byte, even elements in the low nibble; lhs_format the same for packed
+    four-bit activations, lhs bytes [M,K/2].  Four-bit pairs: a bf16 lhs
+    with any four-bit weight (widened to bf16); int4 / uint4 / int8 with
+    int4 / uint4 / int8 (int8 products); fp4 e2m1 / e4m3fn / e5m2 with
+    fp4 e2m1 / e4m3fn / e5m2 (the f8f6f4 products)."""
     lib = load()
     dev = lhs.device
     h = handle(dev)
@@ -217,7 +222,8 @@ def gmm(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tensor, *,
     N = rhs.shape[2] if transpose_rhs else (rhs.shape[1] if rhs.dim() == 3 else 0)
     if out is None:
         out = existing_out if existing_out is not None else torch.empty((M, N), dtype=out_dtype, device=dev)
-    views = [_view(t, n) if (n != "rhs" or rhs_format is None) else _view_packed(t, rhs_format, n)
+    packed = {"lhs": lhs_format, "rhs": rhs_format}
+    views = [_view(t, n) if packed.get(n) is None else _view_packed(t, packed[n], n)
              for t, n in ((lhs, "lhs"), (rhs, "rhs"), (group_sizes, "group_sizes"),
                           (rhs_scale, "rhs_scale"), (rhs_bias, "rhs_bias"),
                           (lhs_scale, "lhs_scale"), (out, "out"))]

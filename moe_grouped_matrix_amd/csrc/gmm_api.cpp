@@ -214,6 +214,10 @@ gmm_status run_gmm(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs, 
 
   gmmk::KernelChoice kc{};
   const int ld = lhs->dtype, rd = rhs->dtype;
+  // operand format codes of the int8 products (0 int8, 3 int4, 4 uint4) and
+  // of the f8f6f4 products (0 e4m3fn, 1 e5m2, 4 fp4 e2m1); -1 for another type
+  auto int_code = [](int d) { return d == GMM_I8 ? 0 : d == GMM_I4 ? 3 : d == GMM_U4 ? 4 : -1; };
+  auto f8_code = [](int d) { return d == GMM_F8E4M3FN ? 0 : d == GMM_F8E5M2 ? 1 : d == GMM_F4E2M1 ? 4 : -1; };
   if (ld == GMM_F32 && rd == GMM_F32) {
     kc.op = gmmk::Op::F32;
   } else if (ld == GMM_BF16 && rd == GMM_BF16) {
@@ -221,16 +225,17 @@ gmm_status run_gmm(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs, 
   } else if (ld == GMM_BF16 && (rd == GMM_F8E4M3FN || rd == GMM_F8E5M2 || rd == GMM_I8)) {
     kc.op = gmmk::Op::BF16;
     kc.b_fp8 = true;
-    kc.fmt = rd == GMM_F8E5M2 ? 2 : (rd == GMM_I8 ? 4 : 0);
+    kc.fmt = (rd == GMM_F8E5M2 ? 1 : (rd == GMM_I8 ? 2 : 0)) << 3;
   } else if (ld == GMM_BF16 && four_bit(rd)) {
     kc.op = gmmk::Op::BF16;
     kc.b_fp8 = true;
-    kc.fmt = rd == GMM_I4 ? 6 : (rd == GMM_U4 ? 8 : 10);
-  } else if (ld == GMM_I8 && rd == GMM_I8) {
+    kc.fmt = (rd == GMM_I4 ? 3 : (rd == GMM_U4 ? 4 : 5)) << 3;
+  } else if (int_code(ld) >= 0 && int_code(rd) >= 0) {
     kc.op = gmmk::Op::I8;
-  } else if ((ld == GMM_F8E4M3FN || ld == GMM_F8E5M2) && (rd == GMM_F8E4M3FN || rd == GMM_F8E5M2)) {
+    kc.fmt = int_code(ld) | int_code(rd) << 3;
+  } else if (f8_code(ld) >= 0 && f8_code(rd) >= 0) {
     kc.op = gmmk::Op::FP8;
-    kc.fmt = (ld == GMM_F8E5M2 ? 1 : 0) | (rd == GMM_F8E5M2 ? 2 : 0);
+    kc.fmt = f8_code(ld) | f8_code(rd) << 3;
   } else {
     const bool known_l = elem_size(ld) > 0 || four_bit(ld), known_r = elem_size(rd) > 0 || four_bit(rd);
     if (!known_l || !known_r || ld == GMM_I32 || rd == GMM_I32 || ld == GMM_E8M0 || rd == GMM_E8M0)

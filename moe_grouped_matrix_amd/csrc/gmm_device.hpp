@@ -278,17 +278,19 @@ __device__ inline int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 
 // ---------------------------------------------------------------------------
 // tile configurations
 
-// FMT_: the narrow formats, FMT_ & 1 for lhs (0 e4m3fn, 1 e5m2: the
-// format codes of the f8f6f4 matrix instructions) and FMT_ >> 1 for rhs
-// (the same, or for weights widened to bf16 2 int8, 3 int4, 4 uint4, 5 fp4
-// e2m1 -- the last three packed two to a byte).
+// FMT_: the narrow formats, FMT_ & 7 for lhs (FA) and FMT_ >> 3 for rhs
+// (FB).  fp8 x fp8 products (Op::FP8): 0 e4m3fn, 1 e5m2, 4 fp4 e2m1 -- the
+// format codes of the f8f6f4 matrix instructions.  int8 products (Op::I8):
+// 0 int8, 3 int4, 4 uint4.  bf16 products with narrow weights widened to
+// bf16 (B_FP8): FB 0 e4m3fn, 1 e5m2, 2 int8, 3 int4, 4 uint4, 5 fp4 e2m1.
+// The four-bit types are packed two to a byte.
 template <Op OP, bool NN_, bool BFP8_, int BM_, int BN_, int WM_, int WN_, bool SCALED_, int FMT_ = 0>
 struct Cfg {
   static constexpr Op op = OP;
   static constexpr bool NN = NN_;        // rhs is [Ga,K,N]
   static constexpr bool B_FP8 = BFP8_;   // fp8 rhs widened to bf16 operands
   static constexpr bool SCALED = SCALED_;
-  static constexpr int FA = FMT_ & 1, FB = FMT_ >> 1;
+  static constexpr int FA = FMT_ & 7, FB = FMT_ >> 3;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int T = 64 * WM * WN;
   static constexpr int ES = OP == Op::F32 ? 4 : (OP == Op::BF16 ? 2 : 1);  // operand bytes
@@ -302,20 +304,89 @@ struct Cfg {
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   static constexpr int LDS = 2 * (A_BYTES + B_BYTES);
   static constexpr int BSB = B_FP8 ? 1 : ES;  // rhs storage bytes per element (four-bit: half)
-  static constexpr bool B_NIB = B_FP8 && FB >= 3;  // four-bit weights, two to a byte
-  // bytes of `elems` consecutive rhs elements (an even count when four-bit)
-  __device__ static constexpr long long rhs_bytes(long long elems) { return B_NIB ? elems / 2 : elems * BSB; }
+  static constexpr bool B_NIB = B_FP8 && FB >= 3;  // four-bit weights widened to bf16
+  // four-bit operands of a one-byte product (fp4 e2m1 on the f8f6f4
+  // instruction as it is; int4 / uint4 widened to int8 in LDS): a K step of
+  // 128 elements is 64 bytes of a row, loaded 8 bytes a chunk
+  static constexpr bool A_Q4 = (OP == Op::FP8 && FA == 4) || (OP == Op::I8 && FA >= 3);
+  static constexpr bool B_Q4 = (OP == Op::FP8 && FB == 4) || (OP == Op::I8 && FB >= 3);
+  // bytes of `elems` consecutive rhs / lhs elements (an even count when four-bit)
+  __device__ static constexpr long long rhs_bytes(long long elems) {
+    return (B_NIB || B_Q4) ? elems / 2 : elems * BSB;
+  }
+  __device__ static constexpr long long lhs_bytes(long long elems) { return A_Q4 ? elems / 2 : elems * ES; }
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
   static_assert(A_CH >= 1 && A_CH * T == BM * 8, "A tile must split evenly");
   static_assert(B_CH >= 1 && B_CH * T == BN * 8, "B tile must split evenly");
   static_assert(!NN || (!B_FP8 && OP != Op::FP8), "NN needs f32 or bf16 weights");
   static_assert(!NN || NW == 2 || NW == 4 || NW == 8, "NN thread block width");
   static_assert(!B_FP8 || OP == Op::BF16, "fp8 weights widen to bf16");
-  static_assert(OP == Op::FP8 || FA == 0, "an lhs format only for fp8 x fp8");
-  static_assert(OP == Op::FP8 || B_FP8 || FB == 0, "an rhs format only for fp8 weights");
-  static_assert(OP != Op::FP8 || FB <= 1, "fp8 x fp8 formats are e4m3fn or e5m2");
+  static_assert(OP == Op::FP8 || OP == Op::I8 || FA == 0, "an lhs format only for one-byte products");
+  static_assert(OP == Op::FP8 || OP == Op::I8 || B_FP8 || FB == 0, "an rhs format only for narrow weights");
+  static_assert(OP != Op::FP8 || ((FA <= 1 || FA == 4) && (FB <= 1 || FB == 4)),
+                "f8f6f4 formats: e4m3fn, e5m2 or fp4 e2m1");
+  static_assert(OP != Op::I8 || ((FA == 0 || FA == 3 || FA == 4) && (FB == 0 || FB == 3 || FB == 4)),
+                "int8 products: int8, int4 or uint4 operands");
   static_assert(!NN || OP != Op::I8, "NN needs f32 or bf16 weights");
 };
+
+// 16 nibbles (two words, the low nibble of each byte first) widened to 16
+// int8: F = 3 int4 (sign-extended), 4 uint4.  Byte 2j of the result is the
+// low nibble of input byte j and byte 2j+1 its high nibble.
+template <int F>
+__device__ inline i32x4 nib16_to_i8x16(i32x2 v) {
+  i32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t x = (uint32_t)v[h];
+    const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+    // interleave: bytes (lo.b0, hi.b0, lo.b1, hi.b1), then (lo.b2, hi.b2, lo.b3, hi.b3)
+    uint32_t w0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    uint32_t w1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+    if constexpr (F == 3) {  // bit 3 of a nibble set: its byte gets 0xF0 (the sign extension)
+      w0 |= (w0 & 0x08080808u) * 0x1Eu;
+      w1 |= (w1 & 0x08080808u) * 0x1Eu;
+    }
+    r[2 * h] = (int)w0;
+    r[2 * h + 1] = (int)w1;
+  }
+  return r;
+}
+
+// Staged operand chunk into its 16-byte LDS slot.  A four-bit chunk (Q4,
+// 16 values in v[0..1]) of an int8 product is widened to 16 int8; of an
+// f8f6f4 product (fp4 e2m1) it stays packed in the slot's first 8 bytes.
+template <Op OP, bool Q4, int F>
+__device__ __forceinline__ void store_q(char* slot, i32x4 v) {
+  if constexpr (!Q4) {
+    *reinterpret_cast<i32x4*>(slot) = v;
+  } else if constexpr (OP == Op::I8) {
+    *reinterpret_cast<i32x4*>(slot) = nib16_to_i8x16<F>(i32x2{v[0], v[1]});
+  } else {
+    *reinterpret_cast<i32x2*>(slot) = i32x2{v[0], v[1]};
+  }
+}
+
+// One operand of the 16x16x128 f8f6f4 instruction for the K step in a row
+// (lane quarter q).  The instruction's lane layouts differ by width (read
+// off gfx950 with a one-hot probe): a one-byte operand's lane quarter q
+// holds K elements 16 q + [0,16) in its first four registers and
+// 64 + 16 q + [0,16) in the next four -- 16 bytes from slots q and q + 4;
+// an fp4 e2m1 operand's holds K elements 32 q + [0,32), packed in four
+// registers -- the 8 bytes of slots 2 q and 2 q + 1.  Each side in its own
+// layout, mixed products pair the same K elements.
+template <int F>
+__device__ __forceinline__ i32x8 f8f6f4_operand(const char* base, int r, int q) {
+  if constexpr (F == 4) {
+    const i32x2 lo = *reinterpret_cast<const i32x2*>(base + lds_off(r, 2 * q));
+    const i32x2 hi = *reinterpret_cast<const i32x2*>(base + lds_off(r, 2 * q + 1));
+    return i32x8{lo[0], lo[1], hi[0], hi[1], 0, 0, 0, 0};
+  } else {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(base + lds_off(r, q));
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(base + lds_off(r, q + 4));
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+}
 
 // ---------------------------------------------------------------------------
 // the kernel
@@ -337,14 +408,22 @@ __device__ inline void load_tile(const C&, Stage<C>& st, __amdgpu_buffer_rsrc_t 
   for (int i = 0; i < C::A_CH; ++i) {
     const int c = tid + i * C::T;
     const int r = c >> 3, cc = c & 7;
-    st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, r * arow_bytes + kt * 128 + cc * 16, 0, 0);
+    if constexpr (C::A_Q4) {
+      const i32x2 v = __builtin_amdgcn_raw_buffer_load_b64(ar, r * (K / 2) + kt * 64 + cc * 8, 0, 0);
+      st.a[i] = i32x4{v[0], v[1], 0, 0};
+    } else {
+      st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, r * arow_bytes + kt * 128 + cc * 16, 0, 0);
+    }
   }
   if constexpr (!C::NN) {
 #pragma unroll
     for (int i = 0; i < C::B_CH; ++i) {
       const int c = tid + i * C::T;
       const int r = c >> 3, cc = c & 7;
-      if constexpr (C::B_NIB) {
+      if constexpr (C::B_Q4) {
+        const i32x2 v = __builtin_amdgcn_raw_buffer_load_b64(br, r * (K / 2) + kt * 64 + cc * 8, 0, 0);
+        st.b[i] = i32x4{v[0], v[1], 0, 0};
+      } else if constexpr (C::B_NIB) {
         st.b[i][0] = __builtin_amdgcn_raw_buffer_load_b32(br, r * (K / 2) + kt * 32 + cc * 4, 0, 0);
         st.b[i][1] = 0;
       } else if constexpr (C::B_FP8) {
@@ -389,7 +468,7 @@ __device__ inline void store_tile(const C&, const Stage<C>& st, char* sa, char* 
 #pragma unroll
   for (int i = 0; i < C::A_CH; ++i) {
     const int c = tid + i * C::T;
-    *reinterpret_cast<i32x4*>(sa + lds_off(c >> 3, c & 7)) = st.a[i];
+    store_q<C::op, C::A_Q4, C::FA>(sa + lds_off(c >> 3, c & 7), st.a[i]);
   }
   if constexpr (!C::NN) {
 #pragma unroll
@@ -400,7 +479,7 @@ __device__ inline void store_tile(const C&, const Stage<C>& st, char* sa, char* 
         v = nib8_to_bf16x8<C::FB>((unsigned)st.b[i][0]);
       else if constexpr (C::B_FP8)
         v = fp8x8_to_bf16x8<C::FB>(i32x2{st.b[i][0], st.b[i][1]});
-      *reinterpret_cast<i32x4*>(sb + lds_off(c >> 3, c & 7)) = v;
+      store_q<C::op, C::B_Q4, C::FB>(sb + lds_off(c >> 3, c & 7), v);
     }
   } else {
     constexpr int NBLK = C::BN / C::NW;
@@ -466,18 +545,10 @@ __device__ inline void mma_tile(f32x4 (&acc)[C::FM][C::FN], const char* sa, cons
   } else if constexpr (C::op == Op::FP8) {
     i32x8 bf[C::FN];
 #pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn) {
-      const int r = wn * C::TN + fn * 16 + r16;
-      i32x4 lo = *reinterpret_cast<const i32x4*>(sb + lds_off(r, q));
-      i32x4 hi = *reinterpret_cast<const i32x4*>(sb + lds_off(r, q + 4));
-      bf[fn] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
+    for (int fn = 0; fn < C::FN; ++fn) bf[fn] = f8f6f4_operand<C::FB>(sb, wn * C::TN + fn * 16 + r16, q);
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
-      const int r = wm * C::TM + fm * 16 + r16;
-      i32x4 lo = *reinterpret_cast<const i32x4*>(sa + lds_off(r, q));
-      i32x4 hi = *reinterpret_cast<const i32x4*>(sa + lds_off(r, q + 4));
-      i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const i32x8 af = f8f6f4_operand<C::FA>(sa, wm * C::TM + fm * 16 + r16, q);
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn)
         acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[fn], acc[fm][fn],
@@ -596,8 +667,8 @@ __global__ __launch_bounds__(C::T) void gmm_kernel(Params p) {
     const int n0 = j * C::BN;
     const int ncols = N - n0 < C::BN ? N - n0 : C::BN;
 
-    const char* lhs = reinterpret_cast<const char*>(p.lhs) + (long long)row0 * K * C::ES;
-    const __amdgpu_buffer_rsrc_t ar = make_rsrc(lhs, (long long)rows * K * C::ES);
+    const char* lhs = reinterpret_cast<const char*>(p.lhs) + C::lhs_bytes((long long)row0 * K);
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(lhs, C::lhs_bytes((long long)rows * K));
     const char* rhs_h = reinterpret_cast<const char*>(p.rhs) + C::rhs_bytes((long long)h * N * K);
     __amdgpu_buffer_rsrc_t br;
     if constexpr (C::NN)

@@ -160,13 +160,14 @@ hipError_t by_size(const Params& p, const KernelChoice& kc, int cu, hipStream_t 
       return bias ? launch_big<BigCfg<NN, false, true>>(p, cu, cap, st) : launch_big<BigCfg<NN, false, false>>(p, cu, cap, st);
     }
   }
-  if constexpr (OP == Op::BF16 && BF8 && !NN && (FMT >> 1) < 3) {  // one-byte weights
+  if constexpr (OP == Op::BF16 && BF8 && !NN && (FMT >> 3) < 3) {  // one-byte weights
     if (sz == SizeClass::Small && stream_fits(p)) {
-      if (p.out_f32) return launch_stream<StreamCfg<true, (FMT >> 1)>>(p, cu, cap, st);
-      return launch_stream<StreamCfg<false, (FMT >> 1)>>(p, cu, cap, st);
+      if (p.out_f32) return launch_stream<StreamCfg<true, (FMT >> 3)>>(p, cu, cap, st);
+      return launch_stream<StreamCfg<false, (FMT >> 3)>>(p, cu, cap, st);
     }
   }
-  if constexpr (OP == Op::FP8 && !NN && SC) {  // W8A8 with scale blocks of one K step
+  // W8A8 (one-byte fp8 operands) with scale blocks of one K step
+  if constexpr (OP == Op::FP8 && !NN && SC && (FMT & 7) <= 1 && (FMT >> 3) <= 1) {
     using CB = typename Pick<OP, NN, BF8, SC, SizeClass::Big, FMT>::type;
     if (sz == SizeClass::Big && p.blk == CB::BK) return launch_w8a8<CB>(p, cu, cap, st);
   }
@@ -195,33 +196,49 @@ hipError_t launch_gmm(const Params& p, const KernelChoice& c, int cu, hipStream_
       return c.nn ? by_scaled<Op::F32, true, false>(p, c, cu, st)
                   : by_scaled<Op::F32, false, false>(p, c, cu, st);
     case Op::BF16:
-      if (c.b_fp8) {
-        if (c.nn || (c.fmt & 1)) return hipErrorInvalidValue;
-        switch (c.fmt) {
-          case 0: return by_scaled<Op::BF16, false, true, 0>(p, c, cu, st);
-          case 2: return by_scaled<Op::BF16, false, true, 2>(p, c, cu, st);
-          case 4: return by_scaled<Op::BF16, false, true, 4>(p, c, cu, st);
-          case 6: return by_scaled<Op::BF16, false, true, 6>(p, c, cu, st);
-          case 8: return by_scaled<Op::BF16, false, true, 8>(p, c, cu, st);
-          case 10: return by_scaled<Op::BF16, false, true, 10>(p, c, cu, st);
+      if (c.b_fp8) {  // widened weights: the rhs format in bits 3..5
+        if (c.nn || (c.fmt & 7)) return hipErrorInvalidValue;
+        switch (c.fmt >> 3) {
+          case 0: return by_scaled<Op::BF16, false, true, 0 << 3>(p, c, cu, st);
+          case 1: return by_scaled<Op::BF16, false, true, 1 << 3>(p, c, cu, st);
+          case 2: return by_scaled<Op::BF16, false, true, 2 << 3>(p, c, cu, st);
+          case 3: return by_scaled<Op::BF16, false, true, 3 << 3>(p, c, cu, st);
+          case 4: return by_scaled<Op::BF16, false, true, 4 << 3>(p, c, cu, st);
+          case 5: return by_scaled<Op::BF16, false, true, 5 << 3>(p, c, cu, st);
         }
         return hipErrorInvalidValue;
       }
       if (c.fmt) return hipErrorInvalidValue;
       return c.nn ? by_scaled<Op::BF16, true, false>(p, c, cu, st)
                   : by_scaled<Op::BF16, false, false>(p, c, cu, st);
-    case Op::FP8:
+    case Op::FP8:  // lhs and rhs format codes 0 e4m3fn, 1 e5m2, 4 fp4 e2m1
       if (c.nn || c.b_fp8) return hipErrorInvalidValue;
       switch (c.fmt) {
-        case 0: return by_scaled<Op::FP8, false, false, 0>(p, c, cu, st);
-        case 1: return by_scaled<Op::FP8, false, false, 1>(p, c, cu, st);
-        case 2: return by_scaled<Op::FP8, false, false, 2>(p, c, cu, st);
-        case 3: return by_scaled<Op::FP8, false, false, 3>(p, c, cu, st);
+        case 0 | 0 << 3: return by_scaled<Op::FP8, false, false, 0 | 0 << 3>(p, c, cu, st);
+        case 1 | 0 << 3: return by_scaled<Op::FP8, false, false, 1 | 0 << 3>(p, c, cu, st);
+        case 4 | 0 << 3: return by_scaled<Op::FP8, false, false, 4 | 0 << 3>(p, c, cu, st);
+        case 0 | 1 << 3: return by_scaled<Op::FP8, false, false, 0 | 1 << 3>(p, c, cu, st);
+        case 1 | 1 << 3: return by_scaled<Op::FP8, false, false, 1 | 1 << 3>(p, c, cu, st);
+        case 4 | 1 << 3: return by_scaled<Op::FP8, false, false, 4 | 1 << 3>(p, c, cu, st);
+        case 0 | 4 << 3: return by_scaled<Op::FP8, false, false, 0 | 4 << 3>(p, c, cu, st);
+        case 1 | 4 << 3: return by_scaled<Op::FP8, false, false, 1 | 4 << 3>(p, c, cu, st);
+        case 4 | 4 << 3: return by_scaled<Op::FP8, false, false, 4 | 4 << 3>(p, c, cu, st);
       }
       return hipErrorInvalidValue;
-    case Op::I8:
-      if (c.nn || c.b_fp8 || c.fmt) return hipErrorInvalidValue;
-      return by_scaled<Op::I8, false, false, 0>(p, c, cu, st);
+    case Op::I8:  // lhs and rhs format codes 0 int8, 3 int4, 4 uint4
+      if (c.nn || c.b_fp8) return hipErrorInvalidValue;
+      switch (c.fmt) {
+        case 0 | 0 << 3: return by_scaled<Op::I8, false, false, 0 | 0 << 3>(p, c, cu, st);
+        case 3 | 0 << 3: return by_scaled<Op::I8, false, false, 3 | 0 << 3>(p, c, cu, st);
+        case 4 | 0 << 3: return by_scaled<Op::I8, false, false, 4 | 0 << 3>(p, c, cu, st);
+        case 0 | 3 << 3: return by_scaled<Op::I8, false, false, 0 | 3 << 3>(p, c, cu, st);
+        case 3 | 3 << 3: return by_scaled<Op::I8, false, false, 3 | 3 << 3>(p, c, cu, st);
+        case 4 | 3 << 3: return by_scaled<Op::I8, false, false, 4 | 3 << 3>(p, c, cu, st);
+        case 0 | 4 << 3: return by_scaled<Op::I8, false, false, 0 | 4 << 3>(p, c, cu, st);
+        case 3 | 4 << 3: return by_scaled<Op::I8, false, false, 3 | 4 << 3>(p, c, cu, st);
+        case 4 | 4 << 3: return by_scaled<Op::I8, false, false, 4 | 4 << 3>(p, c, cu, st);
+      }
+      return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
 }

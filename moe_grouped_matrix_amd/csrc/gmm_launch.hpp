@@ -14,8 +14,9 @@ struct KernelChoice {
   Op op;
   bool nn;      // rhs [Ga,K,N]
   bool b_fp8;   // fp8 rhs widened to bf16 operands
-  int fmt;      // narrow formats: fmt & 1 lhs (0 e4m3fn, 1 e5m2), fmt >> 1 rhs (the same, or
-                // widened weights 2 int8, 3 int4, 4 uint4, 5 fp4 e2m1)
+  int fmt;      // narrow formats: fmt & 7 lhs, fmt >> 3 rhs.  FP8 products: 0 e4m3fn, 1 e5m2,
+                // 4 fp4 e2m1; I8 products: 0 int8, 3 int4, 4 uint4; widened bf16 weights
+                // (b_fp8): rhs 0 e4m3fn, 1 e5m2, 2 int8, 3 int4, 4 uint4, 5 fp4 e2m1
   bool scaled;  // rhs_scale and/or lhs_scale present
   SizeClass size;
   int grid_cap;  // > 0: at most this many workgroups (a test hook)

@@ -70,6 +70,7 @@ __device__ __forceinline__ void w8a8_issue(char* st, __amdgpu_buffer_rsrc_t ra, 
 
 template <class C>
 __global__ __launch_bounds__(C::T) void gmm_w8a8_kernel(Params p) {
+  static_assert(C::op == Op::FP8 && C::FA <= 1 && C::FB <= 1, "one-byte fp8 operands (e4m3fn or e5m2)");
   using R = W8A8Ring<C>;
   // one LDS array for the ring and the plan: with a second LDS variable the
   // compiler tags LDS accesses with alias scopes and then drains the

@@ -164,6 +164,71 @@ def test_four_bit_weights_are_bit_exact(fmt, tile_policy):
     assert m.device_flags() == 0
 
 
+FOUR_BIT_PAIRS = [
+    # (lhs, rhs): a packed four-bit format name or a one-byte dtype
+    ("int4", "int4"), ("int4", "uint4"), ("int4", torch.int8), ("uint4", "int4"), ("uint4", "uint4"),
+    ("uint4", torch.int8), (torch.int8, "int4"), (torch.int8, "uint4"),
+    ("fp4_e2m1", "fp4_e2m1"), ("fp4_e2m1", torch.float8_e4m3fn), ("fp4_e2m1", torch.float8_e5m2),
+    (torch.float8_e4m3fn, "fp4_e2m1"), (torch.float8_e5m2, "fp4_e2m1"),
+]
+
+
+def _pair_id(p):
+    return "x".join(k if isinstance(k, str) else str(k).split(".")[-1] for k in p)
+
+
+def _operand(kind, shape, g):
+    """(tensor, packed format or None): packed bytes with every nibble
+    value, or small integers in a one-byte type."""
+    if isinstance(kind, str):
+        return torch.randint(0, 256, (*shape[:-1], shape[-1] // 2), generator=g).to(torch.uint8), kind
+    lo, hi = (-8, 8) if kind == torch.int8 else (-6, 7)
+    return torch.randint(lo, hi, shape, generator=g).to(torch.float32).to(kind), None
+
+
+@pytest.mark.parametrize("pair", FOUR_BIT_PAIRS, ids=[_pair_id(p) for p in FOUR_BIT_PAIRS])
+def test_four_bit_activations_are_bit_exact(pair, tile_policy):
+    """Four-bit activations (the Megablox gmm's dtype list holds for lhs as
+    for rhs): int4 / uint4 on the int8 matrix instruction, fp4 e2m1 on the
+    f8f6f4 one, each with the other four-bit and one-byte types.  Every
+    product and partial sum is exact in fp32 (block partials below 2^15,
+    power-of-two scales 2^-3 .. 2^3), so the outputs equal the oracle's bit
+    for bit: plain (f32 and bf16 out) and with both block scales and a
+    bias."""
+    import moe_grouped_matrix_amd as m
+    g = torch.Generator().manual_seed(8)
+    sizes = [33, 0, 70, 257, 5]
+    M, K, N, nb = sum(sizes) + 7, 256, 200, 2
+    lhs, lf = _operand(pair[0], (M, K), g)
+    rhs, rf = _operand(pair[1], (len(sizes), N, K), g)
+    rs = 2.0 ** torch.randint(-2, 3, (len(sizes), nb, 1, N), generator=g).to(torch.float32)
+    ls = 2.0 ** torch.randint(-1, 2, (M, nb), generator=g).to(torch.float32)
+    bias = torch.randint(-8, 9, (len(sizes), 1, N), generator=g).to(torch.bfloat16)
+    gs = torch.tensor(sizes, dtype=torch.int32)
+    print(f"four-bit activations {_pair_id(pair)} policy {tile_policy}", flush=True)
+    for out_dtype, kw in ((torch.float32, {}), (torch.bfloat16, {}),
+                          (torch.float32, dict(rhs_scale=rs, lhs_scale=ls, rhs_bias=bias))):
+        out = m.gmm(lhs.cuda(), rhs.cuda(), gs.cuda(), lhs_format=lf, rhs_format=rf, out_dtype=out_dtype,
+                    **{k: v.cuda() for k, v in kw.items()}).cpu()
+        want = oracle.round_to(oracle.gmm_reference(lhs, rhs, gs, lhs_format=lf, rhs_format=rf, **kw), out_dtype)
+        iv = torch.int16 if out_dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(out.view(iv), want.view(iv)), (_pair_id(pair), out_dtype, list(kw))
+    assert m.device_flags() == 0
+
+
+def test_four_bit_activations_need_a_matching_family():
+    """A four-bit activation with a weight outside its family (int4 with an
+    fp8 weight, fp4 with a bf16 weight) is a valid problem this library does
+    not run."""
+    import moe_grouped_matrix_amd as m
+    gs = torch.tensor([4], dtype=torch.int32, device="cuda")
+    lhs = torch.zeros(4, 64, dtype=torch.uint8, device="cuda")
+    for fmt, rhs in (("int4", torch.zeros(1, 8, 128, dtype=torch.float8_e4m3fn, device="cuda")),
+                     ("fp4_e2m1", torch.zeros(1, 8, 128, dtype=torch.bfloat16, device="cuda"))):
+        with pytest.raises(m.GmmUnsupported):
+            m.gmm(lhs, rhs, gs, lhs_format=fmt)
+
+
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 def test_scaled_exact_inputs_are_bit_exact(path, tile_policy):
     """Power-of-two block scales, per-row scales and a bias keep the integer
