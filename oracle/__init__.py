@@ -150,6 +150,15 @@ def widen_scales_reference(src: torch.Tensor, dtype: int) -> torch.Tensor:
     return out.view(src.shape)
 
 
+def _e8m0_to_f32(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if t is None or t.dtype != torch.float8_e8m0fnu:
+        return t
+    b = t.view(torch.uint8)
+    if bool((b == 255).any()):
+        raise OracleError("E8M0 scale byte 255 (NaN) in a gmm block scale")
+    return widen_scales_reference(b.reshape(-1), SCALE_E8M0).view(t.shape)
+
+
 def quant_fp8_reference(x: torch.Tensor, blk: int = 128):
     """Per-token activation quantisation (per_token_group_quant_fp8, metrale
     gemm_quant.rs page): x bf16 [M,K] -> (q float8_e4m3fn [M,K], scale f32
@@ -213,6 +222,10 @@ def gmm_reference(lhs: torch.Tensor, rhs: torch.Tensor, group_sizes: torch.Tenso
     lib = _load()
     lhs, rhs, gs = _cpu(lhs), _cpu(rhs), _cpu(group_sizes)
     rhs_scale, rhs_bias, lhs_scale = _cpu(rhs_scale), _cpu(rhs_bias), _cpu(lhs_scale)
+    # E8M0 block scales (the microscaling scale byte) are the power of two
+    # the page's widening gives, 2^(e-127); byte 255 (the encoding's NaN,
+    # 0.0 in the page's widening) is outside the operation
+    rhs_scale, lhs_scale = _e8m0_to_f32(rhs_scale), _e8m0_to_f32(lhs_scale)
     if lhs.dim() != 2 or rhs.dim() != 3 or gs.dim() != 1 or gs.dtype != torch.int32:
         raise OracleError("bad ranks / group_sizes dtype")
     M, K = lhs.shape

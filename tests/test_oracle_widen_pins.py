@@ -11,6 +11,7 @@ pins reject them."""
 import os
 
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -74,3 +75,29 @@ def test_planted_mistakes_are_caught():
     assert rows[255] != nan_bits
     assert rows[0] != 0
     assert rows[128] != (128 - 1) << 23 and rows[128] == 128 << 23
+
+
+def test_gmm_with_e8m0_block_scales_equals_the_powers_of_two():
+    """gmm's block scales may come as E8M0 bytes (microscaling): the oracle
+    multiplies by 2^(e-127), the same products as f32 scales built here
+    with ldexp; byte 255 (NaN in that encoding) is rejected."""
+    import numpy as np
+    import torch
+
+    import oracle
+    g = torch.Generator().manual_seed(9)
+    sizes = [6, 0, 9]
+    M, N, K, nb = sum(sizes) + 2, 12, 128, 4
+    lhs = torch.randint(-3, 4, (M, K), generator=g).to(torch.float8_e4m3fn)
+    rhs = torch.randint(-3, 4, (len(sizes), N, K), generator=g).to(torch.float8_e4m3fn)
+    er = torch.randint(1, 255, (len(sizes), nb, 1, N), generator=g).to(torch.uint8)
+    el = torch.randint(1, 255, (M, nb), generator=g).to(torch.uint8)
+    gs = torch.tensor(sizes, dtype=torch.int32)
+    got = oracle.gmm_reference(lhs, rhs, gs, rhs_scale=er.view(torch.float8_e8m0fnu),
+                               lhs_scale=el.view(torch.float8_e8m0fnu))
+    f = lambda e: torch.from_numpy(np.ldexp(1.0, e.numpy().astype(np.int64) - 127)).to(torch.float32)  # noqa: E731
+    want = oracle.gmm_reference(lhs, rhs, gs, rhs_scale=f(er), lhs_scale=f(el))
+    assert np.array_equal(got, want)
+    er[0, 0, 0, 0] = 255
+    with pytest.raises(oracle.OracleError):
+        oracle.gmm_reference(lhs, rhs, gs, rhs_scale=er.view(torch.float8_e8m0fnu))
