@@ -134,6 +134,13 @@ const char* gmm_last_error(const gmm_handle* h);
  *   rhs_bias     NULL or [Ga,1,N], F32 or BF16.
  *   lhs_scale    NULL or F32 [M,nb] (its nb must equal rhs_scale's when both
  *                are given).
+ *                Either scale may instead be E8M0 bytes (then every given
+ *                scale is): microscaling block scales of 32 K elements
+ *                (nb = K/32), byte e meaning 2^(e-127) as in the metrale
+ *                gemm_quant.rs page's E8M0 widening, applied by the gfx950
+ *                scaled f8f6f4 matrix instruction itself, for any pair of
+ *                F8E4M3FN / F8E5M2 / F4E2M1 operands.  Byte 255 (NaN in the
+ *                microscaling encoding) is outside the contract.
  *   group_offset NULL (s = 0) or a device pointer to one int32 s.
  *   out          [M,N], F32 or BF16.  All M rows are written.  out must not
  *                overlap any input.

@@ -248,16 +248,20 @@ gmm_status run_gmm(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs, 
   if (kc.nn && kc.op == gmmk::Op::I8) return fail(h, GMM_E_UNSUPPORTED, "int8 weights are read in the [G,N,K] layout only");
 
   long long nb = 1;
+  // block scales: f32 (folded per block), or E8M0 bytes of 32-element blocks
+  // for the scaled matrix instruction -- then every given scale is E8M0
+  const bool mx = (rhs_scale && rhs_scale->dtype == GMM_E8M0) || (lhs_scale && lhs_scale->dtype == GMM_E8M0);
+  const int scale_dtype = mx ? GMM_E8M0 : GMM_F32;
   if (rhs_scale) {
-    if (rhs_scale->ndim != 4 || rhs_scale->dtype != GMM_F32)
-      return fail(h, GMM_E_INVALID, "expected an f32 4-tensor for rhs_scale");
+    if (rhs_scale->ndim != 4 || rhs_scale->dtype != scale_dtype)
+      return fail(h, GMM_E_INVALID, "expected an f32 (or, with E8M0 scales on both sides, E8M0) 4-tensor for rhs_scale");
     nb = rhs_scale->shape[1];
     if (rhs_scale->shape[0] != Ga || rhs_scale->shape[2] != 1 || rhs_scale->shape[3] != N || nb < 1)
       return fail(h, GMM_E_INVALID, "expected rhs_scale of shape (Ga, nb, 1, N), got " + shape_str(rhs_scale));
   }
   if (lhs_scale) {
-    if (lhs_scale->ndim != 2 || lhs_scale->dtype != GMM_F32 || lhs_scale->shape[0] != M || lhs_scale->shape[1] < 1)
-      return fail(h, GMM_E_INVALID, "expected lhs_scale of shape (M, nb), f32");
+    if (lhs_scale->ndim != 2 || lhs_scale->dtype != scale_dtype || lhs_scale->shape[0] != M || lhs_scale->shape[1] < 1)
+      return fail(h, GMM_E_INVALID, "expected lhs_scale of shape (M, nb), of rhs_scale's dtype (f32 or E8M0)");
     if (rhs_scale && lhs_scale->shape[1] != nb)
       return fail(h, GMM_E_INVALID, "lhs_scale and rhs_scale disagree on the number of blocks");
     nb = lhs_scale->shape[1];
@@ -269,7 +273,13 @@ gmm_status run_gmm(gmm_handle* h, const gmm_tensor* lhs, const gmm_tensor* rhs, 
     if (rhs_bias->dtype != GMM_F32 && rhs_bias->dtype != GMM_BF16)
       return fail(h, GMM_E_INVALID, "rhs_bias must be f32 or bf16");
   }
-  kc.scaled = rhs_scale != nullptr || lhs_scale != nullptr;
+  kc.scaled = !mx && (rhs_scale != nullptr || lhs_scale != nullptr);
+  kc.mx = mx;
+  if (mx) {
+    if (kc.op != gmmk::Op::FP8)
+      return fail(h, GMM_E_UNSUPPORTED, "E8M0 block scales need e4m3fn, e5m2 or fp4 e2m1 operands on both sides");
+    if (K != 32 * nb) return fail(h, GMM_E_UNSUPPORTED, "E8M0 block scales cover blocks of 32 K elements (nb = K/32)");
+  }
 
   // Limits of the kernels (valid problems outside them are unsupported).
   const int kt = gmmk::k_tile(kc.op);

@@ -284,12 +284,16 @@ __device__ inline int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 
 // 0 int8, 3 int4, 4 uint4.  bf16 products with narrow weights widened to
 // bf16 (B_FP8): FB 0 e4m3fn, 1 e5m2, 2 int8, 3 int4, 4 uint4, 5 fp4 e2m1.
 // The four-bit types are packed two to a byte.
-template <Op OP, bool NN_, bool BFP8_, int BM_, int BN_, int WM_, int WN_, bool SCALED_, int FMT_ = 0>
+// MX_: E8M0 block scales of 32 K elements applied by the scaled f8f6f4
+// instruction itself (no fold; SCALED_ is false).
+template <Op OP, bool NN_, bool BFP8_, int BM_, int BN_, int WM_, int WN_, bool SCALED_, int FMT_ = 0,
+          bool MX_ = false>
 struct Cfg {
   static constexpr Op op = OP;
   static constexpr bool NN = NN_;        // rhs is [Ga,K,N]
   static constexpr bool B_FP8 = BFP8_;   // fp8 rhs widened to bf16 operands
   static constexpr bool SCALED = SCALED_;
+  static constexpr bool MX = MX_;
   static constexpr int FA = FMT_ & 7, FB = FMT_ >> 3;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int T = 64 * WM * WN;
@@ -328,6 +332,7 @@ struct Cfg {
   static_assert(OP != Op::I8 || ((FA == 0 || FA == 3 || FA == 4) && (FB == 0 || FB == 3 || FB == 4)),
                 "int8 products: int8, int4 or uint4 operands");
   static_assert(!NN || OP != Op::I8, "NN needs f32 or bf16 weights");
+  static_assert(!MX || (OP == Op::FP8 && !SCALED), "E8M0 block scales on the f8f6f4 instruction");
 };
 
 // 16 nibbles (two words, the low nibble of each byte first) widened to 16
@@ -585,6 +590,35 @@ __device__ inline void mma_tile(f32x4 (&acc)[C::FM][C::FN], const char* sa, cons
   }
 }
 
+// acc[fm][fn] += A * B over one K step with the instruction's E8M0 block
+// scales: sca[fm] the scale byte of this lane's tile row (wave row block
+// fm) and K block q of the step, scb[fn] that of its tile column.  The
+// scale a lane quarter q supplies covers the instruction's K elements
+// 32 q + [0,32) whichever lanes hold them (measured on gfx950: with the
+// operands in the layouts of f8f6f4_operand, where the step's K element k
+// is the instruction's element k in either width, the products match
+// block-scaled sums exactly; with a one-byte operand's lane quarter given
+// its own 32 consecutive elements instead, they do not).  So each operand
+// keeps its unscaled layout and any pair of widths takes E8M0 scales.
+template <class C>
+__device__ inline void mma_tile_mx(f32x4 (&acc)[C::FM][C::FN], const char* sa, const char* sb,
+                                   const int (&sca)[C::FM], const int (&scb)[C::FN]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w / C::WN, wn = w % C::WN;
+  const int q = lane >> 4, r16 = lane & 15;
+  i32x8 bf[C::FN];
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) bf[fn] = f8f6f4_operand<C::FB>(sb, wn * C::TN + fn * 16 + r16, q);
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) {
+    const i32x8 af = f8f6f4_operand<C::FA>(sa, wm * C::TM + fm * 16 + r16, q);
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+      acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[fn], acc[fm][fn], C::FA, C::FB, 0,
+                                                                     sca[fm], 0, scb[fn]);
+  }
+}
+
 // Bytes [off, off + 16) of a row outside the active groups: zeros, or the
 // same bytes of the existing output.  (With kFillKeep nothing is written;
 // the callers then have no such bytes to fill.)
@@ -731,6 +765,32 @@ __global__ __launch_bounds__(C::T) void gmm_kernel(Params p) {
       load_scales(0);
       store_scales(0);
     }
+    // E8M0 block scales for the instruction (MX): the bytes of this lane's
+    // rows and columns for K block 4 kt + q, one K step ahead in registers.
+    // Rows and columns outside the tile read 0 (their outputs are dropped);
+    // an absent scale is 127 (1.0).
+    constexpr int XA = C::MX ? C::FM : 1, XB = C::MX ? C::FN : 1;
+    int sca[XA], scb[XB], nsca[XA], nscb[XB];
+    const uint8_t* ls8 = reinterpret_cast<const uint8_t*>(p.lhs_scale);
+    const uint8_t* rs8 = reinterpret_cast<const uint8_t*>(p.rhs_scale);
+    const __amdgpu_buffer_rsrc_t lsr =
+        C::MX && ls8 ? make_rsrc(ls8 + (long long)row0 * p.nb, (long long)rows * p.nb) : make_rsrc(p.lhs, 0);
+    const __amdgpu_buffer_rsrc_t rsr =
+        C::MX && rs8 ? make_rsrc(rs8 + (long long)h * p.nb * N + n0, (long long)(p.nb - 1) * N + ncols)
+                     : make_rsrc(p.lhs, 0);
+    auto load_mx = [&](int kt, int (&xa)[XA], int (&xb)[XB]) __attribute__((always_inline)) {
+      const int b = kt * 4 + q;
+#pragma unroll
+      for (int fm = 0; fm < XA; ++fm)
+        xa[fm] = p.lhs_scale ? (int)__builtin_amdgcn_raw_buffer_load_b8(
+                                   lsr, (wm * C::TM + fm * 16 + r16) * p.nb + b, 0, 0)
+                             : 127;
+#pragma unroll
+      for (int fn = 0; fn < XB; ++fn)
+        xb[fn] = p.rhs_scale ? (int)__builtin_amdgcn_raw_buffer_load_b8(rsr, b * N + wn * C::TN + fn * 16 + r16, 0, 0)
+                             : 127;
+    };
+    if constexpr (C::MX) load_mx(0, sca, scb);
     __syncthreads();
 
     for (int kt = 0; kt < KT; ++kt) {
@@ -742,7 +802,16 @@ __global__ __launch_bounds__(C::T) void gmm_kernel(Params p) {
         if (next_scales) load_scales(kt / kt_per_blk + 1);
       }
       if (kt + 1 < KT) load_tile(cfg, st, ar, br, kt + 1, K, N, n0);
-      mma_tile<C>(acc, sa, sb);
+      if constexpr (C::MX) {
+        if (kt + 1 < KT) load_mx(kt + 1, nsca, nscb);
+        mma_tile_mx<C>(acc, sa, sb, sca, scb);
+#pragma unroll
+        for (int fm = 0; fm < XA; ++fm) sca[fm] = nsca[fm];
+#pragma unroll
+        for (int fn = 0; fn < XB; ++fn) scb[fn] = nscb[fn];
+      } else {
+        mma_tile<C>(acc, sa, sb);
+      }
       if constexpr (C::SCALED) {
         if ((kt + 1) % kt_per_blk == 0) {
           const int bb = (kt / kt_per_blk) & 1;

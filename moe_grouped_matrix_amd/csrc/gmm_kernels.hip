@@ -39,13 +39,13 @@ namespace {
 // partial and the running total both stay in registers.  Small: 32 x 64,
 // four waves of 32 x 16 (decode-sized groups).  F32 uses 64 x 64 tiles of
 // four 32 x 32 waves.
-template <Op OP, bool NN, bool BF8, bool SC, SizeClass SZ, int FMT>
+template <Op OP, bool NN, bool BF8, bool SC, SizeClass SZ, int FMT, bool MX = false>
 struct Pick {
-  using type = Cfg<OP, NN, BF8, 256, 128, SC ? 4 : 2, 2, SC, FMT>;
+  using type = Cfg<OP, NN, BF8, 256, 128, SC ? 4 : 2, 2, SC, FMT, MX>;
 };
-template <Op OP, bool NN, bool BF8, bool SC, int FMT>
-struct Pick<OP, NN, BF8, SC, SizeClass::Small, FMT> {
-  using type = Cfg<OP, NN, BF8, 32, 64, 1, 4, SC, FMT>;
+template <Op OP, bool NN, bool BF8, bool SC, int FMT, bool MX>
+struct Pick<OP, NN, BF8, SC, SizeClass::Small, FMT, MX> {
+  using type = Cfg<OP, NN, BF8, 32, 64, 1, 4, SC, FMT, MX>;
 };
 
 // Every kernel below walks its work items with a grid stride, so any grid
@@ -176,6 +176,16 @@ hipError_t by_size(const Params& p, const KernelChoice& kc, int cu, hipStream_t 
   return launch_cfg<typename Pick<OP, NN, BF8, SC, SizeClass::Small, FMT>::type>(p, cu, cap, st);
 }
 
+// E8M0 block scales on the scaled f8f6f4 instruction (general kernel).
+template <int FMT>
+hipError_t by_size_mx(const Params& p, const KernelChoice& kc, int cu, hipStream_t st) {
+  if (kc.size == SizeClass::Big)
+    return launch_cfg<typename Pick<Op::FP8, false, false, false, SizeClass::Big, FMT, true>::type>(
+        p, cu, kc.grid_cap, st);
+  return launch_cfg<typename Pick<Op::FP8, false, false, false, SizeClass::Small, FMT, true>::type>(
+      p, cu, kc.grid_cap, st);
+}
+
 template <Op OP, bool NN, bool BF8, int FMT = 0>
 hipError_t by_scaled(const Params& p, const KernelChoice& c, int cu, hipStream_t st) {
   if (c.scaled) return by_size<OP, NN, BF8, true, FMT>(p, c, cu, st);
@@ -213,6 +223,21 @@ hipError_t launch_gmm(const Params& p, const KernelChoice& c, int cu, hipStream_
                   : by_scaled<Op::BF16, false, false>(p, c, cu, st);
     case Op::FP8:  // lhs and rhs format codes 0 e4m3fn, 1 e5m2, 4 fp4 e2m1
       if (c.nn || c.b_fp8) return hipErrorInvalidValue;
+      if (c.mx) {
+        if (c.scaled) return hipErrorInvalidValue;
+        switch (c.fmt) {
+          case 0 | 0 << 3: return by_size_mx<0 | 0 << 3>(p, c, cu, st);
+          case 1 | 0 << 3: return by_size_mx<1 | 0 << 3>(p, c, cu, st);
+          case 4 | 0 << 3: return by_size_mx<4 | 0 << 3>(p, c, cu, st);
+          case 0 | 1 << 3: return by_size_mx<0 | 1 << 3>(p, c, cu, st);
+          case 1 | 1 << 3: return by_size_mx<1 | 1 << 3>(p, c, cu, st);
+          case 4 | 1 << 3: return by_size_mx<4 | 1 << 3>(p, c, cu, st);
+          case 0 | 4 << 3: return by_size_mx<0 | 4 << 3>(p, c, cu, st);
+          case 1 | 4 << 3: return by_size_mx<1 | 4 << 3>(p, c, cu, st);
+          case 4 | 4 << 3: return by_size_mx<4 | 4 << 3>(p, c, cu, st);
+        }
+        return hipErrorInvalidValue;
+      }
       switch (c.fmt) {
         case 0 | 0 << 3: return by_scaled<Op::FP8, false, false, 0 | 0 << 3>(p, c, cu, st);
         case 1 | 0 << 3: return by_scaled<Op::FP8, false, false, 1 | 0 << 3>(p, c, cu, st);

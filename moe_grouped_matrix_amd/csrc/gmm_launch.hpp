@@ -17,7 +17,8 @@ struct KernelChoice {
   int fmt;      // narrow formats: fmt & 7 lhs, fmt >> 3 rhs.  FP8 products: 0 e4m3fn, 1 e5m2,
                 // 4 fp4 e2m1; I8 products: 0 int8, 3 int4, 4 uint4; widened bf16 weights
                 // (b_fp8): rhs 0 e4m3fn, 1 e5m2, 2 int8, 3 int4, 4 uint4, 5 fp4 e2m1
-  bool scaled;  // rhs_scale and/or lhs_scale present
+  bool scaled;  // f32 rhs_scale and/or lhs_scale present (folded per block)
+  bool mx;      // E8M0 scales of 32-element blocks, applied by the scaled instruction
   SizeClass size;
   int grid_cap;  // > 0: at most this many workgroups (a test hook)
 };

@@ -229,6 +229,60 @@ def test_four_bit_activations_need_a_matching_family():
             m.gmm(lhs, rhs, gs, lhs_format=fmt)
 
 
+MX_PAIRS = [(torch.float8_e4m3fn, torch.float8_e4m3fn), (torch.float8_e5m2, torch.float8_e4m3fn),
+            (torch.float8_e4m3fn, torch.float8_e5m2), (torch.float8_e5m2, torch.float8_e5m2),
+            ("fp4_e2m1", "fp4_e2m1"), ("fp4_e2m1", torch.float8_e4m3fn), (torch.float8_e4m3fn, "fp4_e2m1"),
+            ("fp4_e2m1", torch.float8_e5m2), (torch.float8_e5m2, "fp4_e2m1")]
+
+
+@pytest.mark.parametrize("pair", MX_PAIRS, ids=[_pair_id(p) for p in MX_PAIRS])
+def test_e8m0_block_scales_on_the_scaled_instruction_are_bit_exact(pair, tile_policy):
+    """E8M0 block scales of 32 K elements (the microscaling block; the
+    metrale gemm_quant.rs page's E8M0 scale bytes) applied by gfx950's
+    scaled f8f6f4 instruction, per row and per column, for every pair of
+    e4m3fn, e5m2 and fp4 e2m1 operands.  Small-integer (fp8) or fp4 operands and scales 2^-2 .. 2^2 keep
+    every sum exact in fp32: bit-exact against the oracle, which multiplies
+    by 2^(e-127) block by block."""
+    import moe_grouped_matrix_amd as m
+    g = torch.Generator().manual_seed(10)
+    sizes = [33, 0, 70, 257, 5]
+    M, K, N = sum(sizes) + 7, 256, 200
+    nb = K // 32
+    lhs, lf = _operand(pair[0], (M, K), g)
+    rhs, rf = _operand(pair[1], (len(sizes), N, K), g)
+    er = torch.randint(125, 130, (len(sizes), nb, 1, N), generator=g).to(torch.uint8).view(torch.float8_e8m0fnu)
+    el = torch.randint(126, 130, (M, nb), generator=g).to(torch.uint8).view(torch.float8_e8m0fnu)
+    bias = torch.randint(-8, 9, (len(sizes), 1, N), generator=g).to(torch.bfloat16)
+    gs = torch.tensor(sizes, dtype=torch.int32)
+    print(f"E8M0 scales {_pair_id(pair)} policy {tile_policy}", flush=True)
+    for out_dtype, kw in ((torch.float32, dict(rhs_scale=er)), (torch.float32, dict(lhs_scale=el)),
+                          (torch.float32, dict(rhs_scale=er, lhs_scale=el, rhs_bias=bias)),
+                          (torch.bfloat16, dict(rhs_scale=er, lhs_scale=el))):
+        out = m.gmm(lhs.cuda(), rhs.cuda(), gs.cuda(), lhs_format=lf, rhs_format=rf, out_dtype=out_dtype,
+                    **{k: v.cuda() for k, v in kw.items()}).cpu()
+        want = oracle.round_to(oracle.gmm_reference(lhs, rhs, gs, lhs_format=lf, rhs_format=rf, **kw), out_dtype)
+        iv = torch.int16 if out_dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(out.view(iv), want.view(iv)), (_pair_id(pair), out_dtype, list(kw))
+    assert m.device_flags() == 0
+
+
+def test_e8m0_block_scales_limits():
+    """E8M0 scales need f8f6f4 operands (e4m3fn, e5m2, fp4 e2m1), blocks
+    of 32, and E8M0 on both sides."""
+    import moe_grouped_matrix_amd as m
+    gs = torch.tensor([4], dtype=torch.int32, device="cuda")
+    e8 = lambda *sh: torch.full(sh, 127, dtype=torch.uint8, device="cuda").view(torch.float8_e8m0fnu)  # noqa: E731
+    lhs8 = torch.zeros(4, 128, dtype=torch.float8_e4m3fn, device="cuda")
+    rhs8 = torch.zeros(1, 8, 128, dtype=torch.float8_e4m3fn, device="cuda")
+    with pytest.raises(m.GmmUnsupported):
+        m.gmm(lhs8, rhs8, gs, rhs_scale=e8(1, 2, 1, 8))  # blocks of 64
+    with pytest.raises(m.GmmInvalid):
+        m.gmm(lhs8, rhs8, gs, rhs_scale=e8(1, 4, 1, 8),
+              lhs_scale=torch.ones(4, 4, dtype=torch.float32, device="cuda"))
+    with pytest.raises(m.GmmUnsupported):
+        m.gmm(torch.zeros(4, 128, dtype=torch.bfloat16, device="cuda"), rhs8, gs, rhs_scale=e8(1, 4, 1, 8))
+
+
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 def test_scaled_exact_inputs_are_bit_exact(path, tile_policy):
     """Power-of-two block scales, per-row scales and a bias keep the integer
