@@ -1,58 +1,71 @@
 // gmm_stream.hpp -- the weight-streaming kernel of the gfx950 grouped matmul:
-// bf16 lhs x e4m3 weight [G,N,K] with per-block rhs_scale and an optional
-// bias, for problems with few rows per group (decode), where the run time is
-// the time to read every active group's weight once from HBM.
+// bf16 lhs x one-byte weight [G,N,K] (e4m3fn, e5m2 or int8, widened exactly
+// to bf16) with per-block rhs_scale and an optional bias, for problems with
+// few rows per group (decode), where the run time is the time to read every
+// active group's weight once from HBM.
 //
-// Output tiles are 32 rows (group-aligned) x 64 columns; a tile reads its
-// group's 64 x K weight slab once.  K is consumed in stages of 128 (one
-// quantisation block of the scale; without a scale every block counts 1),
-// each stage holding in LDS the weight slab
-// (64 rows of 128 bytes), the tile's lhs rows (32 rows of 256 bytes), the
-// block's 64 scales and the tile's 64 bias values.  Six stages form a ring
-// filled by direct-to-LDS loads five stages ahead, across the workgroup's
-// tiles, so the HBM stream never drains.  Eight waves, two per SIMD: wave w
-// takes K half w / 4 of every stage and columns 16 (w % 4) .. +16 of the
-// tile for all 32 rows, with 16x16x32 bf16 MFMAs after widening its e4m3
-// weight fragment to bf16 (so no weight byte is widened twice), and folds
-// each block's product into fp32 totals with that block's scales (the weight
-// fragment is the MFMA's first operand, so a lane holds four consecutive
-// columns of a row and their four scales).  At the end of a tile the two K
-// halves add their totals through LDS and each stores one 16-row half.
+// Output tiles are 64 rows (group-aligned) x 256 columns; a tile reads its
+// group's 256 x K weight slab once, so a group of up to 64 rows reads its
+// weight once.  K is consumed in stages of 128 (one quantisation block of
+// the scale; without a scale every block counts 1), each stage holding in
+// LDS the weight slab (256 rows of 128 bytes), the tile's lhs rows (64 rows
+// of 256 bytes), the block's 256 scales and the tile's 256 bias values.
+// Three stages form a ring filled by direct-to-LDS loads two stages ahead,
+// across the workgroup's tiles, so the HBM stream never drains.  Four
+// waves, one per SIMD: wave w computes columns 128 (w % 2) .. +128 for rows
+// 32 (w / 2) .. +32 over the whole of K with 32x32x16 bf16 MFMAs, so no
+// partial sums cross waves.  The weight fragment is the MFMA's first
+// operand (a lane holds runs of four columns of one row), widened from its
+// one-byte format to bf16 in registers, and each block's product is folded
+// into fp32 totals with that block's scales.
 //
-// Every wave issues the same four loads per stage (weight, lhs, scale, bias;
-// loads past a range return zeros and still count) and one store per tile,
-// so the vmcnt waits are constants.
+// What sets the shape: the lhs rows share the LDS ring with the weights,
+// and a stage's time is set by the bytes and loads it moves, not by its
+// multiplies (measured: 64-row tiles 32, 64, 128 and 256 columns wide run
+// a 128-K stage in 0.49, 0.67, 1.05 and 2.1 us, the widest moving the most
+// weight per lhs byte: 33.4 us per decode call against 38.9 us for the
+// 32 x 64 tiles, which also read each expert's weight once per 32 rows).
+//
+// Every wave issues the same loads in every stage (eight weight and four
+// lhs; wave 0 also the scales, wave 1 the bias; loads past a range return
+// zeros and still count) and the same stores per tile, so the vmcnt waits
+// are constants (one set for waves 0 and 1, one for 2 and 3).
 #pragma once
 
 #include "gmm_big.hpp"
 
 namespace gmmk {
 
-// FB_: the weight's fp8 format (0 e4m3fn, 1 e5m2).
+// FB_: the weight's one-byte format (0 e4m3fn, 1 e5m2, 2 int8).
 template <bool OUT_F32_, int FB_ = 0>
 struct StreamCfg {
   static constexpr bool OUT_F32 = OUT_F32_;
   static constexpr int FB = FB_;
-  static constexpr int BM = 32, BN = 64, BKS = 128;  // tile rows, tile columns, K per stage
-  static constexpr int NWAVES = 8, T = 64 * NWAVES;
+  static constexpr int BM = 64, BN = 256, BKS = 128;  // tile rows, tile columns, K per stage
+  static constexpr int NWAVES = 4, T = 64 * NWAVES;
   static constexpr int W_ROW = BKS, A_ROW = BKS * 2;  // bytes per weight / lhs row in a stage
   static constexpr int W_BYTES = BN * W_ROW, A_BYTES = BM * A_ROW;
-  static constexpr int SLOT = 256;                    // per-wave scale / bias slot
-  static constexpr int SC_OFF = W_BYTES + A_BYTES, BI_OFF = SC_OFF + NWAVES * SLOT;
-  static constexpr int STAGE = BI_OFF + NWAVES * SLOT;
-  static constexpr int S = 6;
+  // the block's scales (256 f32) and the tile's bias (256 values): one
+  // 16-byte-per-lane load each, whose 64 lanes all write the slot
+  static constexpr int SLOT = 1024;
+  static constexpr int SC_OFF = W_BYTES + A_BYTES, BI_OFF = SC_OFF + SLOT;
+  static constexpr int STAGE = BI_OFF + SLOT;
+  static constexpr int S = 3;
   static constexpr int RING = S * STAGE;
-  static constexpr int XCHG = 4 * 2 * 64 * 16;  // partial totals passed between the two K halves
-  static constexpr int LDS = RING + XCHG;
-  static constexpr int OPS = 4;  // loads per wave and stage
-  static constexpr int E = 1;    // stores per wave and tile
+  static constexpr int LDS = RING;
+  static constexpr int W_OPS = W_BYTES / 1024 / NWAVES, A_OPS = A_BYTES / 1024 / NWAVES;
+  // loads per stage: waves 0 and 1 one more (the scales, the bias)
+  static constexpr int OPS_LO = W_OPS + A_OPS, OPS_HI = OPS_LO + 1;
+  static constexpr int FN = 4;  // 32-column blocks per wave
   static constexpr int es_out = OUT_F32 ? 4 : 2;
-  static_assert(W_BYTES == NWAVES * 1024 && A_BYTES == NWAVES * 1024, "one 1 KB load per wave and operand");
+  static constexpr int E = FN * (OUT_F32 ? 4 : 2);  // 16-byte stores per wave and tile
+  static_assert(W_OPS == 8 && A_OPS == 4, "load split");
 };
 
 // 128-byte weight rows: chunk c of row n at c ^ swz_w(n); 256-byte lhs rows:
-// chunk c of row r at c ^ (r & 15).  Sixteen consecutive rows read at one
-// logical chunk then land in distinct bank groups.
+// chunk c of row r at c ^ (r & 15).  Eight consecutive weight rows, or
+// sixteen consecutive lhs rows, read at one logical chunk then land in
+// distinct bank groups.
 __device__ __forceinline__ int swz_w(int n) { return (n & 7) ^ ((n >> 3) & 1); }
 __device__ __forceinline__ int swz_a(int r) { return r & 15; }
 
@@ -108,49 +121,65 @@ __device__ __forceinline__ StreamSrc stream_src(const Params& p, const StreamIte
   return s;
 }
 
-// Per-lane offsets of this wave's loads.  Weight: rows 8 w + lane/8, chunk
-// lane%8.  Lhs: rows 4 w + lane/16, chunk lane%16.  Scale: column
-// 16 (w%4) + lane for lanes < 16.  Bias: columns 16 (w%4) + 2 lane, +1 (bf16,
-// lanes < 8) or 16 (w%4) + lane (f32, lanes < 16).
+// Per-lane offsets of this wave's loads.  Its weight load i is load
+// j = 4 i + w of the stage: rows 8 j + lane/8, chunk lane%8.  Its lhs load
+// i is load j = 4 i + w: rows 4 j + lane/16, chunk lane%16.  Wave 0 also
+// loads the block's scales (lane: columns 4 lane .. +4) and wave 1 the bias
+// (lane: columns 8 lane .. +8 for bf16, lanes < 32; 4 lane .. +4 for f32).
+// The column test is made per tile (stream_stage).
 struct StreamOff {
-  int w, a, scol, bcol, bbyte;
+  int w[8], a[4], xcols;  // xcols: the first column of this lane's scale / bias chunk, or 1 << 20
 };
 
 template <class C>
 __device__ __forceinline__ StreamOff stream_offsets(int K, int w, int lane, bool bias_f32) {
   StreamOff o;
-  const int n = 8 * w + (lane >> 3);
-  o.w = n * K + (((lane & 7) ^ swz_w(n)) << 4);
-  const int r = 4 * w + (lane >> 4);
-  o.a = r * K * 2 + (((lane & 15) ^ swz_a(r)) << 4);
-  o.scol = lane < 16 ? 16 * (w & 3) + lane : 1 << 20;
-  if (bias_f32) {
-    o.bcol = lane < 16 ? 16 * (w & 3) + lane : 1 << 20;
-    o.bbyte = o.bcol * 4;
-  } else {
-    o.bcol = lane < 8 ? 16 * (w & 3) + 2 * lane : 1 << 20;
-    o.bbyte = o.bcol * 2;
+#pragma unroll
+  for (int i = 0; i < C::W_OPS; ++i) {
+    const int n = 8 * (4 * i + w) + (lane >> 3);
+    o.w[i] = n * K + (((lane & 7) ^ swz_w(n)) << 4);
   }
+#pragma unroll
+  for (int i = 0; i < C::A_OPS; ++i) {
+    const int r = 4 * (4 * i + w) + (lane >> 4);
+    o.a[i] = r * K * 2 + (((lane & 15) ^ swz_a(r)) << 4);
+  }
+  if (w == 1 && !bias_f32)
+    o.xcols = lane < 32 ? 8 * lane : 1 << 20;
+  else
+    o.xcols = 4 * lane;
   return o;
 }
 
-// The four loads of stage k (K elements [128 k, 128 k + 128), scale block
-// k) of a tile into LDS stage `st`.
+// The loads of stage k (K elements [128 k, 128 k + 128), scale block k) of
+// a tile into LDS stage `st`: every wave its weight and lhs rows, wave 0 the
+// block's scales, wave 1 the tile's bias.  N is a multiple of 8, so a
+// lane's 16-byte scale or bias chunk is all inside the tile's columns or
+// all outside.
 template <class C>
 __device__ __forceinline__ void stream_stage(const StreamSrc& s, const StreamOff& o, int k, int N, char* st, int w) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rw, (lds_ptr_t)(st + w * 1024), 16, o.w, k * C::W_ROW, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(s.ra, (lds_ptr_t)(st + C::W_BYTES + w * 1024), 16, o.a, k * C::A_ROW,
-                                           0, 0);
-  const int sv = o.scol < s.ncols ? o.scol * 4 : (int)0x80000000;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rs, (lds_ptr_t)(st + C::SC_OFF + w * C::SLOT), 4, sv, k * N * 4, 0,
-                                           0);
-  const int bv = o.bcol < s.ncols ? o.bbyte : (int)0x80000000;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rb, (lds_ptr_t)(st + C::BI_OFF + w * C::SLOT), 4, bv, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < C::W_OPS; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rw, (lds_ptr_t)(st + (4 * i + w) * 1024), 16, o.w[i],
+                                             k * C::W_ROW, 0, 0);
+#pragma unroll
+  for (int i = 0; i < C::A_OPS; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.ra, (lds_ptr_t)(st + C::W_BYTES + (4 * i + w) * 1024), 16,
+                                             o.a[i], k * C::A_ROW, 0, 0);
+  const int xv = o.xcols < s.ncols ? (int)(threadIdx.x & 63) * 16 : (int)0x80000000;
+  if (w == 0)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rs, (lds_ptr_t)(st + C::SC_OFF), 16, xv, k * N * 4, 0, 0);
+  else if (w == 1)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rb, (lds_ptr_t)(st + C::BI_OFF), 16, xv, 0, 0, 0);
 }
 
-template <int F>
-__device__ __forceinline__ i32x4 fp8x8_to_bf16x8_pk(uint32_t lo, uint32_t hi) {
-  return fp8x8_to_bf16x8<F>(i32x2{(int)lo, (int)hi});
+// s_waitcnt vmcnt for this wave: waves 0 and 1 issue one load more per stage.
+template <int N_LO, int N_HI>
+__device__ __forceinline__ void wait_stream(int w) {
+  if (w < 2)
+    wait_vmcnt<N_HI>();
+  else
+    wait_vmcnt<N_LO>();
 }
 
 template <class C>
@@ -166,8 +195,8 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wk = w >> 2, wc = w & 3;
-  const int r16 = lane & 15, q = lane >> 4;
+  const int wc = w & 1, wr = w >> 1;  // column half, row half of the tile
+  const int kh = lane >> 5, r32 = lane & 31;
   const int M = p.M, N = p.N, K = p.K;
   const int P = gridDim.x;
   const int slot = xcd_slot(blockIdx.x, P);
@@ -186,141 +215,187 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
     StreamSrc scur = stream_src<C>(p, cur, true), snxt = stream_src<C>(p, nxt, !last_item);
     const StreamOff off = stream_offsets<C>(K, w, lane, bias_f32);
 
-    // prologue: stages 0 .. S-2 of the first tile, then one range-dropped
-    // store in place of a previous tile's epilogue store, so that the first
-    // tile finds the same operations outstanding as every later one and the
+    // prologue: stages 0 .. S-2 of the first tile, then E range-dropped
+    // stores (each to an address of its own, so none is merged away) in
+    // place of a previous tile's epilogue stores, so that the first tile
+    // finds the same operations outstanding as every later one and the
     // loop's constant waits hold for it too.  Only stage 0 is waited for:
     // all workgroups ask for their first S-1 stages at once, and the last of
     // those arrive several microseconds after the first.
 #pragma unroll
     for (int st = 0; st < C::S - 1; ++st) stream_stage<C>(scur, off, st, N, smem + st * C::STAGE, w);
-    __builtin_amdgcn_raw_buffer_store_b32(0, uniform_rsrc(reinterpret_cast<const char*>(p.out), 0), (int)0x80000000,
-                                          0, 0);
-    wait_vmcnt<(C::S - 2) * C::OPS + C::E>();
+    {
+      const __amdgpu_buffer_rsrc_t rz = uniform_rsrc(reinterpret_cast<const char*>(p.out), 0);
+#pragma unroll
+      for (int e = 0; e < C::E; ++e)
+        __builtin_amdgcn_raw_buffer_store_b128(i32x4{0, 0, 0, 0}, rz, (int)0x80000000, 64 * e, 0);
+    }
+    wait_stream<(C::S - 2) * C::OPS_LO + C::E, (C::S - 2) * C::OPS_HI + C::E>(w);
     // a bare barrier, as in the loop: __syncthreads() carries a workgroup
     // fence, which the compiler meets by draining every load in flight
     ring_barrier();
 
-    // lane parts of the fragment addresses (stage-relative): weight row
-    // (output column) wn, K half wk -> 16-byte chunk 4 wk + q of the row;
-    // lhs rows 16 ch + r16, chunks 8 wk + 2 q + jj
-    const int wn = 16 * wc + r16;
-    const int w_off = wn * C::W_ROW + (((4 * wk + q) ^ swz_w(wn)) << 4);
-    int a_off[2][2];
+    // lane parts of the fragment addresses (stage-relative).  32x32x16 K
+    // step j of a stage (j = 0..7), lane half kh: K elements 64 kh + 8 j +
+    // [0, 8) of the stage -- weight bytes 8 j .. of the lane's 64-byte run
+    // (16-byte chunks 4 kh .. 4 kh + 3 of its column's 128-byte row), lhs
+    // chunk 8 kh + j of its row's 256-byte row.
+    int w_off[C::FN][4];
 #pragma unroll
-    for (int ch = 0; ch < 2; ++ch)
+    for (int fb = 0; fb < C::FN; ++fb) {
+      const int wn = 128 * wc + 32 * fb + r32;  // weight row = tile column
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int r = 16 * ch + r16;
-        a_off[ch][jj] = C::W_BYTES + r * C::A_ROW + (((8 * wk + 2 * q + jj) ^ swz_a(r)) << 4);
-      }
-    const int sc_off = C::SC_OFF + w * C::SLOT + 16 * q;
-    const int bi_off = C::BI_OFF + w * C::SLOT + (bias_f32 ? 16 * q : 8 * q);
-    // exchange slots: this wave's partial of the other half's rows, and the
-    // partner's partial of this wave's rows
-    char* const x_put = smem + C::RING + ((wc * 2 + (1 - wk)) * 64 + lane) * 16;
-    const char* const x_get = smem + C::RING + ((wc * 2 + wk) * 64 + lane) * 16;
+      for (int c = 0; c < 4; ++c) w_off[fb][c] = wn * C::W_ROW + (((4 * kh + c) ^ swz_w(wn)) << 4);
+    }
+    const int ar = 32 * wr + r32;  // lhs row of the tile
+    const int a_base = C::W_BYTES + ar * C::A_ROW;
+    const int a_swz = swz_a(ar);
+    // this lane's columns of block fb: 128 wc + 32 fb + 8 g + 4 kh + [0, 4), g = 0..3
+    const int col_l = 128 * wc + 4 * kh;
 
-    // a stage's fragments: the weight run (16 e4m3 = two K steps), lhs
-    // (two row chunks x two K steps), the block's scales of the lane's
-    // four columns
-    i32x4 fw, fa[2][2];
-    f32x4 fsc;
+    // a stage's fragments: the weight runs (64 one-byte values per column
+    // block), the lhs row (eight 16-byte chunks), the block's scales of the
+    // lane's columns
+    i32x4 fw[C::FN][4], fa[8];
+    f32x4 fsc[C::FN][4];
     auto read_frags = [&](const char* st) __attribute__((always_inline)) {
-      fw = *reinterpret_cast<const i32x4*>(st + w_off);
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch)
+      for (int fb = 0; fb < C::FN; ++fb)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) fa[ch][jj] = *reinterpret_cast<const i32x4*>(st + a_off[ch][jj]);
-      fsc = scaled ? *reinterpret_cast<const f32x4*>(st + sc_off) : f32x4{1.f, 1.f, 1.f, 1.f};
+        for (int c = 0; c < 4; ++c) fw[fb][c] = *reinterpret_cast<const i32x4*>(st + w_off[fb][c]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        fa[j] = *reinterpret_cast<const i32x4*>(st + a_base + (((8 * kh + j) ^ a_swz) << 4));
+#pragma unroll
+      for (int fb = 0; fb < C::FN; ++fb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          fsc[fb][g] = scaled ? *reinterpret_cast<const f32x4*>(st + C::SC_OFF + (col_l + 32 * fb + 8 * g) * 4)
+                              : f32x4{1.f, 1.f, 1.f, 1.f};
     };
 
     int stage = 0;
     read_frags(smem);  // stage 0 of the first tile
-    f32x4 tot[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    f32x16 tot[C::FN];
+#pragma unroll
+    for (int fb = 0; fb < C::FN; ++fb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tot[fb][i] = 0.f;
 
     // One stage kt of the current tile.  Stage kt+1's loads are complete
-    // (this wave's, then every wave's after the barrier) once at most WAIT
-    // newer operations are outstanding: stages kt+2 .. kt+S-2 (OPS each) and,
-    // in a tile's first S-2 stages, the previous tile's store.  The barrier
-    // also frees the stage kt-1 used, which takes stage kt+S-1 (of this tile,
-    // or kd of the next one when NEXT).  Stage kt's fragments (read during
-    // the previous stage) are multiplied, then the registers are refilled
-    // with stage kt+1's.
+    // (this wave's, then every wave's after the barrier) once at most the
+    // S-3 stages issued after it and, in a tile's first S-2 stages, the
+    // previous tile's E stores are outstanding.  The barrier also frees the
+    // slot stage kt-1 used, which takes stage kt+S-1 (of this tile, or kd of
+    // the next one when NEXT).  Stage kt's fragments (read into registers
+    // during the previous stage) are multiplied and folded with its scales
+    // and, in a tile's last stage, the outputs stored; then the registers
+    // are refilled with stage kt+1's fragments.  (Refilling a slot as soon
+    // as its stage is multiplied, which keeps one more stage in flight at
+    // each wait, measured no faster: 36.5 against 33.4 us per decode call.)
     auto kstage = [&](auto wait_tag, auto next_tag, int kt, int kd) __attribute__((always_inline)) {
-      constexpr int WAIT = decltype(wait_tag)::value;
+      constexpr bool WITH_E = decltype(wait_tag)::value;
       constexpr bool NEXT = decltype(next_tag)::value;
-      wait_vmcnt<WAIT>();
+      wait_stream<(C::S - 3) * C::OPS_LO + (WITH_E ? C::E : 0), (C::S - 3) * C::OPS_HI + (WITH_E ? C::E : 0)>(w);
       ring_barrier();
       stream_stage<C>(NEXT ? snxt : scur, off, kd, N, smem + ((stage + C::S - 1) % C::S) * C::STAGE, w);
-      // K step jj uses bytes 8 jj .. 8 jj + 7 of the lane's weight run
-      const i32x4 bw[2] = {fp8x8_to_bf16x8_pk<C::FB>((uint32_t)fw[0], (uint32_t)fw[1]),
-                           fp8x8_to_bf16x8_pk<C::FB>((uint32_t)fw[2], (uint32_t)fw[3])};
-#pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bw[jj]),
-                                                        __builtin_bit_cast(bf16x8, fa[ch][jj]), acc, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tot[ch][i] += acc[i] * fsc[i];
-      }
       const char* st = smem + stage * C::STAGE;
-      const int stage1 = stage + 1 == C::S ? 0 : stage + 1;
-      if (kt == KT - 1) {
-        // epilogue: the two K halves add their totals (each keeps rows
-        // 16 wk .. +16), then bias from this stage's slot, round, one store of
-        // the lane's four columns (out of range rows / columns drop)
-        *reinterpret_cast<f32x4*>(x_put) = tot[1 - wk];
-        __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));  // lgkmcnt(0)
-        ring_barrier();
-        const f32x4 other = *reinterpret_cast<const f32x4*>(x_get);
-        const f32x4 mine = wk ? tot[1] : tot[0];
-        float v[4];
-        float bias[4] = {0.f, 0.f, 0.f, 0.f};
-        if (p.rhs_bias) {
-          if (bias_f32) {
-            const f32x4 b4 = *reinterpret_cast<const f32x4*>(st + bi_off);
-            bias[0] = b4[0];
-            bias[1] = b4[1];
-            bias[2] = b4[2];
-            bias[3] = b4[3];
-          } else {
-            const i32x2 b2 = *reinterpret_cast<const i32x2*>(st + bi_off);
-            bias[0] = __uint_as_float((uint32_t)b2[0] << 16);
-            bias[1] = __uint_as_float((uint32_t)b2[0] & 0xFFFF0000u);
-            bias[2] = __uint_as_float((uint32_t)b2[1] << 16);
-            bias[3] = __uint_as_float((uint32_t)b2[1] & 0xFFFF0000u);
-          }
-        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = mine[i] + other[i] + bias[i];
+      for (int fb = 0; fb < C::FN; ++fb) {
+        f32x16 acc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          // weight bytes 16 c .. 16 c + 15 of the run: K steps 2 c, 2 c + 1
+          const i32x4 bw0 = fp8x8_to_bf16x8<C::FB>(i32x2{fw[fb][c][0], fw[fb][c][1]});
+          const i32x4 bw1 = fp8x8_to_bf16x8<C::FB>(i32x2{fw[fb][c][2], fw[fb][c][3]});
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bw0),
+                                                        __builtin_bit_cast(bf16x8, fa[2 * c]), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bw1),
+                                                        __builtin_bit_cast(bf16x8, fa[2 * c + 1]), acc, 0, 0, 0);
+        }
+        // register 4 g + i holds column 8 g + 4 kh + i of the block for the lane's row
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tot[fb][4 * g + i] += acc[4 * g + i] * fsc[fb][g][i];
+      }
+      if (kt == KT - 1) {
+        // epilogue: bias from this stage's slot (its next use is past the
+        // barrier below), round, and a permlane32 swap per pair of column
+        // groups so that each lane stores eight consecutive columns of its
+        // row with one 16-byte store (two for an f32 output); out-of-range
+        // rows and columns drop
         char* tile = reinterpret_cast<char*>(p.out) + ((long long)cur.row0 * N + cur.n0) * C::es_out;
         const __amdgpu_buffer_rsrc_t ro = uniform_rsrc(tile, ((cur.rows - 1) * N + cur.ncols) * C::es_out);
-        const int col = 16 * wc + 4 * q;
-        const int row = 16 * wk + r16;
-        const int voff = col < cur.ncols ? (row * N + col) * C::es_out : (int)0x80000000;
-        if constexpr (C::OUT_F32) {
-          __builtin_amdgcn_raw_buffer_store_b128(
-              i32x4{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3])}, ro,
-              voff, 0, 0);
-        } else {
-          const uint32_t x0 = pk_bf16_rne(v[0], v[1]);
-          const uint32_t x1 = pk_bf16_rne(v[2], v[3]);
-          __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)x0, (int)x1}, ro, voff, 0, 0);
+        const int row = 32 * wr + r32;
+#pragma unroll
+        for (int fb = 0; fb < C::FN; ++fb) {
+          float v[16];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float b[4] = {0.f, 0.f, 0.f, 0.f};
+            const int cb = col_l + 32 * fb + 8 * g;  // first of the lane's four columns
+            if (p.rhs_bias) {
+              if (bias_f32) {
+                const f32x4 b4 = *reinterpret_cast<const f32x4*>(st + C::BI_OFF + cb * 4);
+                b[0] = b4[0];
+                b[1] = b4[1];
+                b[2] = b4[2];
+                b[3] = b4[3];
+              } else {
+                const i32x2 b2 = *reinterpret_cast<const i32x2*>(st + C::BI_OFF + cb * 2);
+                b[0] = __uint_as_float((uint32_t)b2[0] << 16);
+                b[1] = __uint_as_float((uint32_t)b2[0] & 0xFFFF0000u);
+                b[2] = __uint_as_float((uint32_t)b2[1] << 16);
+                b[3] = __uint_as_float((uint32_t)b2[1] & 0xFFFF0000u);
+              }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[4 * g + i] = tot[fb][4 * g + i] + b[i];
+          }
+#pragma unroll
+          for (int gp = 0; gp < 4; gp += 2) {
+            // after the swap: kh = 0 holds columns 8 gp + [0, 8) of the
+            // block, kh = 1 holds 8 (gp + 1) + [0, 8)
+            const int col = 128 * wc + 32 * fb + 8 * (gp + kh);
+            const int voff = col < cur.ncols ? (row * N + col) * C::es_out : (int)0x80000000;
+            if constexpr (C::OUT_F32) {
+              int lo[4], hi[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[4 * gp + i]),
+                                                                __float_as_uint(v[4 * gp + 4 + i]), false, false);
+                lo[i] = (int)r[0];
+                hi[i] = (int)r[1];
+              }
+              __builtin_amdgcn_raw_buffer_store_b128(i32x4{lo[0], lo[1], lo[2], lo[3]}, ro, voff, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(i32x4{hi[0], hi[1], hi[2], hi[3]}, ro, voff, 16, 0);
+            } else {
+              const uint32_t x00 = pk_bf16_rne(v[4 * gp], v[4 * gp + 1]);
+              const uint32_t x01 = pk_bf16_rne(v[4 * gp + 2], v[4 * gp + 3]);
+              const uint32_t x10 = pk_bf16_rne(v[4 * gp + 4], v[4 * gp + 5]);
+              const uint32_t x11 = pk_bf16_rne(v[4 * gp + 6], v[4 * gp + 7]);
+              const auto r0 = __builtin_amdgcn_permlane32_swap(x00, x10, false, false);
+              const auto r1 = __builtin_amdgcn_permlane32_swap(x01, x11, false, false);
+              __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1]}, ro,
+                                                     voff, 0, 0);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) tot[fb][i] = 0.f;
         }
-        tot[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        tot[1] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      const int stage1 = stage + 1 == C::S ? 0 : stage + 1;
       read_frags(smem + stage1 * C::STAGE);
       stage = stage1;
     };
-    using WE = std::integral_constant<int, (C::S - 3) * C::OPS + C::E>;
-    using WN = std::integral_constant<int, (C::S - 3) * C::OPS>;
+    using WE = std::true_type;   // the previous tile's stores are among the newer operations
+    using WN = std::false_type;
     using CUR = std::false_type;
     using NXT = std::true_type;
-    // stages kt < S-2 wait for the previous tile's store too; stages
+    // stages kt < S-2 wait for the previous tile's stores too; stages
     // kt >= KT-S+1 load the next tile's first stages
     const int e_end = C::S - 2, n_beg = KT - C::S + 1;
 

@@ -45,7 +45,7 @@ FAMILIES = [
     ("moe_fwd_bf16", 2, "big kernel, NT", (256, 256)),
     ("moe_dlhs_bf16", 2, "big kernel, NN in place", (256, 256)),
     ("w8a8_fp8", 2, "W8A8 ring kernel", (256, 128)),
-    ("decode_fp8w", 1, "weight-streaming kernel", (32, 64)),
+    ("decode_fp8w", 1, "weight-streaming kernel", (64, 256)),
     ("decode_fp8w", 2, "general kernel, big scaled tiles", (256, 128)),
     ("tiny_fp32", 0, "general kernel, f32", (64, 64)),
 ]

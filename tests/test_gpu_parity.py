@@ -430,7 +430,7 @@ STREAM_CASES = [
     (48, 896, 640, torch.float32, "f32", True),
     (48, 1024, 192, torch.bfloat16, None, False),
     (48, 768, 256, torch.bfloat16, "bf16", "blk256"),
-    (48, 640, 136, torch.bfloat16, "bf16", True),
+    (48, 384, 136, torch.bfloat16, "bf16", True),
     (600, 1152, 264, torch.float32, "bf16", True),
 ]
 
@@ -476,17 +476,16 @@ def test_weight_streaming_kernel_mostly_inactive_rows():
 
 
 @pytest.mark.parametrize("tokens,K,N,out_dtype,bias,scaled", STREAM_CASES,
-                         ids=["bf16out_bias", "f32out_f32bias", "noscale_nobias", "blk256", "k640_n136",
-                              "rows_over_32"])
+                         ids=["bf16out_bias", "f32out_f32bias", "noscale_nobias", "blk256", "k384_n136",
+                              "rows_over_64"])
 def test_weight_streaming_kernel(tokens, K, N, out_dtype, bias, scaled):
-    """bf16 x e4m3 with few rows per group and K >= 768 runs the weight-streaming
+    """bf16 x e4m3 with few rows per group and K >= 384 runs the weight-streaming
     kernel: every element against the oracle, with empty groups, a group
-    offset, N tails (N not a multiple of the 64-column tile, down to 8
-    columns past it), the fewest K stages the kernel takes (six), groups of
-    more than one 32-row tile, rows outside the active groups, f32 and bf16
-    outputs and biases, and no scale.  K = 640 (below its minimum) and scale
-    blocks of two K stages run on the general kernel, against the same
-    oracle."""
+    offset, N tails (N not a multiple of the 256-column tile, down to 8
+    columns past one), the fewest K stages the kernel takes (three,
+    K = 384), groups of more than one 64-row tile, rows outside the active
+    groups, f32 and bf16 outputs and biases, and no scale.  Scale blocks of
+    two K stages run on the general kernel, against the same oracle."""
     import moe_grouped_matrix_amd as m
     m.set_tile_policy(0)
     case = workloads.decode_fp8_weight(tokens=tokens, experts=24, K=K, N=N, forced_empty=8,

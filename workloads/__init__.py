@@ -395,7 +395,7 @@ SMALL = {
     "moe_dlhs_bf16": lambda device="cpu": moe_dlhs_bf16(
         device=device, tokens=384, experts=16, K=576, N=320, sizes_seed=77),
     "decode_fp8w": lambda device="cpu": decode_fp8_weight(
-        device=device, tokens=64, experts=32, K=512, N=640, forced_empty=12,
+        device=device, tokens=64, experts=32, K=768, N=640, forced_empty=12,
         group_offset=8, num_active=16),
     "w8a8_fp8": lambda device="cpu": w8a8_fp8(
         device=device, tokens=384, experts=16, K=512, N=320, sizes_seed=77),
