@@ -69,12 +69,19 @@ struct BigCfg {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // 64-byte LDS rows: 16-byte chunk c of row r is stored at chunk c ^ swz64(r).
-// Eight consecutive rows read at one logical chunk cover all 32 banks.
-__device__ __forceinline__ int swz64(int r) { return (r >> 1) & 3; }
-// 512-byte K rows of an N-contiguous weight: chunk c of K row k is stored at
-// chunk c ^ swzkn(k).  A transpose read of four K rows x 16 columns then
-// touches eight distinct 16-byte bank groups.
-__device__ __forceinline__ int swzkn(int k) { return 2 * (k & 3); }
+// Four rows share a 256-byte line of the 64 banks (rows r, r + 4, r + 8,
+// r + 12 the same quarter of it) and two a 128-byte half: the swizzle gives
+// rows 0, 4, 8, 12 and rows 0, 2, 4, 6 (and their shifts) four distinct
+// chunks, so sixteen consecutive rows read at one logical chunk hit sixteen
+// distinct 16-byte bank groups, and any eight consecutive ones eight.
+__device__ __forceinline__ int swz64(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | (r & 4) >> 1; }
+// 512-byte K rows of an N-contiguous operand (the big kernel's [G,K,N]
+// weight, both operands of the weight gradient): chunk c of K row k is
+// stored at chunk c ^ swz_nn(k).  The 32 lanes an LDS cycle serves
+// in a transpose read cover four K rows (512 bytes apart, so the same bank
+// offsets) by four chunks each; the swizzle moves the four rows to the four
+// quarters of the 64 banks.
+__device__ __forceinline__ int swz_nn(int k) { return 4 * (k & 3); }
 
 struct BigItem {
   int h, row0, rows, n0, ncols;
@@ -174,7 +181,7 @@ __device__ __forceinline__ DmaOff dma_offsets(int K, int N, int w, int lane) {
     d.a[i] = r * K * 2 + (((lane & 3) ^ swz64(r)) << 4);
     if constexpr (C::NN) {
       const int k = 4 * w + 2 * i + (lane >> 5);
-      const int c = (lane & 31) ^ swzkn(k);
+      const int c = (lane & 31) ^ swz_nn(k);
       d.b[i] = k * N * 2 + c * 16;
       d.bcol[i] = c * 8;
     } else {
@@ -294,12 +301,12 @@ __device__ __forceinline__ int frag_lane_off(int kh, int r32, int h) {
 // of the block; the read hands lane l column l % 32 at K rows
 // 16 h + 8 (l / 32) + 4 t + [0, 4).  The lane part of the address is
 // nn_lane_off(fn) for a block at column 0 of a 128-column half; the swizzle
-// flips chunk bit 3, so a block at column 64 mod 128 XORs that bit (byte
-// 128) into the lane part.  The K half and read add 512 (16 h + 4 t).
+// flips chunk bits 2 and 3, so a block at column 64 mod 128 XORs bit 3
+// (byte 128) into the lane part.  The K half and read add 512 (16 h + 4 t).
 __device__ __forceinline__ int nn_lane_off(int lane, int fn) {
   const int q = lane >> 4, j = lane & 15;
   const int krow = 8 * (q >> 1) + (j >> 2);
-  const int chunk = (4 * fn + 2 * (q & 1) + ((j >> 1) & 1)) ^ swzkn(j >> 2);
+  const int chunk = (4 * fn + 2 * (q & 1) + ((j >> 1) & 1)) ^ swz_nn(j >> 2);
   return krow * 512 + chunk * 16 + (j & 1) * 8;
 }
 

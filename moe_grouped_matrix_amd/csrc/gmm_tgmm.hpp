@@ -162,7 +162,7 @@ __device__ __forceinline__ TgDma tg_dma(const Params& p, const TgItem& it, bool 
 // This lane's offsets: instruction i of a wave fills contraction row
 // 4 w + 2 i + lane / 32 of the step, 16-byte chunk lane % 32 of the row,
 // which holds the tile's columns 8 c .. 8 c + 7 with c = (lane % 32) ^
-// swzkn(row).
+// swz_nn(row).
 struct TgOff {
   int a[2], b[2];
 };
@@ -172,7 +172,7 @@ __device__ __forceinline__ TgOff tg_offsets(int K, int N, int w, int lane) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = 4 * w + 2 * i + (lane >> 5);
-    const int c = (lane & 31) ^ swzkn(r);
+    const int c = (lane & 31) ^ swz_nn(r);
     o.a[i] = r * K * 2 + c * 16;
     o.b[i] = r * N * 2 + c * 16;
   }
