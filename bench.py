@@ -39,7 +39,7 @@ KERNEL_SOURCES = {
     "moe_fwd_bf16": ("gmm_big.hpp",),
     "moe_dlhs_bf16": ("gmm_big.hpp",),
     "decode_fp8w": ("gmm_big.hpp", "gmm_stream.hpp"),
-    "w8a8_fp8": ("gmm_big.hpp", "gmm_w8a8.hpp"),
+    "w8a8_fp8": ("gmm_big.hpp", "gmm_w8a8.hpp", "gmm_w8a8.hip"),
     "tgmm_bf16": ("gmm_big.hpp", "gmm_tgmm.hpp"),
     "quant_fp8": ("gmm_quant.hip",),
 }

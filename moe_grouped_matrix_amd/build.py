@@ -12,13 +12,17 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgmm.so")
-SOURCES = [os.path.join(CSRC, "gmm_kernels.hip"), os.path.join(CSRC, "gmm_quant.hip"),
-           os.path.join(CSRC, "gmm_api.cpp")]
+SOURCES = [os.path.join(CSRC, "gmm_kernels.hip"), os.path.join(CSRC, "gmm_w8a8.hip"),
+           os.path.join(CSRC, "gmm_quant.hip"), os.path.join(CSRC, "gmm_api.cpp")]
 
 # Packed fp32 VALU instructions are kept out of the generated code.
-HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-Wno-unused-command-line-argument"]
+
+# Per-source additions: the block-scaled fp8 kernel keeps its MFMA results
+# in ordinary VGPRs, where its fold reads them.
+EXTRA_FLAGS = {"gmm_w8a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -28,15 +32,41 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I" + os.path.join(HERE, "..", "include")] + SOURCES + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link."""
+    tag = ".tmp%d" % os.getpid()
+    inc = "-I" + os.path.join(HERE, "..", "include")
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(CSRC, os.path.basename(src) + tag + ".o")
+        cmd = [hipcc()] + HIPCC_FLAGS + EXTRA_FLAGS.get(os.path.basename(src), []) + [inc, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        objs.append(obj)
+    errors = []
+    for cmd, pr in procs:
+        out, err = pr.communicate()
+        if pr.returncode != 0:
+            errors.append(" ".join(cmd) + "\n" + out + err)
+    try:
+        if errors:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
+        tmp = LIB + tag
+        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 

@@ -898,28 +898,4 @@ __global__ __launch_bounds__(C::T) void gmm_kernel(Params p) {
   }
 }
 
-// The plan-building device code above, run on its own to export the tiles.
-__global__ __launch_bounds__(256) void worklist_kernel(Params p, int tm, int32_t* tiles,
-                                                       long long capacity, int32_t* count) {
-  __shared__ Plan pl;
-  if (threadIdx.x == 0) pl.flags = 0;
-  __syncthreads();
-  build_plan<256>(p, pl, tm);
-  for (int t = threadIdx.x; t < pl.n_mtiles; t += 256) {
-    if (t >= capacity) break;
-    const int h = find_group(pl, t);
-    const int row0 = pl.row_start[h] + (t - pl.tile_start[h]) * tm;
-    const int left = pl.row_start[h + 1] - row0;
-    tiles[3 * t + 0] = pl.s + h;
-    tiles[3 * t + 1] = row0;
-    tiles[3 * t + 2] = left < tm ? left : tm;
-  }
-  if (threadIdx.x == 0) {
-    count[0] = pl.n_mtiles;
-    count[1] = pl.row_start[0];
-    count[2] = pl.row_start[pl.ga];
-    count[3] = (int)pl.flags;
-  }
-}
-
 }  // namespace gmmk

@@ -5,7 +5,6 @@
 #include "gmm_big.hpp"
 #include "gmm_device.hpp"
 #include "gmm_stream.hpp"
-#include "gmm_w8a8.hpp"
 #include "gmm_tgmm.hpp"
 #include "gmm_launch.hpp"
 
@@ -106,24 +105,6 @@ hipError_t launch_stream(const Params& p, int cu_count, int cap, hipStream_t str
   return hipGetLastError();
 }
 
-// The block-scaled fp8 x fp8 ring kernel: one workgroup per CU (its ring
-// takes most of the LDS), at most one per work item.
-template <class C>
-hipError_t launch_w8a8(const Params& p, int cu_count, int cap, hipStream_t stream) {
-  const long long n_tiles = (p.N + C::BN - 1) / C::BN;
-  const long long m_tiles = (p.M + C::BM - 1) / C::BM + p.Ga;
-  const long long row_bytes = (long long)p.N * (p.out_f32 ? 4 : 2);
-  const long long zero_items = ((long long)p.M * row_bytes + kZeroChunk - 1) / kZeroChunk + 2;
-  const long long bound = m_tiles * n_tiles + zero_items;
-  long long grid = cu_count;
-  if (grid > bound) grid = bound;
-  if (grid >= 8) grid -= grid % 8;
-  if (grid < 1) grid = 1;
-  grid = apply_cap(grid, cap);
-  hipLaunchKernelGGL(gmm_w8a8_kernel<C>, dim3((unsigned)grid), dim3(C::T), 0, stream, p);
-  return hipGetLastError();
-}
-
 // The weight-streaming kernel takes bf16 x e4m3 NT problems with few rows per
 // group: K in stages of 128 with at least S of them per tile, and scale
 // blocks of exactly one stage (or no scale).
@@ -168,8 +149,7 @@ hipError_t by_size(const Params& p, const KernelChoice& kc, int cu, hipStream_t 
   }
   // W8A8 (one-byte fp8 operands) with scale blocks of one K step
   if constexpr (OP == Op::FP8 && !NN && SC && (FMT & 7) <= 1 && (FMT >> 3) <= 1) {
-    using CB = typename Pick<OP, NN, BF8, SC, SizeClass::Big, FMT>::type;
-    if (sz == SizeClass::Big && p.blk == CB::BK) return launch_w8a8<CB>(p, cu, cap, st);
+    if (sz == SizeClass::Big && w8a8_fits(p)) return launch_w8a8(p, FMT & 7, FMT >> 3, cu, cap, st);
   }
   if (sz == SizeClass::Big)
     return launch_cfg<typename Pick<OP, NN, BF8, SC, SizeClass::Big, FMT>::type>(p, cu, cap, st);
@@ -271,6 +251,31 @@ hipError_t launch_gmm(const Params& p, const KernelChoice& c, int cu, hipStream_
 hipError_t launch_tgmm(const Params& p, int cu, int cap, hipStream_t st) {
   if (p.out_f32) return launch_tgmm_cfg<TgCfg<true>>(p, cu, cap, st);
   return launch_tgmm_cfg<TgCfg<false>>(p, cu, cap, st);
+}
+
+// The plan-building device code of the kernels, run on its own to export
+// the tiles.
+__global__ __launch_bounds__(256) void worklist_kernel(Params p, int tm, int32_t* tiles,
+                                                       long long capacity, int32_t* count) {
+  __shared__ Plan pl;
+  if (threadIdx.x == 0) pl.flags = 0;
+  __syncthreads();
+  build_plan<256>(p, pl, tm);
+  for (int t = threadIdx.x; t < pl.n_mtiles; t += 256) {
+    if (t >= capacity) break;
+    const int h = find_group(pl, t);
+    const int row0 = pl.row_start[h] + (t - pl.tile_start[h]) * tm;
+    const int left = pl.row_start[h + 1] - row0;
+    tiles[3 * t + 0] = pl.s + h;
+    tiles[3 * t + 1] = row0;
+    tiles[3 * t + 2] = left < tm ? left : tm;
+  }
+  if (threadIdx.x == 0) {
+    count[0] = pl.n_mtiles;
+    count[1] = pl.row_start[0];
+    count[2] = pl.row_start[pl.ga];
+    count[3] = (int)pl.flags;
+  }
 }
 
 hipError_t launch_worklist(const Params& p, int tm, int32_t* tiles, long long capacity,

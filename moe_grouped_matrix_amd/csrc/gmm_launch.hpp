@@ -36,6 +36,17 @@ int tile_m(const KernelChoice& c);
 // Queue the gmm kernel.  Returns hipSuccess or the launch error.
 hipError_t launch_gmm(const Params& p, const KernelChoice& c, int cu_count, hipStream_t stream);
 
+// The block-scaled fp8 x fp8 kernel (gmm_w8a8.hip) takes scale blocks of
+// one K step of 128 with both scales given, at least three K steps (its
+// cross-tile load pipeline runs three steps ahead) and N a multiple of 4 (a
+// lane stores four consecutive columns).
+inline bool w8a8_fits(const Params& p) {
+  return p.lhs_scale && p.rhs_scale && p.blk == 128 && p.K >= 3 * 128 && p.K % 128 == 0 && p.N % 4 == 0;
+}
+
+// Queue it for lhs format fa and rhs format fb (0 e4m3fn, 1 e5m2).
+hipError_t launch_w8a8(const Params& p, int fa, int fb, int cu_count, int grid_cap, hipStream_t stream);
+
 // Queue the transposed grouped matmul (out [Ga,K,N]); grid_cap > 0 limits
 // the workgroups.
 hipError_t launch_tgmm(const Params& p, int cu_count, int grid_cap, hipStream_t stream);

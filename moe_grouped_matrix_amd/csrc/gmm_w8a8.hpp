@@ -1,82 +1,203 @@
-// gmm_w8a8.hpp -- the block-scaled fp8 x fp8 grouped matmul (W8A8) with a
-// direct-to-LDS operand ring, for large problems whose scale blocks are one
-// K step (128 elements).
+// gmm_w8a8.hpp -- the block-scaled fp8 x fp8 grouped matmul (W8A8) for large
+// problems whose scale blocks are one K step of 128 elements:
 //
-// The arithmetic is the general kernel's for the same configuration
-// (gmm_device.hpp, Cfg<FP8, NT, ..., 256, 128, 4, 2, scaled>): 256 x 128
-// group-aligned tiles, eight waves of 64 x 64, v_mfma_scale_f32_16x16x128
-// with unit scales, and after each K step (one quantisation block) the fold
-// tot += part * rhs_scale[col] * lhs_scale[row]; bias, rounding and the
-// staged epilogue are the same code.  What differs is how operands reach
-// LDS.  The general kernel loads a step into registers and writes them to
-// LDS after the multiply, so a step's loads have one step of multiplies to
-// arrive.  Here three LDS stages form a ring filled by direct-to-LDS buffer
-// loads two steps ahead, with the block's scales in the same stage:
+//   out[r, n] = bias[h, n] + sum_b ls[r, b] rs[h, b, n] sum_{k in block b} x[r, k] w[h, n, k]
 //
-//   per wave and step: 4 lhs loads (1 KB each: 8 rows of 128 bytes), 2
-//   weight loads, and 1 scale load (waves 0-3: 64 row scales each, waves
-//   4-5: 64 column scales each, waves 6-7: a range-dropped load into a slot
-//   nobody reads, so that every wave counts the same 7 operations).
+// (the quantised matmul of the Megablox gmm with per-token activation and
+// per-channel weight scales, one pair per K block).
 //
-// At the top of step kt each wave waits until only step kt+1's 7 loads are
-// outstanding (or none, in a tile's last step), then a bare barrier makes
-// every wave's loads of stage kt visible and frees the stage step kt-1 read,
-// which takes step kt+2's loads.  Each lane loads the global chunk that the
-// LDS swizzle puts at its position (a load writes 64 lanes x 16 bytes in
-// lane order), so the stage has the layout the multiply reads.
+// Per K step and 16 x 16 output block the work is one 16x16x128 f8f6f4 MFMA
+// (32 cycles of the matrix core) and the fold tot += acc * (ls * rs) -- a
+// multiply and an FMA for each of the block's 256 values, 8 VALU
+// instructions of 4 cycles each on a wave64.  The two units cost the same,
+// so the kernel is built to run them side by side: one wave per SIMD, and
+// within the wave each row block's four MFMAs issue between the fold of the
+// previous row block, while the next K step's fragments stream from LDS into
+// a second register set.
+//
+// Layout: output tiles of 256 tokens x 128 columns (group-aligned in M, as
+// in the general kernel); four waves of 128 x 64 (FM = 8 token blocks by
+// FN = 4 column blocks).  The MFMA's first operand is the weight fragment,
+// so a lane's four results are four consecutive columns of one token and
+// the epilogue stores them straight from registers (8 or 16 bytes per lane
+// and block; an L2 line collects the four 32-byte pieces of a row segment
+// before it is written back).
+//
+// Staging: a K step of both operands (32 KB tokens + 16 KB weights) fills
+// one of three LDS stages by direct-to-LDS buffer loads; its scales (256 row
+// and 128 column scales) one of four scale slots; the tile's bias row one of
+// two bias slots.  The loads of global step g + 3 (across the workgroup's
+// tiles) are issued at step g into stage g % 3, which the waves finished
+// reading into registers during step g - 1 -- the registers are the ring's
+// fourth stage.  Per wave and step that is 14 loads: 8 token-row loads and
+// 4 weight-row loads of 1 KB, one load of 64 row scales, and one of 64
+// column scales (waves 0-1) or of half the tile's bias row (waves 2-3),
+// spread over the step's MFMAs.  Every wave issues the same operations in
+// every step (loads of a missing tile or scale are dropped by the range
+// check), and every tile's epilogue issues the same number of stores (16
+// for bf16 output, 32 for f32), so the waits are constants: at the top of step
+// g the loads of step g + 1 are complete once only those of step g + 2 are
+// outstanding, and in a tile's first two steps also the previous tile's
+// stores.
 #pragma once
 
 #include "gmm_big.hpp"
 
 namespace gmmk {
 
-template <class C>
-struct W8A8Ring {
-  static_assert(C::op == Op::FP8 && !C::NN && C::SCALED && C::T == 512 && C::BM == 256 && C::BN == 128,
-                "the W8A8 ring serves the large scaled fp8 configuration");
-  static constexpr int A_OPS = C::A_BYTES / 1024 / 8, B_OPS = C::B_BYTES / 1024 / 8;
-  static constexpr int OPS = A_OPS + B_OPS + 1;  // + one scale load
-  static constexpr int LSC = C::A_BYTES + C::B_BYTES;  // 256 row scales
-  static constexpr int RSC = LSC + C::BM * 4;          // 128 column scales
-  static constexpr int DUMMY = RSC + C::BN * 4;        // the range-dropped loads' slot
-  static constexpr int STAGE = DUMMY + 256;
-  static constexpr int S = 3;
-  static constexpr int LDS = S * STAGE;
-  static_assert(A_OPS == 4 && B_OPS == 2, "DMA split");
-  static_assert(C::T / 64 * kStageSlice<C> <= LDS, "epilogue staging fits the ring");
+template <int FA_, int FB_, bool OUT_F32_>
+struct W8Cfg {
+  static constexpr int FA = FA_, FB = FB_;  // f8f6f4 format codes: 0 e4m3fn, 1 e5m2
+  static constexpr bool OUT_F32 = OUT_F32_;
+  static constexpr int BM = 256, BN = 128, BK = 128;
+  static constexpr int NWAVES = 4, T = 64 * NWAVES;
+  static constexpr int TM = 128, TN = 64;  // wave tile: tokens x columns
+  static constexpr int FM = TM / 16, FN = TN / 16;
+  static constexpr int X_BYTES = BM * 128, W_BYTES = BN * 128;
+  static constexpr int STAGE = X_BYTES + W_BYTES;
+  static constexpr int S = 3;                  // operand stages
+  static constexpr int SS = 4;                 // scale slots
+  static constexpr int SLOT = (BM + BN) * 4;   // row scales, then column scales
+  static constexpr int BIAS_SLOT = BN * 4;     // a tile's bias row (f32 or bf16)
+  static constexpr int SCALES = S * STAGE;
+  static constexpr int BIASES = SCALES + SS * SLOT;
+  static constexpr int LDS = BIASES + 2 * BIAS_SLOT;
+  static constexpr int X_OPS = X_BYTES / 1024 / NWAVES, W_OPS = W_BYTES / 1024 / NWAVES;
+  static constexpr int OPS = X_OPS + W_OPS + 2;  // + row scales + column scales or bias
+  static constexpr int E = OUT_F32 ? FM * FN : FM * FN / 2;  // epilogue stores per wave and tile
+  static constexpr int es_out = OUT_F32 ? 4 : 2;
+  static_assert(X_OPS == 8 && W_OPS == 4, "load split");
+  static_assert(2 * OPS + E < 64, "vmcnt range");
+  static_assert(LDS + (int)sizeof(Plan) <= 160 * 1024, "LDS");
 };
 
-// The loads of K step k into stage `st`: A_OPS lhs, B_OPS weight and one
-// scale load (row scales step by one block, 4 bytes; column scales by N of
-// them).  A device function, not a lambda in the kernel: a lambda there is
-// also compiled for the host, where these builtins do not exist, and the
-// kernel's host-side launch stub would silently not be emitted.
+// 128-byte operand rows in the stages: chunk c of row r at chunk c ^ (r % 8).
+// The fragment reads (lane q * 16 + r16 reads row base + r16 at chunk q, and
+// at chunk q + 4) then run without bank conflicts; the general kernel's
+// swizzle (r ^ r / 8) % 8 costs four conflict cycles per read in this lane
+// order (both measured on gfx950 with the LDS bank-conflict counter).
+__device__ __forceinline__ int w8_swz(int r) { return r & 7; }
+__device__ __forceinline__ int w8_off(int r, int c) { return r * 128 + ((c ^ w8_swz(r)) << 4); }
+
+struct W8Tile {
+  int h, row0, rows, n0, ncols;
+};
+
 template <class C>
-__device__ __forceinline__ void w8a8_issue(char* st, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                           __amdgpu_buffer_rsrc_t rsc, const int (&aoff)[W8A8Ring<C>::A_OPS],
-                                           const int (&boff)[W8A8Ring<C>::B_OPS], int soff, int sdst, int k, int w,
-                                           int N) {
-  using R = W8A8Ring<C>;
+__device__ __forceinline__ W8Tile w8_tile(const Plan& pl, int L, int n_ntiles, int N) {
+  W8Tile t;
+  const int mt = L / n_ntiles, j = L % n_ntiles;
+  const int h = find_group(pl, mt);
+  const int row0 = pl.row_start[h] + (mt - pl.tile_start[h]) * C::BM;
+  const int left = pl.row_start[h + 1] - row0;
+  t.h = __builtin_amdgcn_readfirstlane(h);
+  t.row0 = __builtin_amdgcn_readfirstlane(row0);
+  t.rows = __builtin_amdgcn_readfirstlane(left < C::BM ? left : C::BM);
+  t.n0 = __builtin_amdgcn_readfirstlane(j * C::BN);
+  t.ncols = __builtin_amdgcn_readfirstlane(N - t.n0 < C::BN ? N - t.n0 : C::BN);
+  return t;
+}
+
+// Buffer resources of one tile's loads; a tile that does not exist (past the
+// workgroup's last) has empty ranges, so its loads are dropped.
+struct W8Src {
+  __amdgpu_buffer_rsrc_t x, w, ls, rs_or_bias;
+};
+
+// Per-lane parts of this wave's load offsets (the K step adds a scalar).
+// Token-row load j fills stage rows 8 (8 w + j) + lane / 8, weight-row load
+// j rows 8 (4 w + j) + lane / 8; lane position lane % 8 of a row holds
+// logical chunk (lane % 8) ^ w8_swz(row).  The row-scale load puts token t(p)
+// at position p = 64 w + lane of the slot, t(p) = 128 (p / 128) +
+// 16 (p % 8) + (p % 128) / 8, so that a lane's eight row scales (its token
+// in each of the wave's eight row blocks) are 32 contiguous bytes.
+struct W8Off {
+  int x[8], w[4];
+  int ls, small;  // row scale; column scale (waves 0-1) or bias (waves 2-3)
+};
+
+template <class C>
+__device__ __forceinline__ W8Off w8_offsets(int K, int nb, int w, int lane) {
+  W8Off o;
 #pragma unroll
-  for (int jj = 0; jj < R::A_OPS; ++jj)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(st + (R::A_OPS * w + jj) * 1024), 16, aoff[jj],
-                                             k * C::BK, 0, 0);
+  for (int j = 0; j < C::X_OPS; ++j) {
+    const int r = 8 * (C::X_OPS * w + j) + (lane >> 3);
+    o.x[j] = r * K + (((lane & 7) ^ w8_swz(r)) << 4);
+  }
 #pragma unroll
-  for (int jj = 0; jj < R::B_OPS; ++jj)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(st + C::A_BYTES + (R::B_OPS * w + jj) * 1024), 16,
-                                             boff[jj], k * C::BK, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (lds_ptr_t)(st + sdst), 4, soff, w < 4 ? k * 4 : k * N * 4, 0, 0);
+  for (int j = 0; j < C::W_OPS; ++j) {
+    const int r = 8 * (C::W_OPS * w + j) + (lane >> 3);
+    o.w[j] = r * K + (((lane & 7) ^ w8_swz(r)) << 4);
+  }
+  const int p = 64 * w + lane;
+  const int t = 128 * (p >> 7) + 16 * (p & 7) + ((p & 127) >> 3);
+  o.ls = t * nb * 4;
+  o.small = w < 2 ? (64 * w + lane) * 4 : (w - 2) * 256 + lane * 4;
+  return o;
 }
 
 template <class C>
+__device__ __forceinline__ W8Src w8_src(const Params& p, const W8Tile& t, bool live, int w) {
+  W8Src s;
+  const int K = p.K, N = p.N, nb = p.nb;
+  s.x = uniform_rsrc(reinterpret_cast<const char*>(p.lhs) + (long long)t.row0 * K, live ? t.rows * K : 0);
+  s.w = uniform_rsrc(reinterpret_cast<const char*>(p.rhs) + ((long long)t.h * N + t.n0) * K, live ? t.ncols * K : 0);
+  const char* lsb = p.lhs_scale ? reinterpret_cast<const char*>(p.lhs_scale) + (long long)t.row0 * nb * 4
+                                : reinterpret_cast<const char*>(p.lhs);
+  s.ls = uniform_rsrc(lsb, live && p.lhs_scale ? t.rows * nb * 4 : 0);
+  if (w < 2) {
+    const char* b = p.rhs_scale ? reinterpret_cast<const char*>(p.rhs_scale) + ((long long)t.h * nb * N + t.n0) * 4
+                                : reinterpret_cast<const char*>(p.lhs);
+    s.rs_or_bias = uniform_rsrc(b, live && p.rhs_scale ? (nb * N - t.n0) * 4 : 0);
+  } else {
+    const int es = p.bias_f32 ? 4 : 2;
+    const char* b = p.rhs_bias ? reinterpret_cast<const char*>(p.rhs_bias) + ((long long)t.h * N + t.n0) * es
+                               : reinterpret_cast<const char*>(p.lhs);
+    s.rs_or_bias = uniform_rsrc(b, live && p.rhs_bias ? (N - t.n0) * es : 0);
+  }
+  return s;
+}
+
+// Load J (0..13) of K step kd of a tile into stage `st`, scale slot `sc`
+// and bias slot `bs`: J < 8 token rows, J < 12 weight rows, 12 row scales,
+// 13 column scales (waves 0-1) or bias (waves 2-3).  A device function, not
+// a lambda in the kernel: a lambda there is also compiled for the host,
+// where these builtins do not exist.
+template <class C>
+__device__ __forceinline__ void w8_load(const W8Src& s, const W8Off& o, int kd, int N, char* st, char* sc,
+                                        char* bs, int w, int J) {
+  if (J < C::X_OPS) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.x, (lds_ptr_t)(st + (C::X_OPS * w + J) * 1024), 16, o.x[J],
+                                             kd * C::BK, 0, 0);
+  } else if (J < C::X_OPS + C::W_OPS) {
+    const int j = J - C::X_OPS;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.w, (lds_ptr_t)(st + C::X_BYTES + (C::W_OPS * w + j) * 1024), 16,
+                                             o.w[j], kd * C::BK, 0, 0);
+  } else if (J == C::X_OPS + C::W_OPS) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.ls, (lds_ptr_t)(sc + 256 * w), 4, o.ls, kd * 4, 0, 0);
+  } else {
+    // column scales (waves 0-1) or bias (waves 2-3), chosen without a branch
+    // (a branch here would split the MFMA loop into blocks, and the
+    // compiler then sinks the folds out of the loop)
+    const bool cs = w < 2;
+    char* dst = cs ? sc + C::BM * 4 + 256 * w : bs + 256 * (w - 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rs_or_bias, (lds_ptr_t)dst, 4, o.small, cs ? kd * N * 4 : 0, 0, 0);
+  }
+}
+
+template <class C>
+struct W8Frags {
+  i32x8 x[C::FM];
+  i32x8 w[C::FN];
+};
+
+template <class C>
 __global__ __launch_bounds__(C::T) void gmm_w8a8_kernel(Params p) {
-  static_assert(C::op == Op::FP8 && C::FA <= 1 && C::FB <= 1, "one-byte fp8 operands (e4m3fn or e5m2)");
-  using R = W8A8Ring<C>;
-  // one LDS array for the ring and the plan: with a second LDS variable the
-  // compiler tags LDS accesses with alias scopes and then drains the
-  // direct-to-LDS loads in flight before every LDS read
-  __shared__ __attribute__((aligned(1024))) char smem[R::LDS + sizeof(Plan)];
-  Plan& pl = *reinterpret_cast<Plan*>(smem + R::LDS);
+  // one LDS array for the ring, the scale and bias slots and the plan: with
+  // a second LDS variable the compiler tags LDS accesses with alias scopes
+  // and then drains the direct-to-LDS loads in flight before every LDS read
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS + sizeof(Plan)];
+  Plan& pl = *reinterpret_cast<Plan*>(smem + C::LDS);
   if (threadIdx.x == 0) pl.flags = 0;
   __syncthreads();
   build_plan<C::T>(p, pl, C::BM);
@@ -84,186 +205,247 @@ __global__ __launch_bounds__(C::T) void gmm_w8a8_kernel(Params p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w / C::WN, wn = w % C::WN;
+  const int wm = w >> 1, wn = w & 1;
   const int q = lane >> 4, r16 = lane & 15;
   const int M = p.M, N = p.N, K = p.K;
-  const int out_es = p.out_f32 ? 4 : 2;
-  const long long row_bytes = (long long)N * out_es;
-  const int n_ntiles = (N + C::BN - 1) / C::BN;
-  const long long n_gemm = (long long)pl.n_mtiles * n_ntiles;
-  const int lo_row = pl.row_start[0], hi_row = pl.row_start[pl.ga];
-  const long long z1_bytes = fill_rows(p, lo_row) * row_bytes;
-  const long long z2_bytes = fill_rows(p, M - hi_row) * row_bytes;
-  const long long z1 = (z1_bytes + kZeroChunk - 1) / kZeroChunk;
-  const long long z2 = (z2_bytes + kZeroChunk - 1) / kZeroChunk;
-  const long long n_items = n_gemm + z1 + z2;
-  const int KT = K / C::BK;  // K steps = scale blocks (the launcher checks blk == BK)
   const int P = gridDim.x;
   const int slot = xcd_slot(blockIdx.x, P);
-  const bool has_ls = p.lhs_scale != nullptr, has_rs = p.rhs_scale != nullptr;
 
-  // per-lane load offsets (K step 0): lhs load j fills LDS rows
-  // 8 (4 w + j) + lane/8 of the stage, weight load j rows 8 (2 w + j) +
-  // lane/8; lane position lane%8 of a row holds logical chunk
-  // (lane%8) ^ swz(row)
-  int aoff[R::A_OPS], boff[R::B_OPS];
-#pragma unroll
-  for (int j = 0; j < R::A_OPS; ++j) {
-    const int r = 8 * (R::A_OPS * w + j) + (lane >> 3);
-    aoff[j] = r * K + (((lane & 7) ^ swz(r)) << 4);
-  }
-#pragma unroll
-  for (int j = 0; j < R::B_OPS; ++j) {
-    const int r = 8 * (R::B_OPS * w + j) + (lane >> 3);
-    boff[j] = r * K + (((lane & 7) ^ swz(r)) << 4);
+  // rows outside the active groups first (grid-stride)
+  {
+    const long long row_bytes = (long long)N * C::es_out;
+    const int lo_row = pl.row_start[0], hi_row = pl.row_start[pl.ga];
+    const long long z1 = fill_rows(p, lo_row) * row_bytes;
+    const long long z2b = (long long)hi_row * row_bytes;
+    const long long total = z1 + fill_rows(p, M - hi_row) * row_bytes;
+    for (long long off = ((long long)slot * C::T + tid) * 16; off < total; off += (long long)P * C::T * 16)
+      fill16(p, off < z1 ? off : z2b + (off - z1));
   }
 
-  for (long long L = slot; L < n_items; L += P) {
-    if (L >= n_gemm) {
-      long long z = L - n_gemm;
-      if (z < z1) {
-        long long b = z * kZeroChunk;
-        fill_item<C>(p, b, b + kZeroChunk < z1_bytes ? b + kZeroChunk : z1_bytes);
-      } else {
-        z -= z1;
-        long long base = (long long)hi_row * row_bytes;
-        long long b = base + z * kZeroChunk;
-        long long e = b + kZeroChunk;
-        long long end = base + z2_bytes;
-        fill_item<C>(p, b, e < end ? e : end);
-      }
-      continue;
+  const int n_ntiles = (N + C::BN - 1) / C::BN;
+  const int n_items = __builtin_amdgcn_readfirstlane(pl.n_mtiles) * n_ntiles;
+  if (slot >= n_items) return;
+  const int KT = K / C::BK;  // K steps per tile (the launcher guarantees KT >= 3)
+  const int my_tiles = (n_items - slot + P - 1) / P;
+  const int steps = my_tiles * KT;
+  const bool has_bias = p.rhs_bias != nullptr;
+  const W8Off off = w8_offsets<C>(K, p.nb, w, lane);
+
+  // load cursor: the tile and step of global step g + 3
+  int ld_tile = 0, ld_kd = 0;
+  W8Tile ldt = w8_tile<C>(pl, slot, n_ntiles, N);
+  W8Src lsrc = w8_src<C>(p, ldt, true, w);
+  // compute cursor: the tile of the current step and the step within it
+  int ct = 0, kt = 0;
+  W8Tile cur = ldt;
+  // load J of global step g, then (after the last) the cursor's next step
+  auto load = [&](int g, int J) __attribute__((always_inline)) {
+    w8_load<C>(lsrc, off, ld_kd, N, smem + (g % C::S) * C::STAGE, smem + C::SCALES + (g % C::SS) * C::SLOT,
+               smem + C::BIASES + (ld_tile & 1) * C::BIAS_SLOT, w, J);
+  };
+  auto advance = [&]() __attribute__((always_inline)) {
+    if (++ld_kd == KT) {
+      ld_kd = 0;
+      ++ld_tile;
+      const bool live = ld_tile < my_tiles;
+      if (live) ldt = w8_tile<C>(pl, slot + ld_tile * P, n_ntiles, N);
+      lsrc = w8_src<C>(p, ldt, live, w);
     }
-    const int t = (int)(L / n_ntiles);
-    const int j = (int)(L % n_ntiles);
-    const int h = __builtin_amdgcn_readfirstlane(find_group(pl, t));
-    const int row0 = __builtin_amdgcn_readfirstlane(pl.row_start[h] + (t - pl.tile_start[h]) * C::BM);
-    const int rows_left = pl.row_start[h + 1] - row0;
-    const int rows = __builtin_amdgcn_readfirstlane(rows_left < C::BM ? rows_left : C::BM);
-    const int n0 = j * C::BN;
-    const int ncols = N - n0 < C::BN ? N - n0 : C::BN;
+  };
 
-    // buffer resources of the tile: lhs rows, the weight's n-tile rows, the
-    // tile rows' scales, the group's column scales from n0
-    const __amdgpu_buffer_rsrc_t ra =
-        uniform_rsrc(reinterpret_cast<const char*>(p.lhs) + (long long)row0 * K, rows * K);
-    const __amdgpu_buffer_rsrc_t rb = uniform_rsrc(
-        reinterpret_cast<const char*>(p.rhs) + ((long long)h * N + n0) * K, ncols * K);
-    // this wave's scale load: row scales of rows 64 w + lane (waves 0-3;
-    // the tile rows' scales), column scales of columns 64 (w - 4) + lane
-    // (waves 4-5; the group's scales from column n0), or nothing
-    const char* sbase = reinterpret_cast<const char*>(p.lhs);
-    int sbytes = 0;
-    if (w < 4) {
-      if (has_ls) {
-        sbase = reinterpret_cast<const char*>(p.lhs_scale) + (long long)row0 * p.nb * 4;
-        sbytes = rows * p.nb * 4;
-      }
-    } else if (has_rs) {
-      sbase = reinterpret_cast<const char*>(p.rhs_scale) + ((long long)h * p.nb * N + n0) * 4;
-      sbytes = (p.nb * N - n0) * 4;
+  // prologue: steps 0, 1, 2 (every older memory operation -- the fill -- is
+  // complete after the wait, so the loop's counts start from an empty queue)
+  for (int g = 0; g < 3; ++g) {
+    if (g > 0) advance();
+#pragma unroll
+    for (int J = 0; J < C::OPS; ++J) load(g, J);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // Fragment addresses.  A lane's row in token block fm is
+  // 128 wm + 16 fm + r16, whose swizzle does not depend on fm: one lane
+  // pattern per 16-byte half of the fragment, the block adding 2048 fm as an
+  // immediate (the weight side likewise, per column block).
+  int xo[4][2], wo[4][2];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      xo[f][hh] = w8_off(wm * C::TM + f * 16 + r16, q + 4 * hh) - f * 2048;
+      wo[f][hh] = w8_off(wn * C::TN + f * 16 + r16, q + 4 * hh);
     }
-    const __amdgpu_buffer_rsrc_t rsc = uniform_rsrc(sbase, sbytes);
-    const int srow = 64 * w + lane, scol = 64 * (w - 4) + lane;
-    const int soff = w < 4 ? srow * p.nb * 4 : (w < 6 && scol < ncols ? scol * 4 : (int)0x80000000);
-    const int sdst = w < 4 ? R::LSC + 256 * w : (w < 6 ? R::RSC + 256 * (w - 4) : R::DUMMY);
+  const int ls_lane = (wm * C::TM + r16 * 8) * 4, rs_lane = C::BM * 4 + (wn * C::TN + 4 * q) * 4;
+  auto frag = [&](const char* base, int o, int imm) __attribute__((always_inline)) {
+    return *reinterpret_cast<const i32x4*>(base + o + imm);
+  };
+  auto read_x = [&](const char* st, int fm) __attribute__((always_inline)) {
+    const i32x4 lo = frag(st, xo[fm & 3][0], fm * 2048), hi = frag(st, xo[fm & 3][1], fm * 2048);
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  auto read_w = [&](const char* st, int fn) __attribute__((always_inline)) {
+    const i32x4 lo = frag(st, wo[fn][0], C::X_BYTES), hi = frag(st, wo[fn][1], C::X_BYTES);
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
 
-    auto issue = [&](int k) __attribute__((always_inline)) {
-      w8a8_issue<C>(smem + (k % R::S) * R::STAGE, ra, rb, rsc, aoff, boff, soff, sdst, k, w, N);
-    };
+  W8Frags<C> f;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) f.x[fm] = read_x(smem, fm);
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) f.w[fn] = read_w(smem, fn);
 
-    f32x4 acc[C::FM][C::FN], tot[C::FM][C::FN];
+  f32x4 tot[C::FM][C::FN];
 #pragma unroll
-    for (int a = 0; a < C::FM; ++a)
+  for (int a = 0; a < C::FM; ++a)
 #pragma unroll
-      for (int b = 0; b < C::FN; ++b) {
-        acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        tot[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < C::FN; ++b) tot[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Epilogue of a tile: bias, rounding, stores straight from registers.  A
+  // lane holds columns 4q + [0, 4) of each 16-column block for its token.
+  // bf16 output: the permlane16 swap of blocks 2p and 2p + 1 hands lanes
+  // q = 0, 2 eight consecutive columns of block 2p and lanes q = 1, 3 eight
+  // of block 2p + 1, so each store writes 16 bytes per lane (16 per tile);
+  // f32 output: the lane's four columns are 16 bytes already (32 per tile).
+  // Stores outside the tile's valid rows and columns are dropped.
+  auto epilogue = [&]() __attribute__((always_inline)) {
+    char* tile = reinterpret_cast<char*>(p.out) + ((long long)cur.row0 * N + cur.n0) * C::es_out;
+    const int nrec = ((cur.rows - 1) * N + cur.ncols) * C::es_out;
+    const __amdgpu_buffer_rsrc_t ro = uniform_rsrc(tile, nrec);
+    const char* bslot = smem + C::BIASES + (ct & 1) * C::BIAS_SLOT;
+    float bias[C::FN][4];
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int cl = wn * C::TN + fn * 16 + 4 * q;  // this lane's first column of block fn
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bias[fn][i] = 0.f;
+      if (has_bias) {
+        if (p.bias_f32) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(bslot + cl * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bias[fn][i] = v[i];
+        } else {
+          const i32x2 v = *reinterpret_cast<const i32x2*>(bslot + cl * 2);
+          bias[fn][0] = __uint_as_float((uint32_t)v[0] << 16);
+          bias[fn][1] = __uint_as_float((uint32_t)v[0] & 0xFFFF0000u);
+          bias[fn][2] = __uint_as_float((uint32_t)v[1] << 16);
+          bias[fn][3] = __uint_as_float((uint32_t)v[1] & 0xFFFF0000u);
+        }
       }
-
-    issue(0);
-    if (KT > 1) issue(1);
-    for (int kt = 0; kt < KT; ++kt) {
-      // step kt's loads are complete once only step kt+1's are outstanding
-      // (older operations -- the previous tile's stores -- finish first)
-      if (kt + 1 < KT)
-        wait_vmcnt<R::OPS>();
-      else
-        wait_vmcnt<0>();
-      ring_barrier();
-      if (kt + 2 < KT) issue(kt + 2);
-      const char* st = smem + (kt % R::S) * R::STAGE;
-      mma_tile<C>(acc, st, st + C::A_BYTES);
-      // fold this block: tot += part * rhs_scale[col] * lhs_scale[row]
-      const float* lsc = reinterpret_cast<const float*>(st + R::LSC);
-      const float* rsc_l = reinterpret_cast<const float*>(st + R::RSC);
-      float rs[C::FN];
-      f32x4 ls[C::FM];
+    }
 #pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn) rs[fn] = has_rs ? rsc_l[wn * C::TN + fn * 16 + r16] : 1.f;
-#pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
-        ls[fm] = has_ls ? *reinterpret_cast<const f32x4*>(lsc + wm * C::TM + fm * 16 + 4 * q)
-                        : f32x4{1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int rl = wm * C::TM + fm * 16 + r16;
+      if constexpr (C::OUT_F32) {
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) tot[fm][fn][i] += acc[fm][fn][i] * (rs[fn] * ls[fm][i]);
-          acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+          const int cl = wn * C::TN + fn * 16 + 4 * q;
+          const int voff = rl < cur.rows && cl < cur.ncols ? (rl * N + cl) * 4 : (int)0x80000000;
+          const f32x4 v = tot[fm][fn];
+          __builtin_amdgcn_raw_buffer_store_b128(
+              i32x4{__float_as_int(v[0] + bias[fn][0]), __float_as_int(v[1] + bias[fn][1]),
+                    __float_as_int(v[2] + bias[fn][2]), __float_as_int(v[3] + bias[fn][3])},
+              ro, voff, 0, 0);
         }
+      } else {
+#pragma unroll
+        for (int pr = 0; pr < C::FN / 2; ++pr) {
+          uint32_t a[2], b[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const f32x4 va = tot[fm][2 * pr], vb = tot[fm][2 * pr + 1];
+            a[x] = pk_bf16_rne(va[2 * x] + bias[2 * pr][2 * x], va[2 * x + 1] + bias[2 * pr][2 * x + 1]);
+            b[x] = pk_bf16_rne(vb[2 * x] + bias[2 * pr + 1][2 * x], vb[2 * x + 1] + bias[2 * pr + 1][2 * x + 1]);
+          }
+          const auto s0 = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+          const int cl = wn * C::TN + (2 * pr + (q & 1)) * 16 + (q >> 1) * 8;
+          const int voff = rl < cur.rows && cl < cur.ncols ? (rl * N + cl) * 2 : (int)0x80000000;
+          __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]}, ro, voff, 0,
+                                                 0);
+        }
+      }
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) tot[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // every wave's reads of the last stages are done before the epilogue
-    // stages its output there
-    ring_barrier();
+  };
 
-    // epilogue (as the general kernel's): bias, round, and each 16-row block
-    // of the wave's tile through the wave's staging slice, stored as 16-byte
-    // chunks of output rows
-    {
-      const int es = out_es;
-      const int pitch = C::TN * es + 16;
-      char* const stg = smem + w * kStageSlice<C>;
-      const int cpr = C::TN * es / 16;
-      float bias[C::FN];
+  // One K step g: its fragments are in `f`; each is refilled with step
+  // g + 1's from stage (g + 1) % 3 right after its last MFMA.  In a tile's
+  // first two steps the previous tile's stores are newer than the loads
+  // waited for.
+  auto kstep = [&](int g) __attribute__((always_inline)) {
+    // the load cursor to step g + 3 first: its branch (a new tile every KT
+    // steps) placed after the MFMA loop lets the compiler sink the folds
+    // out of the loop, past it
+    advance();
+    // this step's scales: complete and visible since the last step's barrier
+    // (its loads were waited for then), and their slot is not reloaded
+    // before the next step -- read them while the waits below run
+    const char* sc = smem + C::SCALES + (g % C::SS) * C::SLOT;
+    const f32x4 ls0 = *reinterpret_cast<const f32x4*>(sc + ls_lane);
+    const f32x4 ls1 = *reinterpret_cast<const f32x4*>(sc + ls_lane + 16);
+    f32x4 rs[C::FN];
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) rs[fn] = *reinterpret_cast<const f32x4*>(sc + rs_lane + fn * 64);
+    if (kt < 2)
+      wait_vmcnt<C::OPS + C::E>();
+    else
+      wait_vmcnt<C::OPS>();
+    // this wave's reads of stage g % 3 (last step's fragment refills) and of
+    // the scale slot of step g - 1 are complete before the barrier frees them
+    __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+    ring_barrier();
+    const char* stn = smem + ((g + 1) % C::S) * C::STAGE;
+    // Row block fm: its four MFMAs, each followed by a quarter of the fold of
+    // row block fm - 1 (whose MFMAs finished a row block ago) and one of the
+    // next step's fragment reads.  The fold's quarters are eight independent
+    // VALU instructions each -- the products l * rs of column blocks 0-1,
+    // of 2-3, then the FMAs of 0-1, of 2-3 -- so that no instruction waits
+    // on the one before it.
+    f32x4 acc[2][C::FN];
+    float sc8[2][8];
+#pragma unroll
+    for (int fm = 0; fm <= C::FM; ++fm) {
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn) {
-        const int cl = wn * C::TN + fn * 16 + r16;
-        bias[fn] = 0.f;
-        if (p.rhs_bias && cl < ncols) {
-          const long long bi = (long long)h * N + n0 + cl;
-          bias[fn] = p.bias_f32 ? reinterpret_cast<const float*>(p.rhs_bias)[bi]
-                                : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.rhs_bias)[bi]);
-        }
-      }
+        if (fm < C::FM)
+          acc[fm & 1][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              f.w[fn], f.x[fm], f32x4{0.f, 0.f, 0.f, 0.f}, C::FB, C::FA, 0, 0, 0, 0);
+        if (fm > 0) {
+          const int pm = fm - 1;
+          const float l = pm < 4 ? ls0[pm] : ls1[pm - 4];
+          if (fn < 2) {
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm) {
+            for (int i = 0; i < 8; ++i) sc8[fn][i] = l * rs[2 * fn + i / 4][i % 4];
+          } else {
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = tot[fm][fn][i] + bias[fn];
-            char* d = stg + (4 * q + i) * pitch + (fn * 16 + r16) * es;
-            if (p.out_f32)
-              *reinterpret_cast<float*>(d) = v;
-            else
-              *reinterpret_cast<uint16_t*>(d) = f32_to_bf16_rne(v);
+            for (int i = 0; i < 8; ++i) {
+              const int cb = 2 * (fn - 2) + i / 4;
+              tot[pm][cb][i % 4] += acc[pm & 1][cb][i % 4] * sc8[fn - 2][i];
+            }
           }
-        for (int c = lane; c < 16 * cpr; c += 64) {
-          const int r = c / cpr, cb = c % cpr;
-          const i32x4 d = *reinterpret_cast<const i32x4*>(stg + r * pitch + cb * 16);
-          const int rl = wm * C::TM + fm * 16 + r;
-          const int cl = wn * C::TN + cb * (16 / es);
-          if (rl < rows && cl < ncols)
-            *reinterpret_cast<i32x4*>(reinterpret_cast<char*>(p.out) +
-                                      ((long long)(row0 + rl) * N + n0 + cl) * es) = d;
         }
+        // step g + 3's loads, one after every other MFMA: issued in one
+        // burst they queue at the texture unit and hold up the wave
+        if (fm < C::FM && (fm * C::FN + fn) % 2 == 0 && (fm * C::FN + fn) / 2 < C::OPS)
+          load(g + 3, (fm * C::FN + fn) / 2);
+        // refill each fragment with the next step's right after its last use
+        if (fm < C::FM && fn == C::FN - 1) f.x[fm] = read_x(stn, fm);
+        if (fm == C::FM - 1) f.w[fn] = read_w(stn, fn);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // the next tile's first loads overwrite the staging slices
-    __syncthreads();
-  }
+    if (++kt == KT) {
+      epilogue();
+      kt = 0;
+      if (++ct < my_tiles) cur = w8_tile<C>(pl, slot + ct * P, n_ntiles, N);
+    }
+  };
+
+  for (int g = 0; g < steps; ++g) kstep(g);
+  // the loads issued for steps past the last are dropped, but they still
+  // write their LDS destination: let them land before the workgroup ends
+  wait_vmcnt<0>();
 }
 
 }  // namespace gmmk
