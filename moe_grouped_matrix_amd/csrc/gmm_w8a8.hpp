@@ -104,31 +104,27 @@ struct W8Src {
   __amdgpu_buffer_rsrc_t x, w, ls, rs_or_bias;
 };
 
-// Per-lane parts of this wave's load offsets (the K step adds a scalar).
-// Token-row load j fills stage rows 8 (8 w + j) + lane / 8, weight-row load
-// j rows 8 (4 w + j) + lane / 8; lane position lane % 8 of a row holds
-// logical chunk (lane % 8) ^ w8_swz(row).  The row-scale load puts token t(p)
-// at position p = 64 w + lane of the slot, t(p) = 128 (p / 128) +
-// 16 (p % 8) + (p % 128) / 8, so that a lane's eight row scales (its token
-// in each of the wave's eight row blocks) are 32 contiguous bytes.
+// Per-lane parts of this wave's load offsets (the K step and the load's row
+// group add a scalar).  Token-row load j fills stage rows 8 (8 w + j) +
+// lane / 8, weight-row load j rows 8 (4 w + j) + lane / 8; lane position
+// lane % 8 of a row holds logical chunk (lane % 8) ^ w8_swz(row), which does
+// not depend on j, so load j is load 0 moved by 8 j rows (a scalar).  The
+// row-scale load puts token t(p) at position p = 64 w + lane of the slot,
+// t(p) = 128 (p / 128) + 16 (p % 8) + (p % 128) / 8, so that a lane's eight
+// row scales (its token in each of the wave's eight row blocks) are 32
+// contiguous bytes.  Four VGPRs: with one per load the offsets do not stay
+// in VGPRs, and each is read back from an accumulation register before use.
 struct W8Off {
-  int x[8], w[4];
+  int x, w;       // token-row and weight-row loads (j = 0)
   int ls, small;  // row scale; column scale (waves 0-1) or bias (waves 2-3)
 };
 
 template <class C>
 __device__ __forceinline__ W8Off w8_offsets(int K, int nb, int w, int lane) {
   W8Off o;
-#pragma unroll
-  for (int j = 0; j < C::X_OPS; ++j) {
-    const int r = 8 * (C::X_OPS * w + j) + (lane >> 3);
-    o.x[j] = r * K + (((lane & 7) ^ w8_swz(r)) << 4);
-  }
-#pragma unroll
-  for (int j = 0; j < C::W_OPS; ++j) {
-    const int r = 8 * (C::W_OPS * w + j) + (lane >> 3);
-    o.w[j] = r * K + (((lane & 7) ^ w8_swz(r)) << 4);
-  }
+  const int rx = 8 * C::X_OPS * w + (lane >> 3), rw = 8 * C::W_OPS * w + (lane >> 3);
+  o.x = rx * K + (((lane & 7) ^ w8_swz(rx)) << 4);
+  o.w = rw * K + (((lane & 7) ^ w8_swz(rw)) << 4);
   const int p = 64 * w + lane;
   const int t = 128 * (p >> 7) + 16 * (p & 7) + ((p & 127) >> 3);
   o.ls = t * nb * 4;
@@ -164,15 +160,15 @@ __device__ __forceinline__ W8Src w8_src(const Params& p, const W8Tile& t, bool l
 // a lambda in the kernel: a lambda there is also compiled for the host,
 // where these builtins do not exist.
 template <class C>
-__device__ __forceinline__ void w8_load(const W8Src& s, const W8Off& o, int kd, int N, char* st, char* sc,
+__device__ __forceinline__ void w8_load(const W8Src& s, const W8Off& o, int kd, int K, int N, char* st, char* sc,
                                         char* bs, int w, int J) {
   if (J < C::X_OPS) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.x, (lds_ptr_t)(st + (C::X_OPS * w + J) * 1024), 16, o.x[J],
-                                             kd * C::BK, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.x, (lds_ptr_t)(st + (C::X_OPS * w + J) * 1024), 16, o.x,
+                                             kd * C::BK + 8 * J * K, 0, 0);
   } else if (J < C::X_OPS + C::W_OPS) {
     const int j = J - C::X_OPS;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(s.w, (lds_ptr_t)(st + C::X_BYTES + (C::W_OPS * w + j) * 1024), 16,
-                                             o.w[j], kd * C::BK, 0, 0);
+                                             o.w, kd * C::BK + 8 * j * K, 0, 0);
   } else if (J == C::X_OPS + C::W_OPS) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(s.ls, (lds_ptr_t)(sc + 256 * w), 4, o.ls, kd * 4, 0, 0);
   } else {
@@ -240,7 +236,7 @@ __global__ __launch_bounds__(C::T) void gmm_w8a8_kernel(Params p) {
   W8Tile cur = ldt;
   // load J of global step g, then (after the last) the cursor's next step
   auto load = [&](int g, int J) __attribute__((always_inline)) {
-    w8_load<C>(lsrc, off, ld_kd, N, smem + (g % C::S) * C::STAGE, smem + C::SCALES + (g % C::SS) * C::SLOT,
+    w8_load<C>(lsrc, off, ld_kd, K, N, smem + (g % C::S) * C::STAGE, smem + C::SCALES + (g % C::SS) * C::SLOT,
                smem + C::BIASES + (ld_tile & 1) * C::BIAS_SLOT, w, J);
   };
   auto advance = [&]() __attribute__((always_inline)) {
@@ -432,6 +428,13 @@ __global__ __launch_bounds__(C::T) void gmm_w8a8_kernel(Params p) {
         // refill each fragment with the next step's right after its last use
         if (fm < C::FM && fn == C::FN - 1) f.x[fm] = read_x(stn, fm);
         if (fm == C::FM - 1) f.w[fn] = read_w(stn, fn);
+        // in this order: the MFMA, then the VALU work that runs beside it,
+        // then the memory operations (left to itself the scheduler puts
+        // two groups' MFMAs back to back, and the second waits for the first)
+        if (fm < C::FM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }

@@ -4,7 +4,7 @@ The kernel takes problems with both block scales, scale blocks of one K step
 of 128, K >= 384 and N a multiple of 4 (the big tile policy, or the auto
 policy on large groups).  Covered here: the four one-byte format pairs,
 f32 and bf16 output, no bias / bf16 bias / f32 bias, empty groups, partial
-m-tiles, an N tail of 4 columns, the minimum of three K steps and more, and
+m-tiles, an N tail of 8 columns, the minimum of three K steps and more, and
 grids capped so that each workgroup runs several tiles back to back (its
 load pipeline crosses from one tile into the next).
 
