@@ -9,7 +9,8 @@ waits after a half tile would be short by that many operations and the next
 stages could read LDS before their loads land.  This test compiles the
 kernels to assembly and checks that each big-kernel instantiation still has
 both epilogues' stores: E for a full tile and E (real plus padding) for a half
-tile."""
+tile; likewise the tgmm and W8A8 kernels' loads and stores, and that the loop
+kernels do not spill."""
 import os
 import re
 import shutil
@@ -26,17 +27,28 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 E_FULL = {"true": 32, "false": 16}
 
 
-@pytest.fixture(scope="module")
-def kernel_asm(tmp_path_factory):
+def _compile(tmp_path_factory, source):
+    """gfx950 assembly of one translation unit, with the library's flags."""
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("isa") / "kernels.s"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-Wno-unused-command-line-argument", "-I" + os.path.join(ROOT, "include"),
-           "-S", "--cuda-device-only", os.path.join(CSRC, "gmm_kernels.hip"), "-o", str(out)]
+    from moe_grouped_matrix_amd import build
+    out = tmp_path_factory.mktemp("isa") / (source + ".s")
+    flags = [f for f in build.HIPCC_FLAGS if f != "-fPIC"] + build.EXTRA_FLAGS.get(source, [])
+    cmd = [HIPCC] + flags + ["-I" + os.path.join(ROOT, "include"), "-S", "--cuda-device-only",
+                             os.path.join(CSRC, source), "-o", str(out)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     return out.read_text()
+
+
+@pytest.fixture(scope="module")
+def kernel_asm(tmp_path_factory):
+    return _compile(tmp_path_factory, "gmm_kernels.hip")
+
+
+@pytest.fixture(scope="module")
+def w8a8_asm(tmp_path_factory):
+    return _compile(tmp_path_factory, "gmm_w8a8.hip")
 
 
 def _functions(asm, pattern):
@@ -68,9 +80,29 @@ def test_tgmm_kernel_keeps_every_counted_store(kernel_asm):
     assert seen == 2  # bf16 / f32 output
 
 
-def test_loop_kernels_do_not_spill(kernel_asm):
+def test_loop_kernels_do_not_spill(kernel_asm, w8a8_asm):
     # a spill reload is a vector memory load: its wait would drain every
     # direct-to-LDS load queued behind the K loop's constant counts
-    for pattern in (r"_ZN4gmmk15gmm_tgmm_kernel", r"_ZN4gmmk17gmm_stream_kernel", r"_ZN4gmmk15gmm_w8a8_kernel"):
-        for name, lines in _functions(kernel_asm, pattern):
+    seen = 0
+    for asm, pattern in ((kernel_asm, r"_ZN4gmmk15gmm_tgmm_kernel"), (kernel_asm, r"_ZN4gmmk17gmm_stream_kernel"),
+                         (w8a8_asm, r"_ZN4gmmk15gmm_w8a8_kernel")):
+        for name, lines in _functions(asm, pattern):
             assert not any(ln.startswith("scratch_") for ln in lines), name
+            seen += 1
+    assert seen == 2 + 6 + 8
+
+
+def test_w8a8_kernel_keeps_every_counted_operation(w8a8_asm):
+    """The W8A8 kernel's waits count 14 direct-to-LDS loads per wave and K
+    step (three steps' worth in the prologue, one in the loop) and the
+    epilogue's stores: 16 for bf16 output (16 bytes per lane after the
+    permlane16 swap), 32 for f32."""
+    seen = 0
+    for name, lines in _functions(w8a8_asm, r"_ZN4gmmk15gmm_w8a8_kernel"):
+        out_f32 = re.search(r"W8CfgILi[01]ELi[01]ELb([01])E", name).group(1) == "1"
+        loads = sum(1 for ln in lines if ln.startswith("buffer_load") and ln.endswith(" lds"))
+        stores = sum(1 for ln in lines if ln.startswith("buffer_store"))
+        assert loads == 4 * 14, (name, loads)
+        assert stores == (32 if out_f32 else 16), (name, stores)
+        seen += 1
+    assert seen == 8  # e4m3 / e5m2 on either side x bf16 / f32 output
