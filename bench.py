@@ -40,7 +40,7 @@ KERNEL_SOURCES = {
     "moe_dlhs_bf16": ("gmm_big.hpp",),
     "decode_fp8w": ("gmm_big.hpp", "gmm_stream.hpp"),
     "w8a8_fp8": ("gmm_big.hpp", "gmm_w8a8.hpp", "gmm_w8a8.hip"),
-    "tgmm_bf16": ("gmm_big.hpp", "gmm_tgmm.hpp"),
+    "tgmm_bf16": ("gmm_big.hpp", "gmm_tgmm.hpp", "gmm_tgmm_tiles.hpp"),
     "quant_fp8": ("gmm_quant.hip",),
 }
 # workloads whose weights fit in the caches between calls: each timed call

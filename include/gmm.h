@@ -265,7 +265,7 @@ gmm_status gmm_widen_scales_run(gmm_handle* h, const gmm_tensor* src, const gmm_
  *                out must not overlap an input.
  *
  * Size limits: K % 8 == 0, N % 8 == 0, M*K*2 and M*N*2 below 2 GiB, Ga*K
- * below 2^31, 256*N*(output element size) below 2 GiB.  Outside them the
+ * below 2^31, 384*N*(output element size) below 2 GiB.  Outside them the
  * call returns GMM_E_UNSUPPORTED and queues nothing; shape or dtype
  * inconsistencies return GMM_E_INVALID; a launch failure returns GMM_E_HIP
  * (as does a failed allocation of a new stream's counters).  Invalid

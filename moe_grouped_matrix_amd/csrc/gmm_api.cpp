@@ -483,9 +483,9 @@ static gmm_status run_tgmm(gmm_handle* h, const gmm_tensor* lhs, const gmm_tenso
   if (K % 8 || N % 8) return fail(h, GMM_E_UNSUPPORTED, "K and N must be multiples of 8");
   if (M * K * 2 >= 0x7FFFFFF0LL || M * N * 2 >= 0x7FFFFFF0LL || Ga * K >= (1LL << 31))
     return fail(h, GMM_E_UNSUPPORTED, "an operand beyond 2 GiB or Ga*K beyond 2^31");
-  // the epilogue addresses a 256-row output tile with 32-bit byte offsets
-  if (256LL * N * elem_size(out->dtype) >= 0x7FFFFFF0LL)
-    return fail(h, GMM_E_UNSUPPORTED, "a 256-row output tile exceeds 2 GiB");
+  // the epilogue addresses an output tile of up to 384 rows with 32-bit byte offsets
+  if (384LL * N * elem_size(out->dtype) >= 0x7FFFFFF0LL)
+    return fail(h, GMM_E_UNSUPPORTED, "a 384-row output tile exceeds 2 GiB");
   const gmm_tensor* ins[] = {lhs, rhs, group_sizes};
   for (const gmm_tensor* t : ins) {
     if (numel(t) > 0 && !t->data) return fail(h, GMM_E_INVALID, "null data pointer");

@@ -5,73 +5,196 @@
 // operation (tpu-inference wheel diff page, megablox/gmm.py,
 // make_group_metadata, visit_empty_groups).
 //
-// An output tile is 256 (k) x 256 (n) of one group, computed by the big
-// kernel's machinery (gmm_big.hpp): eight waves of 128 x 64 (64 x 64 over
-// the valid half of a tile with at most 128 valid rows or columns),
-// 32x32x16 bf16 MFMAs with the column-side fragment as the first operand,
-// a four-stage ring of direct-to-LDS loads running three steps ahead across
-// the workgroup's tiles, and the same epilogue.  The contraction runs over
-// the group's rows, 32 per step.  Both operands are row-major with the
-// contraction as their row index, so both are staged like the big kernel's
-// [G,K,N] weight -- 512-byte rows of 256 columns -- and both fragments come
-// from LDS transpose reads.  The step's row offset is part of the
-// range-checked vector offset, so the rows past the group's end (the
-// contraction tail) read as zeros; a tile runs at least five steps (the
-// phased loop's minimum), the extra ones reading zeros.
+// The contraction runs over the group's rows, 32 per step.  Both operands
+// are row-major with the contraction as their row index, so a step stages
+// 32 rows of each operand's column slices in LDS and the MFMA fragments come
+// from LDS transpose reads.  A stage is four areas of 32 rows x 128 columns
+// (256-byte rows); an output tile takes its lhs columns from the first `na`
+// areas and its rhs columns from the rest: 256 x 256 tiles two and two,
+// 384 x 128 tiles three and one, 128 x 384 tiles one and three.  Eight
+// waves, two per SIMD, compute 128 x 64 (96 x 64, 64 x 96) each with
+// 32x32x16 bf16 MFMAs, the rhs-side fragment first; a four-stage ring of
+// direct-to-LDS loads runs three steps ahead, across the workgroup's tiles;
+// the epilogue is the big kernel's, staged through LDS.  The step's row
+// offset is part of the range-checked vector offset, so the rows past the
+// group's end (the contraction tail) read as zeros; a tile runs at least
+// five steps (the phased loop's minimum), the extra ones reading zeros.
 //
-// Tiles are handed out dynamically, per XCD: the active groups, largest
-// first, are dealt to eight queues (one per XCD) so that each queue gets the
-// same number of contraction steps (each to the least-loaded queue), and the
-// workgroups of an XCD take their queue's tiles in order with an atomic
-// counter, so a group's tiles share that XCD's L2 and the long contractions
-// are spread first, the short ones filling in behind.  The counters are the
-// caller's (Params::queue: a block of the handle's per stream); the last
-// workgroup of a queue to finish resets its counters for the next call.
+// Two schedules, both with one work queue per XCD (workgroup b runs on XCD
+// b mod 8) when the grid is a multiple of 8 and there are at least 16
+// groups:
+//  - Gang: when a group's output splits into T <= W tiles of the shapes in
+//    gmm_tgmm_tiles.hpp, T >= 3/4 of the W workgroups of a queue: the
+//    groups are dealt to the queues by rows, and workgroup j of a queue
+//    computes tile j of each of its queue's groups in turn.  All of a
+//    group's tiles then run side by side on one XCD and read each
+//    contraction row of both operands at about the same time, once from
+//    HBM into that XCD's L2.  The tiles that hold fewer accumulators (tall,
+//    wide) finish their steps sooner; so that they do not run ahead into the
+//    next group alone, each workgroup, before it queues the next group's
+//    first loads, counts itself on its queue's counter and waits (bounded)
+//    until the queue's other workgroups have done the same.
+//  - Dynamic (otherwise): 256 x 256 tiles handed out through the queues'
+//    atomic counters, largest groups first (the counters are the caller's:
+//    Params::queue, a block of the handle's per stream; the last workgroup
+//    of a queue to finish resets them for the next call).
 #pragma once
 
 #include "gmm_big.hpp"
+#include "gmm_tgmm_tiles.hpp"
 
 namespace gmmk {
 
 template <bool OUT_F32_>
 struct TgCfg {
   static constexpr bool OUT_F32 = OUT_F32_;
-  static constexpr int BM = 256, BN = 256;  // output tile: k rows x n columns
-  static constexpr int WM = 2, WN = 4, NWAVES = WM * WN, T = 64 * NWAVES;
-  static constexpr int FM = 4, FN = 2;      // 32 x 32 blocks of a full-tile wave (128 x 64)
+  static constexpr int BM = 256, BN = 256;  // dynamic-schedule tile: k rows x n columns
+  static constexpr int NWAVES = 8, T = 64 * NWAVES;
   static constexpr int BK = 32;             // contraction rows per step
-  static constexpr int ROWB = 512;          // bytes of one 256-column operand row
-  static constexpr int A_BYTES = BK * ROWB, B_BYTES = BK * ROWB;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int AREA_ROW = 256;      // bytes of 128 columns
+  static constexpr int AREA = BK * AREA_ROW;
+  static constexpr int NAREA = 4;
+  static constexpr int STAGE = NAREA * AREA;
   static constexpr int S = 4;  // stages in the ring
   static constexpr int RING = S * STAGE;
-  static constexpr int DMA_STEP = 4;  // 1 KB direct-to-LDS loads per wave and step (two per operand)
+  static constexpr int DMA_STEP = 4;  // 1 KB direct-to-LDS loads per wave and step
   static constexpr int MIN_STEPS = 5;
+  static constexpr int NSLOT = 6;     // fragment slots per K half
+  static constexpr int NACC = 8;      // 32 x 32 accumulator blocks
   static constexpr int es_out = OUT_F32 ? 4 : 2;
-  // epilogue stores per wave and tile (as in the big kernel)
+  // epilogue stores per wave and tile: the full tile's (the others pad)
   static constexpr int ST_BLOCK = OUT_F32 ? 4 : 2;
-  static constexpr int E = FM * FN * ST_BLOCK;
-  static_assert(A_BYTES == NWAVES * 2 * 1024, "two 1 KB loads per wave and operand");
+  static constexpr int E = NACC * ST_BLOCK;
+  static_assert(STAGE == NWAVES * DMA_STEP * 1024, "each wave fills half an area per step");
 };
 
+// Per-shape compile-time layout: FM x FN accumulator blocks per wave and the
+// first rhs-side fragment slot BS (slots [0, BS) hold lhs-side fragments).
+template <int SH>
+struct TgShapeCfg {
+  static constexpr int FM = SH == kTgFull ? 4 : SH == kTgTall ? 3 : 2;
+  static constexpr int FN = SH == kTgWide ? 3 : 2;
+  static constexpr int BS = SH == kTgTall ? 3 : SH == kTgWide ? 2 : 4;
+  static_assert(FM * FN <= 8 && BS + FN <= 6, "shape fits the accumulators and slots");
+};
+
+// Gang schedule: the queue's workgroups meet once per group.  Lane 0 of wave
+// 0 adds one to the queue's counter and waits until it reaches `target` (the
+// arrivals of every workgroup of the queue at this group), for at most
+// kGangSpin polls of a few hundred cycles each; the wait only keeps the
+// workgroups in step (shared L2 reads), the results never depend on it.  The
+// atomic's return and the polls are waited for by the compiler (vmcnt 0),
+// which only makes the loop's later constant waits hold sooner.
+constexpr int kGangSpin = 2048;
+
+__device__ __forceinline__ void tg_gang_meet(int* counter, int target, int lane) {
+  if (lane == 0) {
+    int v = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+    for (int spin = 0; v < target && spin < kGangSpin; ++spin) {
+      __builtin_amdgcn_s_sleep(4);
+      v = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// A tile as the loop and the epilogue see it.  The kernel keeps two (the
+// current and the next), in scalar registers, so the fields that outlive
+// the decode are packed two to a word where they fit in 16 bits.
 struct TgItem {
-  int h;           // active group
-  int rlo, nrow;   // the group's first row and row count (the contraction)
-  int steps;       // contraction steps of this tile (at least MIN_STEPS)
-  BigItem out;     // output tile as rows h * K + k0 .. of the [Ga*K, N] output
+  // decode-time only (the loads' source is formed from them)
+  int h;              // active group
+  int rlo, nrow;      // the group's first row and row count (the contraction)
+  int k0, n0;         // origin in the group's K x N output
+  int rows;           // valid rows from the origin
+  int na;             // areas holding lhs columns
+  // used by the loop and the epilogue
+  int steps;          // contraction steps of this tile (at least MIN_STEPS)
+  int shape;          // TgShape
+  int ncols;          // valid columns from the origin
+  int skip;           // skip_r | skip_c << 16: [0, skip_r) x [0, skip_c) is another tile's (not stored)
+  int rc;             // rbase | cbase << 16: this wave's first row / column in the tile
+  int sofs[3];        // fragment slot 2i (low half) and 2i+1 (high half): area * AREA | block << 6
+  long long obase;    // byte offset of the tile's origin in the output
+  int nrec;           // output bytes from the origin to the end of the valid part
 };
 
-// Scheduling units: a group's tiles, or, for a group whose tiles are long,
-// one of the four quadrants of its tile grid (k-tiles [0, ka) or [ka, nkt),
-// n-tiles [0, na) or [na, nnt)), so that its tiles can spread over several
-// queues.  A unit is an int: the active group in bits 0..9, the quadrant in
-// bits 10 (upper k half) and 11 (upper n half), bit 12 set for a quadrant.
+template <int S>
+__device__ __forceinline__ int tg_slot_off(const TgItem& it) {
+  return (it.sofs[S >> 1] >> (16 * (S & 1))) & 0xFFFF;
+}
+
+// Scheduling units of the dynamic schedule: a group's tiles, or, for a group
+// whose tiles are long, one of the four quadrants of its tile grid (k-tiles
+// [0, ka) or [ka, nkt), n-tiles [0, na) or [na, nnt)), so that its tiles can
+// spread over several queues.  A unit is an int: the active group in bits
+// 0..9, the quadrant in bits 10 (upper k half) and 11 (upper n half), bit 12
+// set for a quadrant.  The gang schedule's units are whole groups.
 constexpr int kMaxSplit = 128;                          // groups split at most
 constexpr int kMaxUnits = kMaxGroups + 3 * kMaxSplit;  // units at most
 
 struct TgGrid {
   int nkt, nnt, ka, na;
 };
+
+// The tile's rows, steps, wave layout and fragment slots.
+template <class C>
+__device__ __forceinline__ void tg_finish(const Params& p, const Plan& pl, TgItem& it, int skip_r, int skip_c,
+                                          int w) {
+  it.rlo = __builtin_amdgcn_readfirstlane(pl.row_start[it.h]);
+  it.nrow = __builtin_amdgcn_readfirstlane(pl.row_start[it.h + 1] - pl.row_start[it.h]);
+  const int st = (it.nrow + C::BK - 1) / C::BK;
+  it.steps = st < C::MIN_STEPS ? C::MIN_STEPS : st;
+  int bs, fnx, rbase, cbase;
+  if (it.shape == kTgTall) {  // 4 x 2 waves of 96 x 64
+    rbase = (w >> 1) * 96;
+    cbase = (w & 1) * 64;
+    it.na = 3;
+    bs = 3;
+    fnx = 2;
+  } else if (it.shape == kTgWide) {  // 2 x 4 waves of 64 x 96
+    rbase = (w >> 2) * 64;
+    cbase = (w & 3) * 96;
+    it.na = 1;
+    bs = 2;
+    fnx = 3;
+  } else {
+    it.na = 2;
+    bs = 4;
+    fnx = 2;
+    if (it.shape == kTgFull) {  // 2 x 4 waves of 128 x 64
+      rbase = (w >> 2) * 128;
+      cbase = (w & 3) * 64;
+    } else if (it.rows <= C::BM / 2) {  // 2 x 4 waves of 64 x 64 over 128 x 256
+      rbase = (w >> 2) * 64;
+      cbase = (w & 3) * 64;
+    } else {  // 4 x 2 waves of 64 x 64 over 256 x 128
+      rbase = (w >> 1) * 64;
+      cbase = (w & 1) * 64;
+    }
+  }
+  it.rc = rbase | cbase << 16;
+  it.skip = skip_r | skip_c << 16;
+  it.obase = ((long long)(it.h * p.K + it.k0) * p.N + it.n0) * C::es_out;
+  it.nrec = ((it.rows - 1) * p.N + it.ncols) * C::es_out;
+  // Slot s < bs: the lhs-side fragment at tile row rbase + 32 s; slot s >=
+  // bs: the rhs-side one at column cbase + 32 (s - bs).  Slots past the
+  // shape's fragments repeat the first rhs-side one (read, never used).
+#pragma unroll
+  for (int i = 0; i < 3; ++i) it.sofs[i] = 0;
+#pragma unroll
+  for (int s = 0; s < C::NSLOT; ++s) {
+    int area, col;
+    if (s < bs) {
+      col = rbase + 32 * s;
+      area = col >> 7;
+    } else {
+      const int fn = s - bs < fnx ? s - bs : 0;
+      col = cbase + 32 * fn;
+      area = it.na + (col >> 7);
+    }
+    it.sofs[s >> 1] |= (area * C::AREA | ((col & 127) >> 5) << 6) << (16 * (s & 1));
+  }
+}
 
 // The unit of queue tile L: the last of the queue's units [*cur, u_end) whose
 // first tile (ustart, increasing along a queue) is at most L, 64 at a time
@@ -90,15 +213,16 @@ __device__ __forceinline__ int tg_find_unit(const int* ustart, int* cur, int u_e
   return u;
 }
 
-// Tile L of a queue: its unit, then k-tile, then n-tile within the unit.
+// Dynamic schedule: tile L of a queue -- its unit, then k-tile, then n-tile
+// within the unit.
 template <class C>
-__device__ __forceinline__ TgItem decode_tg(const Plan& pl, const int* units, const int* ustart, int* cur,
-                                            int u_end, int L, const TgGrid& gr, int K, int N, int w, int lane) {
+__device__ __forceinline__ TgItem decode_tg(const Params& p, const Plan& pl, const int* units, const int* ustart,
+                                            int* cur, int u_end, int L, const TgGrid& gr, int w, int lane) {
+  const int K = p.K, N = p.N;
   TgItem it;
   const int u = tg_find_unit(ustart, cur, u_end, L, lane);
   const int d = __builtin_amdgcn_readfirstlane(units[u]);
   const int t = L - __builtin_amdgcn_readfirstlane(ustart[u]);
-  const int h = d & 1023;
   int kt, nt;
   if (d & 4096) {
     const int k0 = (d & 1024) ? gr.ka : 0, n0 = (d & 2048) ? gr.na : 0;
@@ -109,74 +233,62 @@ __device__ __forceinline__ TgItem decode_tg(const Plan& pl, const int* units, co
     kt = t / gr.nnt;
     nt = t % gr.nnt;
   }
-  it.h = h;
-  it.rlo = __builtin_amdgcn_readfirstlane(pl.row_start[h]);
-  it.nrow = __builtin_amdgcn_readfirstlane(pl.row_start[h + 1] - pl.row_start[h]);
-  const int st = (it.nrow + C::BK - 1) / C::BK;
-  it.steps = st < C::MIN_STEPS ? C::MIN_STEPS : st;
-  BigItem& o = it.out;
-  const int k0 = kt * C::BM;
-  o.h = it.h;
-  o.row0 = it.h * K + k0;
-  o.rows = K - k0 < C::BM ? K - k0 : C::BM;
-  o.n0 = nt * C::BN;
-  o.ncols = N - o.n0 < C::BN ? N - o.n0 : C::BN;
-  const bool half_m = o.rows <= C::BM / 2, half_n = o.ncols <= C::BN / 2;
-  o.half = half_m || half_n;
-  if (!o.half) {  // 2 x 4 waves of 128 x 64
-    o.rbase = (w / C::WN) * 128;
-    o.cbase = (w % C::WN) * 64;
-  } else if (!half_n) {  // 2 x 4 waves of 64 x 64 over 128 x 256
-    o.rbase = (w / 4) * 64;
-    o.cbase = (w % 4) * 64;
-  } else {  // 4 x 2 waves of 64 x 64 over 256 x 128
-    o.rbase = (w / 2) * 64;
-    o.cbase = (w % 2) * 64;
-  }
+  it.h = d & 1023;
+  it.k0 = kt * C::BM;
+  it.n0 = nt * C::BN;
+  it.rows = K - it.k0 < C::BM ? K - it.k0 : C::BM;
+  it.ncols = N - it.n0 < C::BN ? N - it.n0 : C::BN;
+  it.shape = (it.rows <= C::BM / 2 || it.ncols <= C::BN / 2) ? kTgHalf : kTgFull;
+  tg_finish<C>(p, pl, it, 0, 0, w);
   return it;
 }
 
-// Direct-to-LDS sources of one tile: buffer resources over the group's rows
-// from the tile's first column (zero-size past the end of the stream).
-// Columns past the tile's valid part are loaded too (the next columns of
-// the row, or zeros past the group): they only feed output rows and columns
-// that the epilogue's range check drops.
+// Gang schedule: item L of workgroup j of a queue is tile j (t) of the
+// queue's L-th group.
+template <class C>
+__device__ __forceinline__ TgItem decode_gang(const Params& p, const Plan& pl, const int* units, int ubase, int L,
+                                              const TgTile& t, int w) {
+  TgItem it;
+  it.h = __builtin_amdgcn_readfirstlane(units[ubase + L]) & 1023;
+  it.shape = t.shape;
+  it.k0 = t.k0;
+  it.n0 = t.n0;
+  it.rows = t.rows;
+  it.ncols = t.ncols;
+  tg_finish<C>(p, pl, it, t.skip_r, t.skip_c, w);
+  return it;
+}
+
+// This wave's direct-to-LDS source for a tile: wave w fills rows
+// 16 (w % 2) .. + 16 of area w / 2, whose columns are the lhs's from k0 +
+// 128 a (a < na) or the rhs's from n0 + 128 (a - na), over the group's rows
+// (zero-size past the end of the stream).  Instruction i of a step fills 4
+// rows (1 KB); lane l takes row 16 (w % 2) + 4 i + l / 16 and 16-byte chunk
+// (l % 16) ^ swz_nn(row) of it (the row's low two bits are l / 16's).
+// Columns past the tile's valid part are loaded too (the next columns of the
+// row, or zeros past the group): they only feed output rows and columns that
+// the epilogue drops.
 struct TgDma {
-  __amdgpu_buffer_rsrc_t ra, rb;
+  __amdgpu_buffer_rsrc_t r;
+  int s2;  // bytes per operand row
+  int lo;  // lane part of the offset
 };
 
 template <class C>
-__device__ __forceinline__ TgDma tg_dma(const Params& p, const TgItem& it, bool live) {
-  const int K = p.K, N = p.N;
+__device__ __forceinline__ TgDma tg_dma(const Params& p, const TgItem& it, bool live, int w, int lane) {
+  const int a = w >> 1;
+  const bool lhs = a < it.na;
+  const int col = lhs ? it.k0 + 128 * a : it.n0 + 128 * (a - it.na);
+  const int width = lhs ? p.K : p.N;
+  const char* src = reinterpret_cast<const char*>(lhs ? p.lhs : p.rhs);
+  const long long off = ((long long)it.rlo * width + col) * 2;
+  const long long bytes = (long long)it.nrow * width * 2 - (long long)col * 2;
   TgDma d;
-  const BigItem& o = it.out;
-  const int k0 = o.row0 - it.h * K;
-  const char* a = reinterpret_cast<const char*>(p.lhs) + ((long long)it.rlo * K + k0) * 2;
-  const char* b = reinterpret_cast<const char*>(p.rhs) + ((long long)it.rlo * N + o.n0) * 2;
-  const int abytes = it.nrow * K * 2 - k0 * 2, bbytes = it.nrow * N * 2 - o.n0 * 2;
-  d.ra = uniform_rsrc(a, live && abytes > 0 ? abytes : 0);
-  d.rb = uniform_rsrc(b, live && bbytes > 0 ? bbytes : 0);
+  d.r = uniform_rsrc(src + off, live && bytes > 0 ? (int)bytes : 0);
+  d.s2 = __builtin_amdgcn_readfirstlane(width * 2);
+  const int q = lane >> 4;
+  d.lo = q * d.s2 + (((lane & 15) ^ swz_nn(q)) << 4);
   return d;
-}
-
-// This lane's offsets: instruction i of a wave fills contraction row
-// 4 w + 2 i + lane / 32 of the step, 16-byte chunk lane % 32 of the row,
-// which holds the tile's columns 8 c .. 8 c + 7 with c = (lane % 32) ^
-// swz_nn(row).
-struct TgOff {
-  int a[2], b[2];
-};
-
-__device__ __forceinline__ TgOff tg_offsets(int K, int N, int w, int lane) {
-  TgOff o;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 4 * w + 2 * i + (lane >> 5);
-    const int c = (lane & 31) ^ swz_nn(r);
-    o.a[i] = r * K * 2 + c * 16;
-    o.b[i] = r * N * 2 + c * 16;
-  }
-  return o;
 }
 
 // lane + uniform, added where it is used: the compiler would otherwise
@@ -188,25 +300,40 @@ __device__ __forceinline__ int add_at_use(int lane_part, int uniform) {
   return r;
 }
 
-// Direct-to-LDS operation J of contraction step k into stage `st`: J = 0, 1
-// the lhs, J = 2, 3 the other operand (1 KB each per wave).  The step's row
-// offset (sa, sb bytes per step) goes into the range-checked vector offset,
-// so rows past the group read as zeros.
+// Direct-to-LDS instruction J (0..3) of contraction step k into stage `st`.
 template <class C, int J>
-__device__ __forceinline__ void tg_dma_op(const TgDma& d, const TgOff& o, int k, int sa, int sb, char* st, int w) {
-  if constexpr (J < 2) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_ptr_t)(st + w * 2048 + J * 1024), 16,
-                                             add_at_use(o.a[J], k * sa), 0, 0, 0);
-  } else {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rb, (lds_ptr_t)(st + C::A_BYTES + w * 2048 + (J - 2) * 1024), 16,
-                                             add_at_use(o.b[J - 2], k * sb), 0, 0, 0);
-  }
+__device__ __forceinline__ void tg_dma_op(const TgDma& d, int k, char* st, int w) {
+  const int row = 16 * (w & 1) + 4 * J + C::BK * k;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.r, (lds_ptr_t)(st + (w >> 1) * C::AREA + (w & 1) * 4096 + J * 1024), 16,
+                                           add_at_use(d.lo, row * d.s2), 0, 0, 0);
 }
 
-// Per K half the refills issue twelve LDS transpose reads in a fixed order
-// (four lhs-side fragments, then two of the other side, two reads each), so
-// a half's fragments have completed once at most the twelve reads of the
-// following half are outstanding.
+// Lane part of a fragment's LDS address in a 256-byte-row area, for the
+// 32-column block at column 0 of the area and K half 0: in transpose read t,
+// lane l (q = l / 16, j = l % 16) points at row 8 (q / 2) + 4 t + j / 4 and
+// columns 16 (q % 2) + 4 (j % 4) + [0, 4) of the block; the read hands lane
+// l column l % 32 at rows 8 (l / 32) + 4 t + [0, 4).  Block b of the area
+// flips chunk bits 2-3 (byte bits 6-7), which the row swizzle also flips, so
+// it is an XOR of b << 6; the area and the K half add (bits 12 and up).  The
+// 32 lanes of an LDS cycle read four rows by four chunks, which the swizzle
+// puts in the four quarters of the 64 banks.
+__device__ __forceinline__ int tg_lane_off(int lane) {
+  const int q = lane >> 4, j = lane & 15;
+  const int row = 8 * (q >> 1) + (j >> 2);
+  const int chunk = (2 * (q & 1) + ((j >> 1) & 1)) ^ swz_nn(j >> 2);
+  return row * 256 + chunk * 16 + (j & 1) * 8;
+}
+
+template <int H>
+__device__ __forceinline__ i32x4 tg_frag(unsigned addr) {
+  const i32x2 lo = ds_read_tr16<H * 16 * 256>(addr);
+  const i32x2 hi = ds_read_tr16<H * 16 * 256 + 4 * 256>(addr);
+  return i32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Per K half the refills issue twelve LDS transpose reads in slot order (six
+// slots, two reads each), so a half's fragments have completed once at most
+// the twelve reads of the following half are outstanding.
 __device__ __forceinline__ void tg_frags_ready() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (12 << 8) | (0x3 << 14));
 }
@@ -253,20 +380,22 @@ constexpr int kSchedOff = 0, kSchedTiles = 12, kSchedSlot = 24;
 // Deal the units to nq queues, each to the queue with the least work so far
 // (the lowest index on ties), in the group order (largest first), so each
 // queue's units are in that order too.  A tile's work is its contraction
-// steps plus two for the epilogue.  A group is split into quadrants when its
-// tiles take more than a quarter of a workgroup's share of all the work (at
-// most kMaxSplit groups, the largest).  Wave 0 runs it: the greedy choice is
-// made in scalar registers, unit after unit, recording each unit's queue,
-// place in the queue and first tile; the lists are then written in parallel.
+// steps plus two for the epilogue.  gang_tiles > 0 (the gang schedule): the
+// units are whole groups of gang_tiles tiles each.  Otherwise a group's tiles
+// are its nkt x nnt grid, and a group is split into quadrants when its tiles
+// take more than a quarter of a workgroup's share of all the work (at most
+// kMaxSplit groups, the largest).  Wave 0 runs it: the greedy choice is made
+// in scalar registers, unit after unit, recording each unit's queue, place
+// in the queue and first tile; the lists are then written in parallel.
 template <class C>
 __device__ inline void tg_deal(const Plan& pl, const int* order, char* smem, int* units, int* ustart, int* sched,
-                               int nq, int P, const TgGrid& gr, int lane) {
+                               int nq, int P, const TgGrid& gr, int gang_tiles, int lane) {
   using Lds = TgLds<C>;
   int* const rec_unit = reinterpret_cast<int*>(smem + Lds::REC_UNIT);
   int* const rec_pos = reinterpret_cast<int*>(smem + Lds::REC_POS);
   int* const rec_start = reinterpret_cast<int*>(smem + Lds::REC_START);
   const int ga = pl.ga;
-  const int per = gr.nnt * gr.nkt;
+  const int per = gang_tiles > 0 ? gang_tiles : gr.nnt * gr.nkt;
   auto tile_cost = [&](int i) {
     const int h = order[i];
     const int st = (pl.row_start[h + 1] - pl.row_start[h] + C::BK - 1) / C::BK;
@@ -298,12 +427,12 @@ __device__ inline void tg_deal(const Plan& pl, const int* order, char* smem, int
       const int cj = __builtin_amdgcn_readlane(cost, jj);
       const int hj = __builtin_amdgcn_readlane(h, jj);
       // a tile longer than a quarter of a workgroup's share: cost > total / (4 P)
-      const bool split = per > 1 && nsplit < kMaxSplit && 4ll * P * cj > total;
+      const bool split = gang_tiles == 0 && per > 1 && nsplit < kMaxSplit && 4ll * P * cj > total;
       nsplit += split;
       for (int qd = 0; qd < (split ? 4 : 1); ++qd) {
         const int nk = !split ? gr.nkt : (qd & 1) ? gr.nkt - gr.ka : gr.ka;
         const int nn = !split ? gr.nnt : (qd & 2) ? gr.nnt - gr.na : gr.na;
-        const int nt = nk * nn;
+        const int nt = gang_tiles > 0 ? gang_tiles : nk * nn;
         if (nt == 0) continue;
         int q = 0, best = load[0];
 #pragma unroll
@@ -365,6 +494,102 @@ __device__ __forceinline__ int tg_grab_wave(int* counter, int lane, bool live) {
   return __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, r, lane * 4, 0, 0);
 }
 
+// Epilogue of one tile, as the big kernel's (big_epilogue): block (fm, fn)
+// of the wave is accumulator fm * FN + fn; lane (kh, r32) holds row
+// rbase + 32 fm + r32 and, in register 4 g + i, column cbase + 32 fn + 8 g +
+// 4 kh + i.  The permlane32 swap of groups (g, g+1) leaves each lane eight
+// consecutive columns, and each 32-row block passes through the wave's 4 KB
+// staging slice so that a store writes eight whole 128-byte row segments.
+// With bf16 output a staging row holds 64 columns: two column blocks, or the
+// last block of a three-block wave alone (the other half of the row is not
+// stored).  Stores outside the tile's valid rows and columns are dropped by
+// the range check, those in its skipped part by an out-of-range offset, and
+// a tile with fewer blocks pads to the full tile's store count E.
+template <class C, int FM, int FN>
+__device__ __forceinline__ void tg_epilogue(const Params& p, const f32x16 (&acc)[C::NACC], const TgItem& it, char* stg,
+                                            int kh, int r32, int lane) {
+  const int N = p.N;
+  const __amdgpu_buffer_rsrc_t ro = uniform_rsrc(reinterpret_cast<char*>(p.out) + it.obase, it.nrec);
+  const int rbase = it.rc & 0xFFFF, cbase = it.rc >> 16;
+  const int skip_r = it.skip & 0xFFFF, skip_c = it.skip >> 16;
+  const int srow = lane >> 3, schunk = lane & 7;  // store phase: row and chunk of this lane
+  const int wr_row = r32 * 128;                   // write phase: this lane's staging row
+  // rows srow + 8 i of the staged block back out, as whole row segments;
+  // col0: the block's first column in the tile, cw: columns per chunk, nch:
+  // chunks of the row that hold data
+  auto drain = [&](int fm, int col0, int cw, int nch) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = srow + 8 * i;
+      const i32x4 d = *reinterpret_cast<const i32x4*>(stg + row * 128 + ((schunk ^ swz_out(row)) << 4));
+      const int col = col0 + cw * schunk;
+      const int trow = rbase + fm * 32 + row;
+      const bool keep = col < it.ncols && schunk < nch && !(trow < skip_r && col < skip_c);
+      const int voff = keep ? trow * N * C::es_out + col * C::es_out : (int)0x80000000;
+      __builtin_amdgcn_raw_buffer_store_b128(d, ro, voff, 0, 0);
+    }
+  };
+  auto stage_write = [&](int chunk, i32x4 v) __attribute__((always_inline)) {
+    *reinterpret_cast<i32x4*>(stg + wr_row + ((chunk ^ swz_out(r32)) << 4)) = v;
+  };
+  // bf16: columns 32 fn + [0, 32) of row block fm into chunks 4 (fn % 2) + ...
+  auto stage_bf16 = [&](int fm, int fn) __attribute__((always_inline)) {
+#pragma unroll
+    for (int gp = 0; gp < 4; gp += 2) {
+      uint32_t x0[2], x1[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const f32x16& a = acc[fm * FN + fn];
+        x0[x] = pk_bf16_rne(a[4 * (gp + x) + 0], a[4 * (gp + x) + 1]);
+        x1[x] = pk_bf16_rne(a[4 * (gp + x) + 2], a[4 * (gp + x) + 3]);
+      }
+      const auto r0 = __builtin_amdgcn_permlane32_swap(x0[0], x0[1], false, false);
+      const auto r1 = __builtin_amdgcn_permlane32_swap(x1[0], x1[1], false, false);
+      stage_write(4 * (fn & 1) + gp + kh, i32x4{(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1]});
+    }
+  };
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    if constexpr (C::OUT_F32) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+        for (int gp = 0; gp < 4; gp += 2) {
+          int lo[4], hi[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[fm * FN + fn][4 * gp + i]),
+                                                            __float_as_uint(acc[fm * FN + fn][4 * (gp + 1) + i]),
+                                                            false, false);
+            lo[i] = (int)r[0];
+            hi[i] = (int)r[1];
+          }
+          // 32 columns of 4 bytes per staging row: chunks 2 (gp + kh) + {0, 1}
+          stage_write(2 * (gp + kh), i32x4{lo[0], lo[1], lo[2], lo[3]});
+          stage_write(2 * (gp + kh) + 1, i32x4{hi[0], hi[1], hi[2], hi[3]});
+        }
+        drain(fm, cbase + fn * 32, 4, 8);
+      }
+    } else {
+#pragma unroll
+      for (int fn = 0; fn < FN; fn += 2) {
+        stage_bf16(fm, fn);
+        if (fn + 1 < FN) stage_bf16(fm, fn + 1);
+        drain(fm, cbase + fn * 32, 8, fn + 1 < FN ? 8 : 4);
+      }
+    }
+  }
+  // pad to the full tile's store count with range-dropped stores, each to
+  // an address of its own: the compiler deletes a store that repeats an
+  // earlier one, and every dropped one would leave the K loop's constant
+  // waits one operation short
+  constexpr int kIssued = C::OUT_F32 ? FM * FN * 4 : FM * ((FN + 1) / 2) * 4;
+  static_assert(kIssued <= C::E, "store count");
+#pragma unroll
+  for (int i = kIssued; i < C::E; ++i)
+    __builtin_amdgcn_raw_buffer_store_b128(i32x4{0, 0, 0, 0}, ro, (int)0x80000000, 64 * i, 0);
+}
+
 template <class C>
 __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
   using Lds = TgLds<C>;
@@ -397,14 +622,22 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
   // divides evenly and there are groups enough to deal, else one
   const int nq = P % kQueues == 0 && pl.ga >= 2 * kQueues ? kQueues : 1;
   const int x = blockIdx.x % nq;
-  if (w == 0) tg_deal<C>(pl, order, smem, units, ustart, sched, nq, P, gr, lane);
-  __syncthreads();
-  // this queue's units [ucur, u_end) and tiles [0, n_items)
-  int ucur = __builtin_amdgcn_readfirstlane(sched[kSchedOff + x]);
-  const int u_end = __builtin_amdgcn_readfirstlane(sched[kSchedOff + x + 1]);
-  const int n_items = __builtin_amdgcn_readfirstlane(sched[kSchedTiles + x]);
-  int* const counter = p.queue + x;
   const int W = P / nq, j = blockIdx.x / nq;  // workgroups of the queue, this one's place
+  const TgGang gg = tg_gang_plan(K, N);
+  const bool gang = nq == kQueues && gg.T <= W && 4 * gg.T >= 3 * W;
+  // the gang schedule's tile of this workgroup, the same in every group
+  const TgTile tj = tg_gang_tile(gg, K, N, j < gg.T ? j : 0);
+  const int gang_tiles = gg.T;
+  if (w == 0) tg_deal<C>(pl, order, smem, units, ustart, sched, nq, P, gr, gang ? gang_tiles : 0, lane);
+  __syncthreads();
+  // this queue's units [ucur, u_end) and items [0, n_items): tiles
+  // (dynamic) or groups (gang; none for a workgroup past the tile count)
+  int ucur = __builtin_amdgcn_readfirstlane(sched[kSchedOff + x]);
+  const int ubase = ucur;
+  const int u_end = __builtin_amdgcn_readfirstlane(sched[kSchedOff + x + 1]);
+  const int n_items = gang ? (j < gang_tiles ? u_end - ubase : 0)
+                           : __builtin_amdgcn_readfirstlane(sched[kSchedTiles + x]);
+  int* const counter = p.queue + x;
   // Output groups the plan dropped (a group offset past G - Ga, which is
   // flagged) are zero.  K * N is a multiple of 64, so 16-byte stores tile it.
   {
@@ -414,7 +647,8 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
       *reinterpret_cast<i32x4*>(o + off) = i32x4{0, 0, 0, 0};
   }
   // The last workgroup of the queue to get here resets its counters; every
-  // index this workgroup grabbed has returned by then (each was used).
+  // index this workgroup grabbed (dynamic), every arrival it counted (gang),
+  // has returned by then.
   auto finish = [&]() {
     if (tid == 0) {
       const int prev = atomicAdd(p.queue + kQueues + x, 1);
@@ -425,100 +659,98 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
     }
   };
 
-  // Tile indices: the queue's first two rounds are fixed, workgroup j of the
-  // queue's W taking tiles j and 2W-1-j (had each grabbed its first two, the
-  // first workgroups would take two of the longest tiles each); afterwards
-  // each tile grabs the index of the tile after next during its first steps
-  // (so the next tile is known before its loads start), from 2W on.
-  int L_cur = j;
-  int L_nxt = 2 * W - 1 - j;
+  // Item indices.  Gang: 0, 1, 2, ...  Dynamic: the queue's first two rounds
+  // are fixed, workgroup j of the queue's W taking tiles j and 2W-1-j (had
+  // each grabbed its first two, the first workgroups would take two of the
+  // longest tiles each); afterwards each tile grabs the index of the tile
+  // after next during its first steps (so the next tile is known before its
+  // loads start), from 2W on.
+  int L_cur = gang ? 0 : j;
+  int L_nxt = gang ? 1 : 2 * W - 1 - j;
   if (L_cur >= n_items) {
     finish();
     return;
   }
+  auto decode = [&](int L) __attribute__((always_inline)) {
+    return gang ? decode_gang<C>(p, pl, units, ubase, L, tj, w)
+                : decode_tg<C>(p, pl, units, ustart, &ucur, u_end, L, gr, w, lane);
+  };
 
-  TgItem cur = decode_tg<C>(pl, units, ustart, &ucur, u_end, L_cur, gr, K, N, w, lane);
+  TgItem cur = decode(L_cur);
   bool last_item = L_nxt >= n_items;
   TgItem nxt = cur;
-  if (!last_item) nxt = decode_tg<C>(pl, units, ustart, &ucur, u_end, L_nxt, gr, K, N, w, lane);
-  TgDma dcur = tg_dma<C>(p, cur, true);
-  TgDma dnxt = tg_dma<C>(p, nxt, !last_item);
-  const TgOff off = tg_offsets(K, N, w, lane);
-  const int sa = C::BK * K * 2, sb = C::BK * N * 2;  // bytes per contraction step
+  if (!last_item) nxt = decode(L_nxt);
+  TgDma dcur = tg_dma<C>(p, cur, true, w, lane);
+  TgDma dnxt = tg_dma<C>(p, nxt, !last_item, w, lane);
 
   // Prologue: the first tile's steps 0..2; every older memory operation is
   // complete after the wait, so the loop's counts start from an empty queue.
 #pragma unroll
   for (int s = 0; s < C::S - 1; ++s) {
-    tg_dma_op<C, 0>(dcur, off, s, sa, sb, smem + s * C::STAGE, w);
-    tg_dma_op<C, 1>(dcur, off, s, sa, sb, smem + s * C::STAGE, w);
-    tg_dma_op<C, 2>(dcur, off, s, sa, sb, smem + s * C::STAGE, w);
-    tg_dma_op<C, 3>(dcur, off, s, sa, sb, smem + s * C::STAGE, w);
+    tg_dma_op<C, 0>(dcur, s, smem + s * C::STAGE, w);
+    tg_dma_op<C, 1>(dcur, s, smem + s * C::STAGE, w);
+    tg_dma_op<C, 2>(dcur, s, smem + s * C::STAGE, w);
+    tg_dma_op<C, 3>(dcur, s, smem + s * C::STAGE, w);
   }
   wait_vmcnt<0>();
   __syncthreads();
 
-  // lane part of a fragment address for the first 32 columns of a
-  // 128-column half; the next 32 are the same XOR 64 (chunk bit 2, which the
-  // K-row swizzle leaves alone) and a block 64 columns on XORs 128
-  const int lo0 = nn_lane_off(lane, 0);
-  // fragment f of K half h from an operand area: 32 rows (lhs side) or
-  // columns (other side) starting 32 f past the wave's first one `base`
-  // The XOR is formed at each use (volatile, so it is not hoisted): hoisted,
-  // the lane parts of every fragment of both tile layouts stay live across
-  // the loop and push the kernel past its register budget into spills.
-  auto frag = [&](const char* area, int base, int f, int h) __attribute__((always_inline)) {
-    const int cb = base * 2 + f * 64;  // byte offset of the block in a K row
+  const int lo0 = tg_lane_off(lane);
+  // fragment slot s of K half h of the step in stage `st`, for the layout of
+  // `it`.  The XOR is formed at each use (volatile, so it is not hoisted):
+  // hoisted, the lane parts of every slot of both tiles stay live across the
+  // loop and push the kernel past its register budget into spills.
+  auto frag = [&](const char* st, const TgItem& it, int s, int h) __attribute__((always_inline)) {
     int lane_part;
-    asm volatile("v_xor_b32 %0, %1, %2" : "=v"(lane_part) : "v"(lo0), "s"(cb & 192));
-    const unsigned addr = (unsigned)(size_t)(lds_ptr_t)(area + (cb & ~192)) + (unsigned)lane_part;
-    return h ? nn_frag<1>(addr) : nn_frag<0>(addr);
-  };
-  auto a_frag = [&](const char* st, const TgItem& it, int f, int h) __attribute__((always_inline)) {
-    return frag(st, it.out.rbase, f, h);
-  };
-  auto b_frag = [&](const char* st, const TgItem& it, int f, int h) __attribute__((always_inline)) {
-    return frag(st + C::A_BYTES, it.out.cbase, f, h);
+    int so;
+    switch (s) {
+      case 0: so = tg_slot_off<0>(it); break;
+      case 1: so = tg_slot_off<1>(it); break;
+      case 2: so = tg_slot_off<2>(it); break;
+      case 3: so = tg_slot_off<3>(it); break;
+      case 4: so = tg_slot_off<4>(it); break;
+      default: so = tg_slot_off<5>(it); break;
+    }
+    asm volatile("v_xor_b32 %0, %1, %2" : "=v"(lane_part) : "v"(lo0), "s"(so));
+    const unsigned addr = (unsigned)(size_t)(lds_ptr_t)st + (unsigned)lane_part;
+    return h ? tg_frag<1>(addr) : tg_frag<0>(addr);
   };
 
-  i32x4 a[C::FM][2], b[C::FN][2];
+  i32x4 f[C::NSLOT][2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int f = 0; f < C::FM; ++f) a[f][h] = a_frag(smem, cur, f, h);
-#pragma unroll
-    for (int f = 0; f < C::FN; ++f) b[f][h] = b_frag(smem, cur, f, h);
-  }
+    for (int s = 0; s < C::NSLOT; ++s) f[s][h] = frag(smem, cur, s, h);
 
   // The transpose reads write their registers when the data arrives, but the
-  // compiler takes an asm output as written when the asm issues: a fragment
-  // it sees no later use of (a[2..3] in a half tile, or every refill after
-  // the last step) would have its registers handed to other values, which
-  // the arriving data then overwrites.  Each fragment is therefore used here,
-  // after the wait that guarantees its data has arrived.
+  // compiler takes an asm output as written when the asm issues: a slot it
+  // sees no later use of (a slot the shape does not use, or every refill
+  // after the last step) would have its registers handed to other values,
+  // which the arriving data then overwrites.  Each slot is therefore used
+  // here, after the wait that guarantees its data has arrived.
   auto hold = [&](int h) __attribute__((always_inline)) {
-    asm volatile("" ::"v"(a[0][h]), "v"(a[1][h]), "v"(a[2][h]), "v"(a[3][h]), "v"(b[0][h]), "v"(b[1][h]));
+    asm volatile("" ::"v"(f[0][h]), "v"(f[1][h]), "v"(f[2][h]), "v"(f[3][h]), "v"(f[4][h]), "v"(f[5][h]));
   };
 
-  f32x16 acc[C::FM][C::FN];
+  f32x16 acc[C::NACC];
   int stage = 0;
   int L_new = 0;  // the grabbed index handed over during the current tile
 
-  // One contraction step s (as the big kernel's K step, without a bias
-  // row): step s+1's operands are complete once at most WAIT newer
-  // operations are outstanding -- step s+2's four loads and, in a tile's
-  // first two steps, the previous tile's E stores (and in the second, the
-  // tile-index grab issued after the first).  The barrier frees the
-  // stage step s-1 used, which takes step s+3 (this tile's step kd, or the
-  // next tile's when NEXT); fragments are refilled with step s+1's right
-  // after their last use.
-  auto kstep = [&](auto full_tag, auto wait_tag, auto next_tag, auto last_tag, int kd)
+  // One contraction step (as the big kernel's K step, without a bias row):
+  // the next step's operands are complete once at most WAIT newer
+  // operations are outstanding -- the step after's four loads and, in a
+  // tile's first two steps, the previous tile's E stores (and in the second,
+  // the tile-index grab issued after the first).  The barrier frees the
+  // stage the step before last used, which takes step kd (this tile's, or
+  // the next tile's when NEXT); slots are refilled with the next step's
+  // fragments right after their last use, in slot order.
+  auto kstep = [&](auto shape_tag, auto wait_tag, auto next_tag, auto last_tag, int kd)
       __attribute__((always_inline)) {
-    constexpr bool FULL = decltype(full_tag)::value;
+    using SC = TgShapeCfg<decltype(shape_tag)::value>;
     constexpr int WAIT = decltype(wait_tag)::value;
     constexpr bool NEXT = decltype(next_tag)::value, LAST = decltype(last_tag)::value;
-    constexpr int FMA = FULL ? C::FM : C::FM / 2;
-    constexpr int NM = 2 * FMA * C::FN;  // MFMAs per step
+    constexpr int NMH = SC::FM * SC::FN;  // MFMAs per K half
+    constexpr int NM = 2 * NMH;
     wait_vmcnt<WAIT>();
     if constexpr (LAST) __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
     ring_barrier();
@@ -526,30 +758,31 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
     char* st3 = smem + ((stage + 3) & (C::S - 1)) * C::STAGE;
     const char* st1 = smem + ((stage + 1) & (C::S - 1)) * C::STAGE;
     const TgItem& it1 = LAST ? nxt : cur;
+    auto dma_at = [&](int m) __attribute__((always_inline)) {
+      if (m == 0 * NM / 4) tg_dma_op<C, 0>(d, kd, st3, w);
+      if (m == 1 * NM / 4) tg_dma_op<C, 1>(d, kd, st3, w);
+      if (m == 2 * NM / 4) tg_dma_op<C, 2>(d, kd, st3, w);
+      if (m == 3 * NM / 4) tg_dma_op<C, 3>(d, kd, st3, w);
+    };
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       tg_frags_ready();
       hold(h);
+      int m = h * NMH;
 #pragma unroll
-      for (int fm = 0; fm < FMA; ++fm) {
+      for (int fm = 0; fm < SC::FM; ++fm) {
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) {
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b[fn][h]),
-                                                                __builtin_bit_cast(bf16x8, a[fm][h]),
-                                                                acc[fm][fn], 0, 0, 0);
-          const int m = (h * FMA + fm) * C::FN + fn;
-          if (m == 0 * NM / 4) tg_dma_op<C, 0>(d, off, kd, sa, sb, st3, w);
-          if (m == 1 * NM / 4) tg_dma_op<C, 1>(d, off, kd, sa, sb, st3, w);
-          if (m == 2 * NM / 4) tg_dma_op<C, 2>(d, off, kd, sa, sb, st3, w);
-          if (m == 3 * NM / 4) tg_dma_op<C, 3>(d, off, kd, sa, sb, st3, w);
+        for (int fn = 0; fn < SC::FN; ++fn) {
+          acc[fm * SC::FN + fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, f[SC::BS + fn][h]), __builtin_bit_cast(bf16x8, f[fm][h]),
+              acc[fm * SC::FN + fn], 0, 0, 0);
+          dma_at(m++);
           __builtin_amdgcn_sched_barrier(0);  // keep this order
         }
-        a[fm][h] = a_frag(st1, it1, fm, h);
+        f[fm][h] = frag(st1, it1, fm, h);
       }
 #pragma unroll
-      for (int fm = FMA; fm < C::FM; ++fm) a[fm][h] = a_frag(st1, it1, fm, h);
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn) b[fn][h] = b_frag(st1, it1, fn, h);
+      for (int s = SC::FM; s < C::NSLOT; ++s) f[s][h] = frag(st1, it1, s, h);
       __builtin_amdgcn_sched_barrier(0);
     }
     stage = (stage + 1) & (C::S - 1);
@@ -562,51 +795,55 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
   using W0G = std::integral_constant<int, C::DMA_STEP + C::E + 1>;
   using W1 = std::integral_constant<int, C::DMA_STEP>;
   // One tile of cur.steps >= 5 steps.
-  auto ktile = [&](auto full_tag) __attribute__((always_inline)) {
-    constexpr bool FULL = decltype(full_tag)::value;
-    constexpr int FMA = FULL ? C::FM : C::FM / 2;
+  auto ktile = [&](auto shape_tag) __attribute__((always_inline)) {
+    using SC = TgShapeCfg<decltype(shape_tag)::value>;
+#pragma unroll
+    for (int i = 0; i < SC::FM * SC::FN; ++i)
+#pragma unroll
+      for (int z = 0; z < 16; ++z) acc[i][z] = 0.f;
     const int KT = cur.steps;
-    kstep(full_tag, W0{}, F_{}, F_{}, 3);
+    kstep(shape_tag, W0{}, F_{}, F_{}, 3);
     // the grab of the tile after next, by wave 0 unless this tile has no
-    // successor: exactly one counted operation in every wave
-    const int g = tg_grab_wave(counter, lane, w == 0 && !last_item);
-    kstep(full_tag, W0G{}, F_{}, F_{}, 4);
-    for (int kt = 2; kt + 3 < KT; ++kt) kstep(full_tag, W1{}, F_{}, F_{}, kt + 3);
-    kstep(full_tag, W1{}, T_{}, F_{}, 0);  // kt = KT-3: the next tile's step 0
+    // successor (or the schedule is the gang's): exactly one counted
+    // operation in every wave
+    const int g = tg_grab_wave(counter, lane, w == 0 && !last_item && !gang);
+    kstep(shape_tag, W0G{}, F_{}, F_{}, 4);
+    for (int kt = 2; kt + 3 < KT; ++kt) kstep(shape_tag, W1{}, F_{}, F_{}, kt + 3);
+    // gang: meet the queue's other workgroups before the next group's loads
+    if (gang && !last_item && w == 0) tg_gang_meet(counter, gang_tiles * L_nxt, lane);
+    kstep(shape_tag, W1{}, T_{}, F_{}, 0);  // kt = KT-3: the next tile's step 0
     // the grab has returned (this step's wait left only the loads of the
     // step before outstanding); hand it to every wave, which reads it after
     // the last step's barrier
     if (w == 0 && lane == 0 && !last_item) sched[kSchedSlot] = g;
-    kstep(full_tag, W1{}, T_{}, F_{}, 1);
-    kstep(full_tag, W1{}, T_{}, T_{}, 2);
+    kstep(shape_tag, W1{}, T_{}, F_{}, 1);
+    kstep(shape_tag, W1{}, T_{}, T_{}, 2);
     // every refill has landed before the epilogue takes registers of its own
     __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
     hold(0);
     hold(1);
-    L_new = 2 * W + __builtin_amdgcn_readfirstlane(sched[kSchedSlot]);
+    L_new = gang ? L_nxt + 1 : 2 * W + __builtin_amdgcn_readfirstlane(sched[kSchedSlot]);
     // the last step's stage holds the epilogue's staging slices, 4 KB per wave
-    big_epilogue<C, FMA, false>(p, acc, cur.out, smem, smem + ((stage + 3) & (C::S - 1)) * C::STAGE + w * 4096, kh, r32,
-                         lane);
+    tg_epilogue<C, SC::FM, SC::FN>(p, acc, cur, smem + ((stage + 3) & (C::S - 1)) * C::STAGE + w * 4096, kh, r32,
+                                   lane);
   };
 
   while (true) {
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-        for (int z = 0; z < 16; ++z) acc[i][j][z] = 0.f;
-    if (!cur.out.half)
-      ktile(std::true_type{});
+    if (cur.shape == kTgFull)
+      ktile(std::integral_constant<int, kTgFull>{});
+    else if (cur.shape == kTgHalf)
+      ktile(std::integral_constant<int, kTgHalf>{});
+    else if (cur.shape == kTgTall)
+      ktile(std::integral_constant<int, kTgTall>{});
     else
-      ktile(std::false_type{});
+      ktile(std::integral_constant<int, kTgWide>{});
     if (last_item) break;
     L_nxt = L_new;
     last_item = L_nxt >= n_items;
     cur = nxt;
     dcur = dnxt;
-    if (!last_item) nxt = decode_tg<C>(pl, units, ustart, &ucur, u_end, L_nxt, gr, K, N, w, lane);
-    dnxt = tg_dma<C>(p, nxt, !last_item);
+    if (!last_item) nxt = decode(L_nxt);
+    dnxt = tg_dma<C>(p, nxt, !last_item, w, lane);
   }
   finish();
 }

@@ -524,9 +524,9 @@ def _fake(shape, dtype, addr=1 << 20):
 
 
 def test_output_tile_beyond_32bit_offsets_is_unsupported():
-    """The epilogues address a 256-row output tile with 32-bit byte offsets:
-    gmm_run and gmm_tgmm_run reject an N whose 256-row output tile reaches
-    2 GiB (checked on the host; nothing is launched)."""
+    """The epilogues address a 256-row output tile (tgmm: up to 384 rows)
+    with 32-bit byte offsets: gmm_run and gmm_tgmm_run reject an N whose
+    output tile reaches 2 GiB (checked on the host; nothing is launched)."""
     import ctypes
 
     import moe_grouped_matrix_amd._binding as b
@@ -542,6 +542,11 @@ def test_output_tile_beyond_32bit_offsets_is_unsupported():
         st = lib.gmm_tgmm_run(h, ctypes.byref(tl), ctypes.byref(tr), ctypes.byref(gs), None, ctypes.byref(tout),
                               None)
         assert st == b.GMM_E_UNSUPPORTED and b"output tile" in lib.gmm_last_error(h), (out_dtype, N)
+    # tgmm's 384-row tiles: an f32 N that a 256-row tile would allow
+    N = 1_500_000
+    tl, tr, tout = _fake((16, K), b.GMM_BF16), _fake((16, N), b.GMM_BF16), _fake((1, K, N), b.GMM_F32)
+    st = lib.gmm_tgmm_run(h, ctypes.byref(tl), ctypes.byref(tr), ctypes.byref(gs), None, ctypes.byref(tout), None)
+    assert st == b.GMM_E_UNSUPPORTED and b"384-row output tile" in lib.gmm_last_error(h)
     # one column less than the limit passes the check (and then fails on the
     # overlap of the fake tensors, still before anything is queued)
     lhs, rhs = _fake((1, K), b.GMM_BF16), _fake((1, 4_194_296, K), b.GMM_BF16)

@@ -6,8 +6,8 @@ not multiples of the 32-row step), groups shorter than the kernel's five
 steps, empty groups (all-zero bits), K and N tails past the 256-column tiles
 (down to 8 columns), a group offset, f32 and bf16 outputs, rows outside the
 active groups (ignored), invalid device sizes (clamped and flagged), and
-both tile schedules (one work queue, and one per XCD over two calls in a
-row).  The
+both tile schedules (dynamic: one work queue, and one per XCD over two
+calls in a row; gang: every tile shape, bit-exact on small integers).  The
 full-size case (the forward workload's shapes) runs in the benchmark's
 launch configuration and compares sampled output rows.
 
@@ -88,6 +88,50 @@ def test_tgmm_work_queues_back_to_back():
         assert m.device_flags() == 0
         ref = oracle.tgmm_reference(lhs, rhs, gs)
         _check(out.cpu(), ref, sizes, 0, torch.float32, f"tgmm queues {n_groups} groups")
+
+
+# (K, N, grid limit, tiles per group T, workgroups per XCD queue W): shapes
+# and grids on which the gang schedule runs (at least 16 groups, a grid that
+# is a multiple of 8, 3/4 W <= T <= W), covering each tile shape: full tiles
+# (one with more than 128 but fewer than 256 valid rows), the L tile with its
+# skipped quadrant, tall and wide tiles with partial extents, and a queue with
+# an idle workgroup (T < W)
+GANG = [
+    (384, 384, 32, 3, 4),      # full + tall + wide, one idle workgroup per queue
+    (448, 384, 32, 4, 4),      # a partial full tile (192 rows), two tall tiles
+    (640, 1408, 128, 15, 16),  # L tile, one tall, three wide; one idle workgroup
+    (1408, 1408, 0, 32, 32),   # the model's shape: 25 full, L, 3 tall, 3 wide
+]
+GANG_SIZES = [0, 37, 300, 5, 128, 77, 0, 250, 33, 96, 1, 160, 64, 200, 31, 400, 17, 90]
+
+
+@pytest.mark.parametrize("K,N,limit,T,W", GANG, ids=[f"{k}x{n}" for k, n, *_ in GANG])
+def test_tgmm_gang_schedule_bit_exact(K, N, limit, T, W):
+    """Small-integer operands (every sum exact in fp32): the gang schedule's
+    output must equal the oracle bit for bit, f32 and bf16 (rounded once),
+    on every element; empty groups all-zero bits; two calls in a row."""
+    import moe_grouped_matrix_amd as m
+    g = torch.Generator().manual_seed(K + N)
+    sizes = GANG_SIZES
+    M = sum(sizes) + 11
+    lhs = torch.randint(-3, 4, (M, K), generator=g).to(torch.bfloat16)
+    rhs = torch.randint(-3, 4, (M, N), generator=g).to(torch.bfloat16)
+    gs = torch.tensor(sizes, dtype=torch.int32)
+    ref = oracle.tgmm_reference(lhs, rhs, gs)
+    m.set_grid_limit(limit)
+    try:
+        for out_dtype in (torch.float32, torch.bfloat16):
+            for call in range(2):
+                print(f"tgmm gang K={K} N={N} grid {limit or 'full'}: T={T} of W={W}, out {out_dtype}, call {call}",
+                      flush=True)
+                out = m.tgmm(lhs.cuda(), rhs.cuda(), gs.cuda(), out_dtype=out_dtype).cpu()
+                iv = torch.int16 if out_dtype == torch.bfloat16 else torch.int32
+                want = oracle.round_to(ref, out_dtype)
+                bad = (out.view(iv) != want.view(iv)).nonzero()
+                assert bad.numel() == 0, f"{bad.shape[0]} elements differ, first {bad[:4].tolist()}"
+        assert m.device_flags() == 0
+    finally:
+        m.set_grid_limit(0)
 
 
 def test_tgmm_invalid_sizes_are_clamped_and_flagged():
