@@ -6,11 +6,12 @@ counters differs (the library's static device scratch, cleared by the call,
 against a per-stream block of the handle).  Each output tile is summed by one
 workgroup in a fixed order whichever workgroup takes it, so the outputs must
 agree bit for bit, and both must meet the float32 / bfloat16 tolerances of
-tests/parity.py against the oracle.  Two calls in a row on a stream no tgmm
-call has used, the second smaller (one work queue instead of eight, fewer
-rows and columns, a bf16 output), queued back to back before one
-synchronisation: the scratch keeps the first call's state until the second
-clears it."""
+tests/parity.py against the oracle.  Three calls in a row on a stream no
+tgmm call has used, each smaller than the one before (the gang schedule at
+the model's K = N = 1408, whose workgroups meet on the counters; the
+dynamic schedule over eight work queues; one work queue, fewer rows and
+columns, a bf16 output), queued back to back before one synchronisation:
+the scratch keeps each call's state until the next clears it."""
 import pytest
 import torch
 
@@ -21,6 +22,10 @@ pytestmark = pytest.mark.gpu
 
 CASES = [
     # (group sizes, rows past the groups, K, N, out dtype)
+    # the model's K = N = 1408 over 16 groups: the gang schedule (32 tiles per
+    # group, one per workgroup of an XCD, meeting on the scratch counters)
+    ([50, 0, 33, 64, 1, 96, 20, 0, 64, 30, 17, 129, 0, 48, 5, 22], 4, 1408, 1408, torch.float32),
+    # the dynamic schedule (its tiles handed out through the same counters)
     ([700, 0, 33, 250, 1, 96, 512, 0, 64, 300, 17, 129, 0, 480, 5, 222, 40, 610], 9, 512, 520, torch.float32),
     ([40, 0, 300, 7], 3, 256, 136, torch.bfloat16),
 ]
