@@ -78,14 +78,17 @@ struct TgShapeCfg {
   static_assert(FM * FN <= 8 && BS + FN <= 6, "shape fits the accumulators and slots");
 };
 
-// Gang schedule: the queue's workgroups meet once per group.  Lane 0 of wave
-// 0 adds one to the queue's counter and waits until it reaches `target` (the
-// arrivals of every workgroup of the queue at this group), for at most
-// kGangSpin polls of a few hundred cycles each; the wait only keeps the
-// workgroups in step (shared L2 reads), the results never depend on it.  The
-// atomic's return and the polls are waited for by the compiler (vmcnt 0),
-// which only makes the loop's later constant waits hold sooner.
+// Gang schedule: the queue's workgroups meet before each group's first
+// loads.  Every workgroup of the queue meets equally often, so at its n-th
+// meet lane 0 of wave 0 adds one to the queue's counter and waits until it
+// reaches n T (T workgroups), for at most kGangSpin polls of a few hundred
+// cycles each; the wait only keeps the workgroups in step (shared L2 reads),
+// the results never depend on it.  The atomic's return and the polls are
+// waited for by the compiler (vmcnt 0), which only makes the loop's later
+// constant waits hold sooner.
 constexpr int kGangSpin = 2048;
+// a group boundary's cost in steps, for the deal (measured)
+constexpr int kGangBoundarySteps = 9;
 
 __device__ __forceinline__ void tg_gang_meet(int* counter, int target, int lane) {
   if (lane == 0) {
@@ -396,10 +399,14 @@ __device__ inline void tg_deal(const Plan& pl, const int* order, char* smem, int
   int* const rec_start = reinterpret_cast<int*>(smem + Lds::REC_START);
   const int ga = pl.ga;
   const int per = gang_tiles > 0 ? gang_tiles : gr.nnt * gr.nkt;
+  // a group boundary of the gang schedule (the epilogue of all of an XCD's
+  // tiles at once, the meet, the refill) costs about nine steps; dynamic
+  // tiles' epilogues overlap other tiles' steps and cost about two
+  const int boundary = gang_tiles > 0 ? kGangBoundarySteps : 2;
   auto tile_cost = [&](int i) {
     const int h = order[i];
     const int st = (pl.row_start[h + 1] - pl.row_start[h] + C::BK - 1) / C::BK;
-    return (st < C::MIN_STEPS ? C::MIN_STEPS : st) + 2;
+    return (st < C::MIN_STEPS ? C::MIN_STEPS : st) + boundary;
   };
   // all the work, and the scale that keeps the queue loads in 31 bits
   long long total = 0;
@@ -734,6 +741,7 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
 
   f32x16 acc[C::NACC];
   int stage = 0;
+  int arrivals = 0;  // gang: this workgroup's meets so far (every workgroup of the queue meets as often)
   int L_new = 0;  // the grabbed index handed over during the current tile
 
   // One contraction step (as the big kernel's K step, without a bias row):
@@ -810,7 +818,7 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
     kstep(shape_tag, W0G{}, F_{}, F_{}, 4);
     for (int kt = 2; kt + 3 < KT; ++kt) kstep(shape_tag, W1{}, F_{}, F_{}, kt + 3);
     // gang: meet the queue's other workgroups before the next group's loads
-    if (gang && !last_item && w == 0) tg_gang_meet(counter, gang_tiles * L_nxt, lane);
+    if (gang && !last_item && w == 0) tg_gang_meet(counter, gang_tiles * ++arrivals, lane);
     kstep(shape_tag, W1{}, T_{}, F_{}, 0);  // kt = KT-3: the next tile's step 0
     // the grab has returned (this step's wait left only the loads of the
     // step before outstanding); hand it to every wave, which reads it after
