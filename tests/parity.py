@@ -92,3 +92,24 @@ def sample_rows(case, tm_list=(32, 256), per_group=3, extra=64, seed=0):
         rows.update(int(x) for x in rng.integers(a, b, size=per_group))
     rows.update(int(x) for x in rng.integers(0, case.M, size=extra))
     return sorted(rows)
+
+
+# Sums of many output elements against exact sums (the every-element checks
+# of the full-size tests).  A bf16 output is the nearest bf16 of its float32
+# value: within half a unit in the last place, at most 2^-8 of the value and
+# about uniform, so a sum of such errors spreads by at most 2^-8/sqrt(3) of
+# the root of the sum of the values' squares.
+BF16_SUM_SD = 2.0 ** -8 / np.sqrt(3.0)
+
+
+def sum_check(got, want, spread, mag, what):
+    """Assert |got - want| <= 8 spread + 1e-5 mag elementwise (spread: the
+    sums' rounding spread; mag: the sum of the summed values' magnitudes,
+    for the float32 accumulation); returns the largest ratio to that
+    tolerance."""
+    got, want, spread, mag = (np.asarray(x, dtype=np.float64) for x in (got, want, spread, mag))
+    tol = 8.0 * spread + 1e-5 * mag + 1e-30
+    ratio = np.abs(got - want) / tol
+    bad = ratio > 1.0
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} sums off, worst {ratio.max():.2f}x the tolerance"
+    return float(ratio.max())
