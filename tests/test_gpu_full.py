@@ -8,9 +8,9 @@ against the oracle.
   to a few thousand rows), random rows per group and overall.
 - Always: rows outside the active groups are all-zero bits (checked on the
   device over all M rows) and no device data flag is raised.
-- moe_fwd_bf16, moe_dlhs_bf16 and the weight gradient tgmm_bf16: every
-  element, through row and per-group column sums against the oracle on
-  reduced operands (see below).
+- moe_fwd_bf16, moe_dlhs_bf16, w8a8_fp8 and the weight gradient tgmm_bf16:
+  every element, through row and per-group column sums against the oracle
+  on reduced operands (see below).
 
 Tolerances are those of tests/parity.py (float32: max error 1e-4 of the
 largest reference value; bfloat16: relative Frobenius error 2e-2, globally
@@ -160,3 +160,61 @@ def test_full_size_tgmm_every_element_by_sums():
     r2 = sum_check(col_sum, want_col, 1e-4 * amax[:, None] * np.sqrt(K) / 8, col_abs, "tgmm column sums")
     print(f"tgmm sums case: {Ga}x{K} row sums and {Ga}x{N} column sums within {max(r1, r2):.3f} of the tolerance",
           flush=True)
+
+
+def test_full_size_w8a8_every_element_by_sums():
+    """The block-scaled W8A8 product (both scales, bf16 out) at full size,
+    every element through the same sums; the scales go into the reduced
+    operands:
+      sum_n out[r, n] = sum_b ls[r, b] sum_{k in b} x[r, k] (sum_n rs[g, b, n] w_g[n, k])
+      sum_{r in g} out[r, n] = sum_b rs[g, b, n] sum_{k in b} (sum_{r in g} ls[r, b] x[r, k]) w_g[n, k]"""
+    import oracle
+    import moe_grouped_matrix_amd as gmm_amd
+    gmm_amd.set_tile_policy(0)
+    case = workloads.FULL["w8a8_fp8"](device="cuda")
+    assert case.group_offset == 0 and not case.transpose_rhs and case.rhs_bias is None
+    print(f"sums case w8a8_fp8: M={case.M} K={case.K} N={case.N}", flush=True)
+    out = torch.empty((case.M, case.N), dtype=case.out_dtype, device="cuda")
+    gmm_amd.gmm(case.lhs, case.rhs, case.group_sizes, rhs_scale=case.rhs_scale, lhs_scale=case.lhs_scale, out=out)
+    torch.cuda.synchronize()
+    assert gmm_amd.device_flags() == 0
+    sizes = case.sizes_list()
+    o = _segments(sizes)
+    M, K, N, G = case.M, case.K, case.N, len(sizes)
+    row_sum, row_ss, row_abs = [], [], []
+    for i in range(0, M, 32768):
+        x = out[i:i + 32768].double()
+        row_sum.append(x.sum(1).cpu())
+        row_ss.append(x.square().sum(1).sqrt().cpu())
+        row_abs.append(x.abs().sum(1).cpu())
+    row_sum, row_ss, row_abs = (torch.cat(v).numpy() for v in (row_sum, row_ss, row_abs))
+    col = [np.zeros((G, N)) for _ in range(3)]
+    for g in range(G):
+        if sizes[g]:
+            x = out[o[g]:o[g + 1]].double()
+            col[0][g], col[1][g], col[2][g] = (x.sum(0).cpu().numpy(), x.square().sum(0).sqrt().cpu().numpy(),
+                                               x.abs().sum(0).cpu().numpy())
+    lhs, rhs, gs = case.lhs.cpu(), case.rhs.cpu(), case.group_sizes.cpu()
+    ls, rs = case.lhs_scale.cpu(), case.rhs_scale.cpu()      # [M, nb], [G, nb, 1, N]
+    nb = ls.shape[1]
+    blk = K // nb
+    # w_red[g, k] = sum_n rs[g, b(k), n] w_g[n, k] (e4m3 decoded exactly; float64, then float32)
+    w_red = torch.empty(G, 1, K)
+    for g in range(G):
+        rs_k = rs[g, :, 0, :].double().repeat_interleave(blk, dim=0)   # [K, N]: rs[g, b(k), n]
+        w_red[g, 0] = (rhs[g].float().double() * rs_k.t()).sum(0).float()
+    want_row = oracle.gmm_reference(lhs, w_red, gs, lhs_scale=ls)[:, 0]
+    # lhs_red[g, k] = sum_{r in g} ls[r, b(k)] x[r, k]
+    lhs_red = torch.zeros(G, K)
+    for g in range(G):
+        if sizes[g]:
+            xs = lhs[o[g]:o[g + 1]].float().double() * ls[o[g]:o[g + 1]].double().repeat_interleave(blk, dim=1)
+            lhs_red[g] = xs.sum(0).float()
+    want_col = oracle.gmm_reference(lhs_red, rhs, torch.ones(G, dtype=torch.int32), rhs_scale=rs)
+    active = np.zeros(M, dtype=bool)
+    active[o[0]:o[-1]] = True
+    assert np.all(row_sum[~active] == 0)
+    r1 = sum_check(row_sum[active], want_row[active], BF16_SUM_SD * row_ss[active], row_abs[active], "w8a8 row sums")
+    r2 = sum_check(col[0], want_col, BF16_SUM_SD * col[1], col[2], "w8a8 per-group column sums")
+    print(f"sums case w8a8_fp8: {active.sum()} row sums and {G}x{N} column sums within {max(r1, r2):.3f} of the "
+          f"tolerance", flush=True)
