@@ -29,15 +29,16 @@
 //    computes tile j of each of its queue's groups in turn.  All of a
 //    group's tiles then run side by side on one XCD and read each
 //    contraction row of both operands at about the same time, once from
-//    HBM into that XCD's L2.  The tiles that hold fewer accumulators (tall,
-//    wide) finish their steps sooner; so that they do not run ahead into the
-//    next group alone, each workgroup, before it queues the next group's
-//    first loads, counts itself on its queue's counter and waits (bounded)
-//    until the queue's other workgroups have done the same.
+//    HBM into that XCD's L2.  The workgroups drift apart as they go; so
+//    that none runs ahead into the next group alone, each workgroup, before
+//    it queues the next group's first loads, counts itself on its queue's
+//    counter and waits (bounded) until the queue's other workgroups have
+//    done the same.
 //  - Dynamic (otherwise): 256 x 256 tiles handed out through the queues'
-//    atomic counters, largest groups first (the counters are the caller's:
-//    Params::queue, a block of the handle's per stream; the last workgroup
-//    of a queue to finish resets them for the next call).
+//    atomic counters, largest groups first.
+// The counters are the caller's (Params::queue: a block of the handle's per
+// stream, or the library's static scratch); in either schedule the last
+// workgroup of a queue to finish resets them for the next call.
 #pragma once
 
 #include "gmm_big.hpp"
