@@ -134,6 +134,43 @@ def test_tgmm_gang_schedule_bit_exact(K, N, limit, T, W):
         m.set_grid_limit(0)
 
 
+def test_tgmm_gang_schedule_with_group_offset():
+    """The gang schedule over a shard: 20 groups, offset s = 2 (a device
+    scalar), 17 active groups (so still one queue per XCD), K = N = 384 on a
+    grid of 32 (T = 3 tiles of W = 4 workgroups per queue), and then an
+    offset past G - Ga, which is flagged and keeps the G - s groups there
+    are (15: one queue, the dynamic schedule); the output groups it drops
+    are zero."""
+    import moe_grouped_matrix_amd as m
+    g = torch.Generator().manual_seed(77)
+    sizes = GANG_SIZES + [45, 12]
+    K = N = 384
+    M = sum(sizes) + 3
+    lhs = torch.randint(-3, 4, (M, K), generator=g).to(torch.bfloat16)
+    rhs = torch.randint(-3, 4, (M, N), generator=g).to(torch.bfloat16)
+    gs = torch.tensor(sizes, dtype=torch.int32)
+    Ga = 17
+    m.set_grid_limit(32)
+    try:
+        s = torch.tensor([2], dtype=torch.int32, device="cuda")
+        print(f"tgmm gang offset 2, Ga={Ga} of G={len(sizes)}", flush=True)
+        out = m.tgmm(lhs.cuda(), rhs.cuda(), gs.cuda(), num_active=Ga, group_offset=s).cpu()
+        want = oracle.round_to(oracle.tgmm_reference(lhs, rhs, gs, group_offset=2, num_active=Ga), torch.float32)
+        assert torch.equal(out.view(torch.int32), want.view(torch.int32))
+        assert m.device_flags() == 0
+        # offset 5 > G - Ga = 3: flagged; groups 5 .. 19 are output groups 0 .. 14, 15 and 16 are zero
+        s = torch.tensor([5], dtype=torch.int32, device="cuda")
+        print("tgmm gang offset 5 (clamped)", flush=True)
+        out = m.tgmm(lhs.cuda(), rhs.cuda(), gs.cuda(), num_active=Ga, group_offset=s).cpu()
+        assert m.device_flags() != 0
+        kept = len(sizes) - 5
+        want = oracle.round_to(oracle.tgmm_reference(lhs, rhs, gs, group_offset=5, num_active=kept), torch.float32)
+        assert torch.equal(out[:kept].view(torch.int32), want.view(torch.int32))
+        assert torch.all(out[kept:].view(torch.int32) == 0)
+    finally:
+        m.set_grid_limit(0)
+
+
 def test_tgmm_invalid_sizes_are_clamped_and_flagged():
     import moe_grouped_matrix_amd as m
     sizes = [40, -3, 25]
