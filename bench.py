@@ -38,7 +38,7 @@ KERNEL_SOURCES = {
     "tiny_fp32": (),
     "moe_fwd_bf16": ("gmm_big.hpp",),
     "moe_dlhs_bf16": ("gmm_big.hpp",),
-    "decode_fp8w": ("gmm_big.hpp", "gmm_stream.hpp"),
+    "decode_fp8w": ("gmm_big.hpp", "gmm_stream.hpp", "gmm_stream.hip"),
     "w8a8_fp8": ("gmm_big.hpp", "gmm_w8a8.hpp", "gmm_w8a8.hip"),
     "tgmm_bf16": ("gmm_big.hpp", "gmm_tgmm.hpp", "gmm_tgmm_tiles.hpp"),
     "quant_fp8": ("gmm_quant.hip",),

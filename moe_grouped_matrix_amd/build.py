@@ -12,17 +12,19 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgmm.so")
-SOURCES = [os.path.join(CSRC, "gmm_kernels.hip"), os.path.join(CSRC, "gmm_w8a8.hip"),
-           os.path.join(CSRC, "gmm_quant.hip"), os.path.join(CSRC, "gmm_api.cpp")]
+SOURCES = [os.path.join(CSRC, n) for n in
+           ("gmm_kernels.hip", "gmm_w8a8.hip", "gmm_stream.hip", "gmm_quant.hip", "gmm_api.cpp")]
 
 # Packed fp32 VALU instructions are kept out of the generated code.
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-Wno-unused-command-line-argument"]
 
-# Per-source additions: the block-scaled fp8 kernel keeps its MFMA results
-# in ordinary VGPRs, where its fold reads them.
-EXTRA_FLAGS = {"gmm_w8a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source additions: the block-scaled fp8 kernel and the weight-streaming
+# kernel keep their MFMA results in ordinary VGPRs, where their scale folds
+# read them.
+EXTRA_FLAGS = {"gmm_w8a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "gmm_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

@@ -4,7 +4,6 @@
 
 #include "gmm_big.hpp"
 #include "gmm_device.hpp"
-#include "gmm_stream.hpp"
 #include "gmm_tgmm.hpp"
 #include "gmm_launch.hpp"
 
@@ -91,28 +90,6 @@ hipError_t launch_big(const Params& p, int cu_count, int cap, hipStream_t stream
   return hipGetLastError();
 }
 
-template <class C>
-hipError_t launch_stream(const Params& p, int cu_count, int cap, hipStream_t stream) {
-  // One workgroup per CU (LDS-bound), even when there are fewer tiles:
-  // workgroups without a tile still take their share of the rows outside
-  // the active groups, which can be most of the output (an expert shard of
-  // a decode batch).
-  long long grid = cu_count;
-  if (grid >= 8) grid -= grid % 8;
-  if (grid < 1) grid = 1;
-  grid = apply_cap(grid, cap);
-  hipLaunchKernelGGL(gmm_stream_kernel<C>, dim3((unsigned)grid), dim3(C::T), 0, stream, p);
-  return hipGetLastError();
-}
-
-// The weight-streaming kernel takes bf16 x e4m3 NT problems with few rows per
-// group: K in stages of 128 with at least S of them per tile, and scale
-// blocks of exactly one stage (or no scale).
-inline bool stream_fits(const Params& p) {
-  return p.K % 128 == 0 && p.K >= StreamCfg<false>::S * 128 && p.lhs_scale == nullptr &&
-         (p.rhs_scale == nullptr || p.blk == 128);
-}
-
 // One workgroup per CU (LDS-bound), at most one per tile.
 template <class C>
 hipError_t launch_tgmm_cfg(const Params& p, int cu_count, int cap, hipStream_t stream) {
@@ -142,10 +119,7 @@ hipError_t by_size(const Params& p, const KernelChoice& kc, int cu, hipStream_t 
     }
   }
   if constexpr (OP == Op::BF16 && BF8 && !NN && (FMT >> 3) < 3) {  // one-byte weights
-    if (sz == SizeClass::Small && stream_fits(p)) {
-      if (p.out_f32) return launch_stream<StreamCfg<true, (FMT >> 3)>>(p, cu, cap, st);
-      return launch_stream<StreamCfg<false, (FMT >> 3)>>(p, cu, cap, st);
-    }
+    if (sz == SizeClass::Small && stream_fits(p)) return launch_stream(p, FMT >> 3, cu, cap, st);
   }
   // W8A8 (one-byte fp8 operands) with scale blocks of one K step
   if constexpr (OP == Op::FP8 && !NN && SC && (FMT & 7) <= 1 && (FMT >> 3) <= 1) {

@@ -12,19 +12,22 @@
 // of 256 bytes), the block's 256 scales and the tile's 256 bias values.
 // Three stages form a ring filled by direct-to-LDS loads two stages ahead,
 // across the workgroup's tiles, so the HBM stream never drains.  Four
-// waves, one per SIMD: wave w computes columns 128 (w % 2) .. +128 for rows
-// 32 (w / 2) .. +32 over the whole of K with 32x32x16 bf16 MFMAs, so no
-// partial sums cross waves.  The weight fragment is the MFMA's first
-// operand (a lane holds runs of four columns of one row), widened from its
-// one-byte format to bf16 in registers, and each block's product is folded
-// into fp32 totals with that block's scales.
+// waves, one per SIMD: wave w computes columns 64 w .. +64 for all 64 rows
+// (two 32-row blocks) over the whole of K with 32x32x16 bf16 MFMAs, so no
+// partial sums cross waves and each weight byte is widened by one wave
+// only.  The weight fragment is the MFMA's first operand (a lane holds runs
+// of four columns of one row), widened from its one-byte format to bf16 in
+// registers and used for both row blocks, and each block's product is
+// folded into fp32 totals with that block's scales.
 //
 // What sets the shape: the lhs rows share the LDS ring with the weights,
-// and a stage's time is set by the bytes and loads it moves, not by its
-// multiplies (measured: 64-row tiles 32, 64, 128 and 256 columns wide run
-// a 128-K stage in 0.49, 0.67, 1.05 and 2.1 us, the widest moving the most
-// weight per lhs byte: 33.4 us per decode call against 38.9 us for the
-// 32 x 64 tiles, which also read each expert's weight once per 32 rows).
+// and the widest tile moves the most weight per lhs byte (64-row tiles 32,
+// 64, 128 and 256 columns wide ran a 128-K stage in 0.49, 0.67, 1.05 and
+// 2.1 us; 32 x 64 tiles, which also read each expert's weight once per 32
+// rows, took 38.9 us per decode call against 33.4 us).  A stage's vector
+// work (widening the weight, the scale fold) is a large part of it:
+// widening each weight byte in one wave instead of two took the call from
+// 33.3 to 32.3 us.
 //
 // Every wave issues the same loads in every stage (eight weight and four
 // lhs; wave 0 also the scales, wave 1 the bias; loads past a range return
@@ -56,9 +59,9 @@ struct StreamCfg {
   static constexpr int W_OPS = W_BYTES / 1024 / NWAVES, A_OPS = A_BYTES / 1024 / NWAVES;
   // loads per stage: waves 0 and 1 one more (the scales, the bias)
   static constexpr int OPS_LO = W_OPS + A_OPS, OPS_HI = OPS_LO + 1;
-  static constexpr int FN = 4;  // 32-column blocks per wave
+  static constexpr int FM = 2, FN = 2;  // 32-row and 32-column blocks per wave
   static constexpr int es_out = OUT_F32 ? 4 : 2;
-  static constexpr int E = FN * (OUT_F32 ? 4 : 2);  // 16-byte stores per wave and tile
+  static constexpr int E = FM * FN * (OUT_F32 ? 4 : 2);  // 16-byte stores per wave and tile
   static_assert(W_OPS == 8 && A_OPS == 4, "load split");
 };
 
@@ -195,7 +198,6 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wc = w & 1, wr = w >> 1;  // column half, row half of the tile
   const int kh = lane >> 5, r32 = lane & 31;
   const int M = p.M, N = p.N, K = p.K;
   const int P = gridDim.x;
@@ -243,20 +245,20 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
     int w_off[C::FN][4];
 #pragma unroll
     for (int fb = 0; fb < C::FN; ++fb) {
-      const int wn = 128 * wc + 32 * fb + r32;  // weight row = tile column
+      const int wn = 64 * w + 32 * fb + r32;  // weight row = tile column
 #pragma unroll
       for (int c = 0; c < 4; ++c) w_off[fb][c] = wn * C::W_ROW + (((4 * kh + c) ^ swz_w(wn)) << 4);
     }
-    const int ar = 32 * wr + r32;  // lhs row of the tile
-    const int a_base = C::W_BYTES + ar * C::A_ROW;
-    const int a_swz = swz_a(ar);
-    // this lane's columns of block fb: 128 wc + 32 fb + 8 g + 4 kh + [0, 4), g = 0..3
-    const int col_l = 128 * wc + 4 * kh;
+    // lhs rows 32 fm + r32 (fm = 0, 1), the same swizzle
+    const int a_base = C::W_BYTES + r32 * C::A_ROW;
+    const int a_swz = swz_a(r32);
+    // this lane's columns of block fb: 64 w + 32 fb + 8 g + 4 kh + [0, 4), g = 0..3
+    const int col_l = 64 * w + 4 * kh;
 
     // a stage's fragments: the weight runs (64 one-byte values per column
-    // block), the lhs row (eight 16-byte chunks), the block's scales of the
-    // lane's columns
-    i32x4 fw[C::FN][4], fa[8];
+    // block), the lhs rows (eight 16-byte chunks per row block), the
+    // block's scales of the lane's columns
+    i32x4 fw[C::FN][4], fa[C::FM][8];
     f32x4 fsc[C::FN][4];
     auto read_frags = [&](const char* st) __attribute__((always_inline)) {
 #pragma unroll
@@ -264,8 +266,11 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) fw[fb][c] = *reinterpret_cast<const i32x4*>(st + w_off[fb][c]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        fa[j] = *reinterpret_cast<const i32x4*>(st + a_base + (((8 * kh + j) ^ a_swz) << 4));
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          fa[fm][j] =
+              *reinterpret_cast<const i32x4*>(st + a_base + fm * 32 * C::A_ROW + (((8 * kh + j) ^ a_swz) << 4));
 #pragma unroll
       for (int fb = 0; fb < C::FN; ++fb)
 #pragma unroll
@@ -276,11 +281,11 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
 
     int stage = 0;
     read_frags(smem);  // stage 0 of the first tile
-    f32x16 tot[C::FN];
+    f32x16 tot[C::FM * C::FN];  // block (fm, fb) at fm * FN + fb
 #pragma unroll
-    for (int fb = 0; fb < C::FN; ++fb)
+    for (int b = 0; b < C::FM * C::FN; ++b)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) tot[fb][i] = 0.f;
+      for (int i = 0; i < 16; ++i) tot[b][i] = 0.f;
 
     // One stage kt of the current tile.  Stage kt+1's loads are complete
     // (this wave's, then every wave's after the barrier) once at most the
@@ -302,24 +307,33 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
       const char* st = smem + stage * C::STAGE;
 #pragma unroll
       for (int fb = 0; fb < C::FN; ++fb) {
-        f32x16 acc;
+        f32x16 acc[C::FM];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+        for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[fm][i] = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          // weight bytes 16 c .. 16 c + 15 of the run: K steps 2 c, 2 c + 1
+          // weight bytes 16 c .. 16 c + 15 of the run: K steps 2 c, 2 c + 1,
+          // widened once for both row blocks
           const i32x4 bw0 = fp8x8_to_bf16x8<C::FB>(i32x2{fw[fb][c][0], fw[fb][c][1]});
           const i32x4 bw1 = fp8x8_to_bf16x8<C::FB>(i32x2{fw[fb][c][2], fw[fb][c][3]});
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bw0),
-                                                        __builtin_bit_cast(bf16x8, fa[2 * c]), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bw1),
-                                                        __builtin_bit_cast(bf16x8, fa[2 * c + 1]), acc, 0, 0, 0);
+#pragma unroll
+          for (int fm = 0; fm < C::FM; ++fm) {
+            acc[fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, bw0), __builtin_bit_cast(bf16x8, fa[fm][2 * c]), acc[fm], 0, 0, 0);
+            acc[fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, bw1), __builtin_bit_cast(bf16x8, fa[fm][2 * c + 1]), acc[fm], 0, 0, 0);
+          }
         }
         // register 4 g + i holds column 8 g + 4 kh + i of the block for the lane's row
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) tot[fb][4 * g + i] += acc[4 * g + i] * fsc[fb][g][i];
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              tot[fm * C::FN + fb][4 * g + i] += acc[fm][4 * g + i] * fsc[fb][g][i];
       }
       if (kt == KT - 1) {
         // epilogue: bias from this stage's slot (its next use is past the
@@ -329,37 +343,37 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
         // rows and columns drop
         char* tile = reinterpret_cast<char*>(p.out) + ((long long)cur.row0 * N + cur.n0) * C::es_out;
         const __amdgpu_buffer_rsrc_t ro = uniform_rsrc(tile, ((cur.rows - 1) * N + cur.ncols) * C::es_out);
-        const int row = 32 * wr + r32;
 #pragma unroll
-        for (int fb = 0; fb < C::FN; ++fb) {
+        for (int b = 0; b < C::FM * C::FN; ++b) {
+          const int row = 32 * (b / C::FN) + r32, fb = b % C::FN;
           float v[16];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            float b[4] = {0.f, 0.f, 0.f, 0.f};
+            float bi[4] = {0.f, 0.f, 0.f, 0.f};
             const int cb = col_l + 32 * fb + 8 * g;  // first of the lane's four columns
             if (p.rhs_bias) {
               if (bias_f32) {
                 const f32x4 b4 = *reinterpret_cast<const f32x4*>(st + C::BI_OFF + cb * 4);
-                b[0] = b4[0];
-                b[1] = b4[1];
-                b[2] = b4[2];
-                b[3] = b4[3];
+                bi[0] = b4[0];
+                bi[1] = b4[1];
+                bi[2] = b4[2];
+                bi[3] = b4[3];
               } else {
                 const i32x2 b2 = *reinterpret_cast<const i32x2*>(st + C::BI_OFF + cb * 2);
-                b[0] = __uint_as_float((uint32_t)b2[0] << 16);
-                b[1] = __uint_as_float((uint32_t)b2[0] & 0xFFFF0000u);
-                b[2] = __uint_as_float((uint32_t)b2[1] << 16);
-                b[3] = __uint_as_float((uint32_t)b2[1] & 0xFFFF0000u);
+                bi[0] = __uint_as_float((uint32_t)b2[0] << 16);
+                bi[1] = __uint_as_float((uint32_t)b2[0] & 0xFFFF0000u);
+                bi[2] = __uint_as_float((uint32_t)b2[1] << 16);
+                bi[3] = __uint_as_float((uint32_t)b2[1] & 0xFFFF0000u);
               }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[4 * g + i] = tot[fb][4 * g + i] + b[i];
+            for (int i = 0; i < 4; ++i) v[4 * g + i] = tot[b][4 * g + i] + bi[i];
           }
 #pragma unroll
           for (int gp = 0; gp < 4; gp += 2) {
             // after the swap: kh = 0 holds columns 8 gp + [0, 8) of the
             // block, kh = 1 holds 8 (gp + 1) + [0, 8)
-            const int col = 128 * wc + 32 * fb + 8 * (gp + kh);
+            const int col = 64 * w + 32 * fb + 8 * (gp + kh);
             const int voff = col < cur.ncols ? (row * N + col) * C::es_out : (int)0x80000000;
             if constexpr (C::OUT_F32) {
               int lo[4], hi[4];
@@ -384,7 +398,7 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
             }
           }
 #pragma unroll
-          for (int i = 0; i < 16; ++i) tot[fb][i] = 0.f;
+          for (int i = 0; i < 16; ++i) tot[b][i] = 0.f;
         }
       }
       const int stage1 = stage + 1 == C::S ? 0 : stage + 1;

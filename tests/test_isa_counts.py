@@ -9,8 +9,9 @@ waits after a half tile would be short by that many operations and the next
 stages could read LDS before their loads land.  This test compiles the
 kernels to assembly and checks that each big-kernel instantiation still has
 both epilogues' stores: E for a full tile and E (real plus padding) for a half
-tile; likewise the tgmm kernel's four tile shapes and the W8A8 kernel's loads
-and stores, and that the loop kernels do not spill."""
+tile; likewise the tgmm kernel's four tile shapes, the W8A8 and
+weight-streaming kernels' loads and stores, and that the loop kernels do not
+spill."""
 import os
 import re
 import shutil
@@ -51,6 +52,11 @@ def w8a8_asm(tmp_path_factory):
     return _compile(tmp_path_factory, "gmm_w8a8.hip")
 
 
+@pytest.fixture(scope="module")
+def stream_asm(tmp_path_factory):
+    return _compile(tmp_path_factory, "gmm_stream.hip")
+
+
 def _functions(asm, pattern):
     for name in re.findall(r"^(" + pattern + r"\S*):", asm, re.M):
         start = asm.index(name + ":")
@@ -81,11 +87,29 @@ def test_tgmm_kernel_keeps_every_counted_store(kernel_asm):
     assert seen == 2  # bf16 / f32 output
 
 
-def test_loop_kernels_do_not_spill(kernel_asm, w8a8_asm):
+def test_stream_kernel_keeps_every_counted_operation(stream_asm):
+    """The weight-streaming kernel's waits count 14 direct-to-LDS loads per
+    stage in the code (8 weight and 4 lhs per wave, the scale load of wave 0
+    and the bias load of wave 1: two stages in the prologue and one in each
+    of the K loop's four variants) and E = 8 (bf16 output) or 16 (f32)
+    stores per tile: the prologue's E range-dropped stores and the epilogue
+    of each of the three loop variants that can end a tile."""
+    seen = 0
+    for name, lines in _functions(stream_asm, r"_ZN4gmmk17gmm_stream_kernel"):
+        out_f32 = re.search(r"StreamCfgILb([01])E", name).group(1) == "1"
+        loads = sum(1 for ln in lines if ln.startswith("buffer_load") and ln.endswith(" lds"))
+        stores = sum(1 for ln in lines if ln.startswith("buffer_store"))
+        assert loads == 6 * 14, (name, loads)
+        assert stores == 4 * (16 if out_f32 else 8), (name, stores)
+        seen += 1
+    assert seen == 6  # e4m3fn / e5m2 / int8 weights x bf16 / f32 output
+
+
+def test_loop_kernels_do_not_spill(kernel_asm, w8a8_asm, stream_asm):
     # a spill reload is a vector memory load: its wait would drain every
     # direct-to-LDS load queued behind the K loop's constant counts
     seen = 0
-    for asm, pattern in ((kernel_asm, r"_ZN4gmmk15gmm_tgmm_kernel"), (kernel_asm, r"_ZN4gmmk17gmm_stream_kernel"),
+    for asm, pattern in ((kernel_asm, r"_ZN4gmmk15gmm_tgmm_kernel"), (stream_asm, r"_ZN4gmmk17gmm_stream_kernel"),
                          (w8a8_asm, r"_ZN4gmmk15gmm_w8a8_kernel")):
         for name, lines in _functions(asm, pattern):
             assert not any(ln.startswith("scratch_") for ln in lines), name
