@@ -83,11 +83,16 @@ typedef struct gmm_handle gmm_handle;
 #define GMM_FLAG_NEGATIVE_SIZE 0x1u  /* some group_sizes[g] < 0 (taken as 0) */
 #define GMM_FLAG_SIZES_EXCEED_M 0x2u /* o[G] > M (offsets clamped to M) */
 #define GMM_FLAG_BAD_OFFSET 0x4u     /* group offset < 0 or s + Ga > G (clamped) */
+/* Not a data error: a gmm_tgmm_run workgroup waited past its bound (about a
+ * second) for its XCD's next group, which only happens when the call's
+ * workgroups cannot all run at once (the GPU shared with other work); the
+ * groups it did not learn of were not computed.  Run the call again. */
+#define GMM_FLAG_SCHEDULE_TIMEOUT 0x8u
 
 /*
  * gmm_create: make a handle on HIP device `device` (must be gfx950).
  * Allocates a 16-byte device block for the data-error flags.  The first
- * gmm_tgmm_run on each stream allocates that stream's 64-byte block of
+ * gmm_tgmm_run on each stream allocates that stream's 144-byte block of
  * work-queue counters (kept until gmm_destroy); no other call allocates.
  * Returns GMM_E_UNSUPPORTED on another architecture, GMM_E_HIP on a HIP
  * failure, GMM_E_INVALID when h is NULL.
@@ -276,7 +281,11 @@ gmm_status gmm_widen_scales_run(gmm_handle* h, const gmm_tensor* src, const gmm_
  * that the call's last workgroup resets.  The handle keeps one counter block
  * per stream (allocated on the first call on that stream), so calls on one
  * stream run one after another on their own counters and calls on different
- * streams may overlap.
+ * streams may overlap.  When each group's tiles fit one XCD's workgroups
+ * (the gang schedule), an XCD's workgroups take the groups together, one
+ * after another, and the next group comes from a grid-wide counter at each
+ * group boundary: that needs every workgroup of the call resident at once,
+ * and a call that waits too long for it sets GMM_FLAG_SCHEDULE_TIMEOUT.
  */
 gmm_status gmm_tgmm_run(gmm_handle* h,
                         const gmm_tensor* lhs,
@@ -296,7 +305,7 @@ gmm_status gmm_tgmm_run(gmm_handle* h,
  * which looks the scratch up once per device, is the only allocating call).
  *
  *   Arguments, limits and errors are those of gmm_tgmm_run.  The scratch is
- *   256 bytes per device, held until the process ends; the counters use 64
+ *   256 bytes per device, held until the process ends; the counters use 144
  *   of them for every problem size, so no size is rejected for want of
  *   scratch.  Each call first clears the counters on `stream` (a one-
  *   workgroup kernel) and then queues the tgmm kernel.

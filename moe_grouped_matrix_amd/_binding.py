@@ -22,6 +22,7 @@ GMM_I4, GMM_U4, GMM_F4E2M1 = 7, 8, 9
 PACKED_FORMATS = {"int4": GMM_I4, "uint4": GMM_U4, "fp4_e2m1": GMM_F4E2M1}
 GMM_OK, GMM_E_INVALID, GMM_E_UNSUPPORTED, GMM_E_HIP, GMM_E_DEVICE_DATA = 0, -1, -2, -3, -4
 FLAG_NEGATIVE_SIZE, FLAG_SIZES_EXCEED_M, FLAG_BAD_OFFSET = 0x1, 0x2, 0x4
+FLAG_SCHEDULE_TIMEOUT = 0x8  # not a data error: a tgmm call's workgroups could not all run at once
 
 EXPORTED = ("gmm_create", "gmm_destroy", "gmm_last_error", "gmm_run", "gmm_run_existing_out", "gmm_tgmm_run",
             "gmm_tgmm_run_noalloc",

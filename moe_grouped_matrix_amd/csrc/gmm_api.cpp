@@ -17,13 +17,16 @@
 #include "gmm_launch.hpp"
 
 constexpr size_t kDeviceBlock = 16;  // the data-error flag word
-constexpr size_t kQueueBlock = 2 * gmmk::kQueues * sizeof(int32_t);
+static_assert(gmmk::kFlagNegative == GMM_FLAG_NEGATIVE_SIZE && gmmk::kFlagExceed == GMM_FLAG_SIZES_EXCEED_M &&
+                  gmmk::kFlagBadOffset == GMM_FLAG_BAD_OFFSET && gmmk::kFlagSchedule == GMM_FLAG_SCHEDULE_TIMEOUT,
+              "the kernels' flag bits are the header's");
+constexpr size_t kQueueBlock = gmmk::kQueueWords * sizeof(int32_t);
 
 struct gmm_handle {
   int device = 0;
   int cu_count = 0;
   uint32_t* flags = nullptr;  // device word of data-error flags (kDeviceBlock bytes)
-  // the transposed product's work-queue counters (2 * kQueues int32, zero
+  // the transposed product's work-queue counters (kQueueWords int32, zero
   // between calls), one block per stream: calls on one stream run in order,
   // so each call finds its stream's counters reset by the previous one;
   // calls on different streams never share counters

@@ -89,7 +89,7 @@ hipError_t launch_widen_scales(const WidenParams& p, int cu_count, hipStream_t s
 // a file-scope array in gmm_kernels.hip, one copy per device, holding the
 // transposed product's work-queue counters.
 constexpr int kStaticScratchBytes = 256;
-static_assert(2 * kQueues * 4 <= kStaticScratchBytes, "work-queue counters fit the scratch");
+static_assert(kQueueWords * 4 <= kStaticScratchBytes && kQueueWords <= 64, "work-queue counters fit the scratch");
 
 // The device address of the current device's scratch (hipGetSymbolAddress).
 hipError_t static_scratch_address(void** ptr);

@@ -11,9 +11,18 @@ enum class Op { F32, BF16, FP8, I8 };
 
 constexpr int kMaxGroups = 1024;
 constexpr int kQueues = 8;  // one per XCD
+// The transposed product's counter block (int32 words, all zero between
+// calls): [0, kQueues) the dynamic schedule's tile counters, [kQueues,
+// 2 kQueues) finished workgroups per queue, kGangNext the gang schedule's
+// next group, kGangDone finished workgroups of the grid, and from
+// kGangMeet one 64-bit meet word per queue (8-byte aligned).
+constexpr int kGangNext = 2 * kQueues, kGangDone = kGangNext + 1;
+constexpr int kGangMeet = kGangNext + 4;
+constexpr int kQueueWords = kGangMeet + 2 * kQueues;
 constexpr uint32_t kFlagNegative = 0x1u;
 constexpr uint32_t kFlagExceed = 0x2u;
 constexpr uint32_t kFlagBadOffset = 0x4u;
+constexpr uint32_t kFlagSchedule = 0x8u;
 // What the rows outside the active groups receive.
 enum Fill : int32_t { kFillZero = 0, kFillCopy = 1, kFillKeep = 2 };
 // Bytes of inactive rows filled by one work item.
@@ -35,8 +44,8 @@ struct Params {
   const void* existing;         // [M, N] like out, or nullptr
   int32_t fill;
   uint32_t* flags;
-  // work queues of the transposed product: kQueues tile counters followed by
-  // kQueues finished-workgroup counters, all zero between calls
+  // the transposed product's counter block (kQueueWords int32, zero between
+  // calls)
   int32_t* queue;
   int32_t M, K, N, G, Ga, nb, blk;
   int32_t bias_f32, out_f32;

@@ -25,15 +25,19 @@
 // groups:
 //  - Gang: when a group's output splits into T <= W tiles of the shapes in
 //    gmm_tgmm_tiles.hpp, T >= 3/4 of the W workgroups of a queue: the
-//    groups are dealt to the queues by rows, and workgroup j of a queue
+//    queues take the groups (largest first) one at a time, each next group
+//    going to the queue that needs one first, and workgroup j of a queue
 //    computes tile j of each of its queue's groups in turn.  All of a
 //    group's tiles then run side by side on one XCD and read each
 //    contraction row of both operands at about the same time, once from
 //    HBM into that XCD's L2.  The workgroups drift apart as they go; so
 //    that none runs ahead into the next group alone, each workgroup, before
-//    it queues the next group's first loads, counts itself on its queue's
-//    counter and waits (bounded) until the queue's other workgroups have
-//    done the same.
+//    it queues the next group's first loads, meets the queue's other
+//    workgroups (tg_gang_meet), where the queue's leader also hands out the
+//    group after it.  Taking groups as they are needed lets an XCD that
+//    runs faster take more of them (measured: the XCDs of one GPU ran the
+//    same number of steps and group boundaries up to 4% apart, the same
+//    XCDs from run to run).
 //  - Dynamic (otherwise): 256 x 256 tiles handed out through the queues'
 //    atomic counters, largest groups first.
 // The counters are the caller's (Params::queue: a block of the handle's per
@@ -79,26 +83,66 @@ struct TgShapeCfg {
   static_assert(FM * FN <= 8 && BS + FN <= 6, "shape fits the accumulators and slots");
 };
 
-// Gang schedule: the queue's workgroups meet before each group's first
-// loads.  Every workgroup of the queue meets equally often, so at its n-th
-// meet lane 0 of wave 0 adds one to the queue's counter and waits until it
-// reaches n T (T workgroups), for at most kGangSpin polls of a few hundred
-// cycles each; the wait only keeps the workgroups in step (shared L2 reads),
-// the results never depend on it.  The atomic's return and the polls are
-// waited for by the compiler (vmcnt 0), which only makes the loop's later
-// constant waits hold sooner.
+// Gang schedule meets.  The T workgroups of a queue take the queue's groups
+// together; meet m (m = 0, 1, ... in every one of them) comes before the
+// loads of their (m+1)-th group.  The queue's leader (workgroup 0) brings to
+// meet m the list index of the queue's (m+2)-th group, which it takes from
+// the grid's counter (the first two groups of queue x are list items x and
+// 2 kQueues - 1 - x, so the counter starts at item 2 kQueues): an XCD that
+// runs faster takes more groups.  One 64-bit word per queue carries both:
+// the arrivals in bits 0..23 and, in the 20-bit field 24 + 20 (m % 2), the
+// sum of the indices published at meets m, m - 2, ...  At meet m lane 0 of
+// wave 0 adds 1 (the leader also its index into the field), then polls
+// until all T (m + 1) arrivals are in -- at most kGangSpin polls: that wait
+// only keeps the workgroups in step (shared L2 reads) -- and until the field
+// has moved past the value this workgroup saw at meet m - 2; the difference
+// is the index.  Meet m + 2's leader cannot add to the field before this
+// workgroup has arrived at meet m + 1, so the difference is exactly meet
+// m's index.  The results depend on that index, so its wait is bounded only
+// by kGangLeaderSpin polls (about a second: it ends early only when the
+// grid's workgroups cannot all run at once); past it the workgroup sets
+// kFlagSchedule and takes no further group.  The atomics' returns and the
+// polls are waited for by the compiler (vmcnt 0), which only makes the
+// loop's later constant waits hold sooner.
 constexpr int kGangSpin = 2048;
-// a group boundary's cost in steps, for the deal (measured)
-constexpr int kGangBoundarySteps = 9;
+constexpr int kGangLeaderSpin = 1 << 20;
+constexpr int kGangNone = 0x7fffffff;  // no further group
 
-__device__ __forceinline__ void tg_gang_meet(int* counter, int target, int lane) {
+__device__ __forceinline__ int tg_gang_meet(unsigned long long* word, int* next, uint32_t* flags, int m, int T,
+                                            bool leader, int& seen0, int& seen1, int lane) {
+  int idx = kGangNone, seen = (m & 1) ? seen1 : seen0;
   if (lane == 0) {
-    int v = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
-    for (int spin = 0; v < target && spin < kGangSpin; ++spin) {
+    const int sh = 24 + 20 * (m & 1);
+    unsigned long long add = 1;
+    if (leader) {
+      const int mine = 2 * kQueues + __hip_atomic_fetch_add(next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      add += (unsigned long long)mine << sh;
+    }
+    unsigned long long v = __hip_atomic_fetch_add(word, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+    const unsigned long long target = (unsigned long long)T * (unsigned long long)(m + 1);
+    for (int spin = 0; (v & 0xFFFFFFull) < target && spin < kGangSpin; ++spin) {
       __builtin_amdgcn_s_sleep(4);
-      v = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    int f = (int)((v >> sh) & 0xFFFFFull);
+    for (int spin = 0; f == seen && spin < kGangLeaderSpin; ++spin) {
+      __builtin_amdgcn_s_sleep(4);
+      v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      f = (int)((v >> sh) & 0xFFFFFull);
+    }
+    if (f == seen) {
+      atomicOr(flags, kFlagSchedule);
+    } else {
+      idx = f - seen;
+      seen = f;
     }
   }
+  seen = __builtin_amdgcn_readlane(seen, 0);
+  if (m & 1)
+    seen1 = seen;
+  else
+    seen0 = seen;
+  return __builtin_amdgcn_readlane(idx, 0);
 }
 
 // A tile as the loop and the epilogue see it.  The kernel keeps two (the
@@ -132,7 +176,8 @@ __device__ __forceinline__ int tg_slot_off(const TgItem& it) {
 // [0, ka) or [ka, nkt), n-tiles [0, na) or [na, nnt)), so that its tiles can
 // spread over several queues.  A unit is an int: the active group in bits
 // 0..9, the quadrant in bits 10 (upper k half) and 11 (upper n half), bit 12
-// set for a quadrant.  The gang schedule's units are whole groups.
+// set for a quadrant.  The gang schedule's list holds whole groups, largest
+// first.
 constexpr int kMaxSplit = 128;                          // groups split at most
 constexpr int kMaxUnits = kMaxGroups + 3 * kMaxSplit;  // units at most
 
@@ -247,13 +292,13 @@ __device__ __forceinline__ TgItem decode_tg(const Params& p, const Plan& pl, con
   return it;
 }
 
-// Gang schedule: item L of workgroup j of a queue is tile j (t) of the
-// queue's L-th group.
+// Gang schedule: list item L (a group) of workgroup j of a queue is tile j
+// (t) of that group.
 template <class C>
-__device__ __forceinline__ TgItem decode_gang(const Params& p, const Plan& pl, const int* units, int ubase, int L,
+__device__ __forceinline__ TgItem decode_gang(const Params& p, const Plan& pl, const int* units, int L,
                                               const TgTile& t, int w) {
   TgItem it;
-  it.h = __builtin_amdgcn_readfirstlane(units[ubase + L]) & 1023;
+  it.h = __builtin_amdgcn_readfirstlane(units[L]) & 1023;
   it.shape = t.shape;
   it.k0 = t.k0;
   it.n0 = t.n0;
@@ -381,11 +426,10 @@ struct TgLds {
 // each queue, and the hand-over slot of a grabbed tile index
 constexpr int kSchedOff = 0, kSchedTiles = 12, kSchedSlot = 24;
 
-// Deal the units to nq queues, each to the queue with the least work so far
-// (the lowest index on ties), in the group order (largest first), so each
-// queue's units are in that order too.  A tile's work is its contraction
-// steps plus two for the epilogue.  gang_tiles > 0 (the gang schedule): the
-// units are whole groups of gang_tiles tiles each.  Otherwise a group's tiles
+// Deal the units of the dynamic schedule to nq queues, each to the queue
+// with the least work so far (the lowest index on ties), in the group order
+// (largest first), so each queue's units are in that order too.  A tile's
+// work is its contraction steps plus two for the epilogue.  A group's tiles
 // are its nkt x nnt grid, and a group is split into quadrants when its tiles
 // take more than a quarter of a workgroup's share of all the work (at most
 // kMaxSplit groups, the largest).  Wave 0 runs it: the greedy choice is made
@@ -393,17 +437,15 @@ constexpr int kSchedOff = 0, kSchedTiles = 12, kSchedSlot = 24;
 // in the queue and first tile; the lists are then written in parallel.
 template <class C>
 __device__ inline void tg_deal(const Plan& pl, const int* order, char* smem, int* units, int* ustart, int* sched,
-                               int nq, int P, const TgGrid& gr, int gang_tiles, int lane) {
+                               int nq, int P, const TgGrid& gr, int lane) {
   using Lds = TgLds<C>;
   int* const rec_unit = reinterpret_cast<int*>(smem + Lds::REC_UNIT);
   int* const rec_pos = reinterpret_cast<int*>(smem + Lds::REC_POS);
   int* const rec_start = reinterpret_cast<int*>(smem + Lds::REC_START);
   const int ga = pl.ga;
-  const int per = gang_tiles > 0 ? gang_tiles : gr.nnt * gr.nkt;
-  // a group boundary of the gang schedule (the epilogue of all of an XCD's
-  // tiles at once, the meet, the refill) costs about nine steps; dynamic
-  // tiles' epilogues overlap other tiles' steps and cost about two
-  const int boundary = gang_tiles > 0 ? kGangBoundarySteps : 2;
+  const int per = gr.nnt * gr.nkt;
+  // a tile's epilogue overlaps other tiles' steps and costs about two
+  const int boundary = 2;
   auto tile_cost = [&](int i) {
     const int h = order[i];
     const int st = (pl.row_start[h + 1] - pl.row_start[h] + C::BK - 1) / C::BK;
@@ -435,12 +477,12 @@ __device__ inline void tg_deal(const Plan& pl, const int* order, char* smem, int
       const int cj = __builtin_amdgcn_readlane(cost, jj);
       const int hj = __builtin_amdgcn_readlane(h, jj);
       // a tile longer than a quarter of a workgroup's share: cost > total / (4 P)
-      const bool split = gang_tiles == 0 && per > 1 && nsplit < kMaxSplit && 4ll * P * cj > total;
+      const bool split = per > 1 && nsplit < kMaxSplit && 4ll * P * cj > total;
       nsplit += split;
       for (int qd = 0; qd < (split ? 4 : 1); ++qd) {
         const int nk = !split ? gr.nkt : (qd & 1) ? gr.nkt - gr.ka : gr.ka;
         const int nn = !split ? gr.nnt : (qd & 2) ? gr.nnt - gr.na : gr.na;
-        const int nt = gang_tiles > 0 ? gang_tiles : nk * nn;
+        const int nt = nk * nn;
         if (nt == 0) continue;
         int q = 0, best = load[0];
 #pragma unroll
@@ -636,16 +678,21 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
   // the gang schedule's tile of this workgroup, the same in every group
   const TgTile tj = tg_gang_tile(gg, K, N, j < gg.T ? j : 0);
   const int gang_tiles = gg.T;
-  if (w == 0) tg_deal<C>(pl, order, smem, units, ustart, sched, nq, P, gr, gang ? gang_tiles : 0, lane);
+  if (w == 0) {
+    if (gang) {
+      for (int i = lane; i < pl.ga; i += 64) units[i] = order[i];  // the list, largest group first
+    } else {
+      tg_deal<C>(pl, order, smem, units, ustart, sched, nq, P, gr, lane);
+    }
+  }
   __syncthreads();
-  // this queue's units [ucur, u_end) and items [0, n_items): tiles
-  // (dynamic) or groups (gang; none for a workgroup past the tile count)
-  int ucur = __builtin_amdgcn_readfirstlane(sched[kSchedOff + x]);
-  const int ubase = ucur;
-  const int u_end = __builtin_amdgcn_readfirstlane(sched[kSchedOff + x + 1]);
-  const int n_items = gang ? (j < gang_tiles ? u_end - ubase : 0)
-                           : __builtin_amdgcn_readfirstlane(sched[kSchedTiles + x]);
+  // dynamic: this queue's units [ucur, u_end) and tiles [0, n_items); gang:
+  // list items [0, n_items) (none for a workgroup past the tile count)
+  int ucur = gang ? 0 : __builtin_amdgcn_readfirstlane(sched[kSchedOff + x]);
+  const int u_end = gang ? 0 : __builtin_amdgcn_readfirstlane(sched[kSchedOff + x + 1]);
+  const int n_items = gang ? (j < gang_tiles ? pl.ga : 0) : __builtin_amdgcn_readfirstlane(sched[kSchedTiles + x]);
   int* const counter = p.queue + x;
+  unsigned long long* const meet_word = reinterpret_cast<unsigned long long*>(p.queue + kGangMeet + 2 * x);
   // Output groups the plan dropped (a group offset past G - Ga, which is
   // flagged) are zero.  K * N is a multiple of 64, so 16-byte stores tile it.
   {
@@ -654,33 +701,40 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
     for (long long off = b0 + ((long long)slot * C::T + tid) * 16; off < b1; off += (long long)P * C::T * 16)
       *reinterpret_cast<i32x4*>(o + off) = i32x4{0, 0, 0, 0};
   }
-  // The last workgroup of the queue to get here resets its counters; every
-  // index this workgroup grabbed (dynamic), every arrival it counted (gang),
-  // has returned by then.
+  // The last workgroup of the queue to get here resets the queue's counters,
+  // and the last of the grid the grid's; every index grabbed and every
+  // arrival counted has returned by then.
   auto finish = [&]() {
     if (tid == 0) {
       const int prev = atomicAdd(p.queue + kQueues + x, 1);
       if (prev == W - 1) {
         atomicExch(counter, 0);
+        atomicExch(meet_word, 0ull);
         atomicExch(p.queue + kQueues + x, 0);
+      }
+      const int all = atomicAdd(p.queue + kGangDone, 1);
+      if (all == P - 1) {
+        atomicExch(p.queue + kGangNext, 0);
+        atomicExch(p.queue + kGangDone, 0);
       }
     }
   };
 
-  // Item indices.  Gang: 0, 1, 2, ...  Dynamic: the queue's first two rounds
+  // Item indices.  Gang: list items x and 2 kQueues - 1 - x, then the
+  // leader's grabs (tg_gang_meet).  Dynamic: the queue's first two rounds
   // are fixed, workgroup j of the queue's W taking tiles j and 2W-1-j (had
   // each grabbed its first two, the first workgroups would take two of the
   // longest tiles each); afterwards each tile grabs the index of the tile
   // after next during its first steps (so the next tile is known before its
   // loads start), from 2W on.
-  int L_cur = gang ? 0 : j;
-  int L_nxt = gang ? 1 : 2 * W - 1 - j;
+  int L_cur = gang ? x : j;
+  int L_nxt = gang ? 2 * kQueues - 1 - x : 2 * W - 1 - j;
   if (L_cur >= n_items) {
     finish();
     return;
   }
   auto decode = [&](int L) __attribute__((always_inline)) {
-    return gang ? decode_gang<C>(p, pl, units, ubase, L, tj, w)
+    return gang ? decode_gang<C>(p, pl, units, L, tj, w)
                 : decode_tg<C>(p, pl, units, ustart, &ucur, u_end, L, gr, w, lane);
   };
 
@@ -743,6 +797,7 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
   f32x16 acc[C::NACC];
   int stage = 0;
   int arrivals = 0;  // gang: this workgroup's meets so far (every workgroup of the queue meets as often)
+  int seen0 = 0, seen1 = 0;  // gang: the meet word's two index fields as last seen
   int L_new = 0;  // the grabbed index handed over during the current tile
 
   // One contraction step (as the big kernel's K step, without a bias row):
@@ -818,20 +873,25 @@ __global__ __launch_bounds__(C::T) void gmm_tgmm_kernel(Params p) {
     const int g = tg_grab_wave(counter, lane, w == 0 && !last_item && !gang);
     kstep(shape_tag, W0G{}, F_{}, F_{}, 4);
     for (int kt = 2; kt + 3 < KT; ++kt) kstep(shape_tag, W1{}, F_{}, F_{}, kt + 3);
-    // gang: meet the queue's other workgroups before the next group's loads
-    if (gang && !last_item && w == 0) tg_gang_meet(counter, gang_tiles * ++arrivals, lane);
+    // gang: meet the queue's other workgroups before the next group's
+    // loads, and learn the group after it
+    int after = kGangNone;
+    if (gang && !last_item && w == 0)
+      after = tg_gang_meet(meet_word, p.queue + kGangNext, p.flags, arrivals++, gang_tiles, j == 0, seen0, seen1,
+                           lane);
     kstep(shape_tag, W1{}, T_{}, F_{}, 0);  // kt = KT-3: the next tile's step 0
     // the grab has returned (this step's wait left only the loads of the
     // step before outstanding); hand it to every wave, which reads it after
     // the last step's barrier
-    if (w == 0 && lane == 0 && !last_item) sched[kSchedSlot] = g;
+    if (w == 0 && lane == 0 && !last_item) sched[kSchedSlot] = gang ? after : g;
     kstep(shape_tag, W1{}, T_{}, F_{}, 1);
     kstep(shape_tag, W1{}, T_{}, T_{}, 2);
     // every refill has landed before the epilogue takes registers of its own
     __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
     hold(0);
     hold(1);
-    L_new = gang ? L_nxt + 1 : 2 * W + __builtin_amdgcn_readfirstlane(sched[kSchedSlot]);
+    L_new = gang ? __builtin_amdgcn_readfirstlane(sched[kSchedSlot])
+                 : 2 * W + __builtin_amdgcn_readfirstlane(sched[kSchedSlot]);
     // the last step's stage holds the epilogue's staging slices, 4 KB per wave
     tg_epilogue<C, SC::FM, SC::FN>(p, acc, cur, smem + ((stage + 3) & (C::S - 1)) * C::STAGE + w * 4096, kh, r32,
                                    lane);

@@ -31,6 +31,20 @@ def test_header_declares_the_entry_points():
                                   "gmm_debug_worklist"])
 
 
+def test_binding_constants_match_the_header():
+    """The binding's status codes and device-flag bits are the values the
+    header defines (the kernels' own flag constants are checked against the
+    header by the library's build: gmm_api.cpp static_asserts them)."""
+    from moe_grouped_matrix_amd import _binding as b
+    text = open(HEADER).read()
+    flags = {k: int(v, 16) for k, v in re.findall(r"#define (GMM_FLAG_\w+) (0x[0-9a-fA-F]+)u", text)}
+    assert flags == {"GMM_FLAG_NEGATIVE_SIZE": b.FLAG_NEGATIVE_SIZE, "GMM_FLAG_SIZES_EXCEED_M": b.FLAG_SIZES_EXCEED_M,
+                     "GMM_FLAG_BAD_OFFSET": b.FLAG_BAD_OFFSET, "GMM_FLAG_SCHEDULE_TIMEOUT": b.FLAG_SCHEDULE_TIMEOUT}
+    status = {k: int(v) for k, v in re.findall(r"^\s*(GMM_(?:OK|E_\w+)) = (-?\d+)", text, flags=re.M)}
+    assert status == {"GMM_OK": b.GMM_OK, "GMM_E_INVALID": b.GMM_E_INVALID, "GMM_E_UNSUPPORTED": b.GMM_E_UNSUPPORTED,
+                      "GMM_E_HIP": b.GMM_E_HIP, "GMM_E_DEVICE_DATA": b.GMM_E_DEVICE_DATA}
+
+
 def test_library_exports_every_declared_symbol(lib_path):
     import moe_grouped_matrix_amd as m
     lib = m.load(lib_path)
