@@ -11,8 +11,8 @@
 // LDS the weight slab (256 rows of 128 bytes), the tile's lhs rows (64 rows
 // of 256 bytes), the block's 256 scales and the tile's 256 bias values.
 // Three stages form a ring filled by direct-to-LDS loads two stages ahead,
-// across the workgroup's tiles, so the HBM stream never drains.  Four
-// waves, one per SIMD: wave w computes columns 64 w .. +64 for all 64 rows
+// across the workgroup's tiles, so the HBM stream never drains.  Eight
+// waves, two per SIMD: wave w computes columns 32 w .. +32 for all 64 rows
 // (two 32-row blocks) over the whole of K with 32x32x16 bf16 MFMAs, so no
 // partial sums cross waves and each weight byte is widened by one wave
 // only.  The weight fragment is the MFMA's first operand (a lane holds runs
@@ -24,15 +24,18 @@
 // and the widest tile moves the most weight per lhs byte (64-row tiles 32,
 // 64, 128 and 256 columns wide ran a 128-K stage in 0.49, 0.67, 1.05 and
 // 2.1 us; 32 x 64 tiles, which also read each expert's weight once per 32
-// rows, took 38.9 us per decode call against 33.4 us).  A stage's vector
-// work (widening the weight, the scale fold) is a large part of it:
-// widening each weight byte in one wave instead of two took the call from
-// 33.3 to 32.3 us.
+// rows, took 38.9 us per decode call against 33.4 us).  A stage's own work
+// (widening the weight, the scale fold, the MFMAs, the LDS reads) is what
+// sets its time, not the HBM stream: with the weight loads dropped the call
+// still took 27.0 of 31.3 us.  So each weight byte is widened by one wave
+// (32.3 us, from 33.3 with two), two waves share each SIMD to hide each
+// other's latencies (29.3 us, from 31.6 with one), and the wait for the next
+// stage comes after the multiply (27.6 us).
 //
-// Every wave issues the same loads in every stage (eight weight and four
+// Every wave issues the same loads in every stage (four weight and two
 // lhs; wave 0 also the scales, wave 1 the bias; loads past a range return
 // zeros and still count) and the same stores per tile, so the vmcnt waits
-// are constants (one set for waves 0 and 1, one for 2 and 3).
+// are constants (one set for waves 0 and 1, one for the others).
 #pragma once
 
 #include "gmm_big.hpp"
@@ -45,7 +48,7 @@ struct StreamCfg {
   static constexpr bool OUT_F32 = OUT_F32_;
   static constexpr int FB = FB_;
   static constexpr int BM = 64, BN = 256, BKS = 128;  // tile rows, tile columns, K per stage
-  static constexpr int NWAVES = 4, T = 64 * NWAVES;
+  static constexpr int NWAVES = 8, T = 64 * NWAVES;
   static constexpr int W_ROW = BKS, A_ROW = BKS * 2;  // bytes per weight / lhs row in a stage
   static constexpr int W_BYTES = BN * W_ROW, A_BYTES = BM * A_ROW;
   // the block's scales (256 f32) and the tile's bias (256 values): one
@@ -59,10 +62,12 @@ struct StreamCfg {
   static constexpr int W_OPS = W_BYTES / 1024 / NWAVES, A_OPS = A_BYTES / 1024 / NWAVES;
   // loads per stage: waves 0 and 1 one more (the scales, the bias)
   static constexpr int OPS_LO = W_OPS + A_OPS, OPS_HI = OPS_LO + 1;
-  static constexpr int FM = 2, FN = 2;  // 32-row and 32-column blocks per wave
+  static constexpr int FM = 2, FN = 1;  // 32-row and 32-column blocks per wave
+  static constexpr int WCOLS = 32 * FN;  // columns per wave
   static constexpr int es_out = OUT_F32 ? 4 : 2;
   static constexpr int E = FM * FN * (OUT_F32 ? 4 : 2);  // 16-byte stores per wave and tile
-  static_assert(W_OPS == 8 && A_OPS == 4, "load split");
+  static_assert(W_OPS * NWAVES == 32 && A_OPS * NWAVES == 16, "load split");
+  static_assert(WCOLS * NWAVES == BN, "the waves cover the tile's columns");
 };
 
 // 128-byte weight rows: chunk c of row n at c ^ swz_w(n); 256-byte lhs rows:
@@ -139,12 +144,12 @@ __device__ __forceinline__ StreamOff stream_offsets(int K, int w, int lane, bool
   StreamOff o;
 #pragma unroll
   for (int i = 0; i < C::W_OPS; ++i) {
-    const int n = 8 * (4 * i + w) + (lane >> 3);
+    const int n = 8 * (C::NWAVES * i + w) + (lane >> 3);
     o.w[i] = n * K + (((lane & 7) ^ swz_w(n)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < C::A_OPS; ++i) {
-    const int r = 4 * (4 * i + w) + (lane >> 4);
+    const int r = 4 * (C::NWAVES * i + w) + (lane >> 4);
     o.a[i] = r * K * 2 + (((lane & 15) ^ swz_a(r)) << 4);
   }
   if (w == 1 && !bias_f32)
@@ -163,11 +168,11 @@ template <class C>
 __device__ __forceinline__ void stream_stage(const StreamSrc& s, const StreamOff& o, int k, int N, char* st, int w) {
 #pragma unroll
   for (int i = 0; i < C::W_OPS; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rw, (lds_ptr_t)(st + (4 * i + w) * 1024), 16, o.w[i],
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rw, (lds_ptr_t)(st + (C::NWAVES * i + w) * 1024), 16, o.w[i],
                                              k * C::W_ROW, 0, 0);
 #pragma unroll
   for (int i = 0; i < C::A_OPS; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.ra, (lds_ptr_t)(st + C::W_BYTES + (4 * i + w) * 1024), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.ra, (lds_ptr_t)(st + C::W_BYTES + (C::NWAVES * i + w) * 1024), 16,
                                              o.a[i], k * C::A_ROW, 0, 0);
   const int xv = o.xcols < s.ncols ? (int)(threadIdx.x & 63) * 16 : (int)0x80000000;
   if (w == 0)
@@ -245,15 +250,15 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
     int w_off[C::FN][4];
 #pragma unroll
     for (int fb = 0; fb < C::FN; ++fb) {
-      const int wn = 64 * w + 32 * fb + r32;  // weight row = tile column
+      const int wn = C::WCOLS * w + 32 * fb + r32;  // weight row = tile column
 #pragma unroll
       for (int c = 0; c < 4; ++c) w_off[fb][c] = wn * C::W_ROW + (((4 * kh + c) ^ swz_w(wn)) << 4);
     }
     // lhs rows 32 fm + r32 (fm = 0, 1), the same swizzle
     const int a_base = C::W_BYTES + r32 * C::A_ROW;
     const int a_swz = swz_a(r32);
-    // this lane's columns of block fb: 64 w + 32 fb + 8 g + 4 kh + [0, 4), g = 0..3
-    const int col_l = 64 * w + 4 * kh;
+    // this lane's columns of block fb: WCOLS w + 32 fb + 8 g + 4 kh + [0, 4), g = 0..3
+    const int col_l = C::WCOLS * w + 4 * kh;
 
     // a stage's fragments: the weight runs (64 one-byte values per column
     // block), the lhs rows (eight 16-byte chunks per row block), the
@@ -287,22 +292,21 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) tot[b][i] = 0.f;
 
-    // One stage kt of the current tile.  Stage kt+1's loads are complete
-    // (this wave's, then every wave's after the barrier) once at most the
-    // S-3 stages issued after it and, in a tile's first S-2 stages, the
-    // previous tile's E stores are outstanding.  The barrier also frees the
-    // slot stage kt-1 used, which takes stage kt+S-1 (of this tile, or kd of
-    // the next one when NEXT).  Stage kt's fragments (read into registers
-    // during the previous stage) are multiplied and folded with its scales
-    // and, in a tile's last stage, the outputs stored; then the registers
-    // are refilled with stage kt+1's fragments.  (Refilling a slot as soon
-    // as its stage is multiplied, which keeps one more stage in flight at
-    // each wait, measured no faster: 36.5 against 33.4 us per decode call.)
+    // One stage kt of the current tile.  The barrier at the end of the
+    // previous stage freed the slot of stage kt-1 (every wave had read its
+    // fragments), which now takes stage kt+S-1 (of this tile, or stage kd of
+    // the next one when NEXT).  Stage kt's fragments, read into registers at
+    // the end of the previous stage, are multiplied and folded with its
+    // scales and, in a tile's last stage, the outputs stored.  Then stage
+    // kt+1's loads are complete (this wave's, then every wave's after the
+    // barrier) once at most the S-2 stages issued after it and, at a tile
+    // boundary (WITH_E), the E stores between them are outstanding, and the
+    // registers are refilled with stage kt+1's fragments.  Waiting there
+    // rather than before the multiply keeps two stages' loads in flight
+    // while a stage is multiplied (27.6 against 29.3 us per decode call).
     auto kstage = [&](auto wait_tag, auto next_tag, int kt, int kd) __attribute__((always_inline)) {
       constexpr bool WITH_E = decltype(wait_tag)::value;
       constexpr bool NEXT = decltype(next_tag)::value;
-      wait_stream<(C::S - 3) * C::OPS_LO + (WITH_E ? C::E : 0), (C::S - 3) * C::OPS_HI + (WITH_E ? C::E : 0)>(w);
-      ring_barrier();
       stream_stage<C>(NEXT ? snxt : scur, off, kd, N, smem + ((stage + C::S - 1) % C::S) * C::STAGE, w);
       const char* st = smem + stage * C::STAGE;
 #pragma unroll
@@ -373,7 +377,7 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
           for (int gp = 0; gp < 4; gp += 2) {
             // after the swap: kh = 0 holds columns 8 gp + [0, 8) of the
             // block, kh = 1 holds 8 (gp + 1) + [0, 8)
-            const int col = 64 * w + 32 * fb + 8 * (gp + kh);
+            const int col = C::WCOLS * w + 32 * fb + 8 * (gp + kh);
             const int voff = col < cur.ncols ? (row * N + col) * C::es_out : (int)0x80000000;
             if constexpr (C::OUT_F32) {
               int lo[4], hi[4];
@@ -401,24 +405,27 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
           for (int i = 0; i < 16; ++i) tot[b][i] = 0.f;
         }
       }
+      wait_stream<(C::S - 2) * C::OPS_LO + (WITH_E ? C::E : 0), (C::S - 2) * C::OPS_HI + (WITH_E ? C::E : 0)>(w);
+      ring_barrier();
       const int stage1 = stage + 1 == C::S ? 0 : stage + 1;
       read_frags(smem + stage1 * C::STAGE);
       stage = stage1;
     };
-    using WE = std::true_type;   // the previous tile's stores are among the newer operations
+    using WE = std::true_type;   // a tile boundary's stores are among the newer operations
     using WN = std::false_type;
     using CUR = std::false_type;
     using NXT = std::true_type;
-    // stages kt < S-2 wait for the previous tile's stores too; stages
-    // kt >= KT-S+1 load the next tile's first stages
-    const int e_end = C::S - 2, n_beg = KT - C::S + 1;
+    // With S = 3 (KT >= 3): the stores sit between stage 1 and stage 2 of a
+    // tile, so the waits of its stage 0 (for stage 1) and of the previous
+    // tile's last stage (for stage 0) count them; stages KT-2 and KT-1 load
+    // the next tile's stages 0 and 1.
+    static_assert(C::S == 3, "the tile loop below is written for a three-stage ring");
 
     while (true) {
-      const int a1 = e_end < n_beg ? e_end : n_beg;
-      for (int kt = 0; kt < a1; ++kt) kstage(WE{}, CUR{}, kt, kt + C::S - 1);
-      for (int kt = a1; kt < e_end; ++kt) kstage(WE{}, NXT{}, kt, kt + C::S - 1 - KT);
-      for (int kt = e_end; kt < n_beg; ++kt) kstage(WN{}, CUR{}, kt, kt + C::S - 1);
-      for (int kt = (e_end > n_beg ? e_end : n_beg); kt < KT; ++kt) kstage(WN{}, NXT{}, kt, kt + C::S - 1 - KT);
+      kstage(WE{}, CUR{}, 0, 2);
+      for (int kt = 1; kt < KT - 2; ++kt) kstage(WN{}, CUR{}, kt, kt + 2);
+      kstage(WN{}, NXT{}, KT - 2, 0);
+      kstage(WE{}, NXT{}, KT - 1, 1);
       if (last_item) break;
       L += P;
       last_item = L + P >= n_items;

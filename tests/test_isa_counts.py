@@ -88,19 +88,23 @@ def test_tgmm_kernel_keeps_every_counted_store(kernel_asm):
 
 
 def test_stream_kernel_keeps_every_counted_operation(stream_asm):
-    """The weight-streaming kernel's waits count 14 direct-to-LDS loads per
-    stage in the code (8 weight and 4 lhs per wave, the scale load of wave 0
+    """The weight-streaming kernel's waits count 8 direct-to-LDS loads per
+    stage in the code (4 weight and 2 lhs per wave, the scale load of wave 0
     and the bias load of wave 1: two stages in the prologue and one in each
-    of the K loop's four variants) and E = 8 (bf16 output) or 16 (f32)
-    stores per tile: the prologue's E range-dropped stores and the epilogue
-    of each of the three loop variants that can end a tile."""
+    of the K loop's four variants) and E = 4 (bf16 output) or 8 (f32) stores
+    per wave and tile: the prologue's E range-dropped stores and the
+    epilogue of each of the three loop variants that can end a tile.  Where
+    a stage is a tile's stage 0, wave 0's scale load and wave 1's bias load
+    have the same form (offset 0) and may be one instruction with the
+    resource chosen per wave -- still one load in each of those waves -- so
+    up to two loads fewer appear in the code."""
     seen = 0
     for name, lines in _functions(stream_asm, r"_ZN4gmmk17gmm_stream_kernel"):
         out_f32 = re.search(r"StreamCfgILb([01])E", name).group(1) == "1"
         loads = sum(1 for ln in lines if ln.startswith("buffer_load") and ln.endswith(" lds"))
         stores = sum(1 for ln in lines if ln.startswith("buffer_store"))
-        assert loads == 6 * 14, (name, loads)
-        assert stores == 4 * (16 if out_f32 else 8), (name, stores)
+        assert 6 * 8 - 2 <= loads <= 6 * 8, (name, loads)
+        assert stores == 4 * (8 if out_f32 else 4), (name, stores)
         seen += 1
     assert seen == 6  # e4m3fn / e5m2 / int8 weights x bf16 / f32 output
 
