@@ -18,7 +18,10 @@ one kernel's.
 The bar is the parity bar of the other tests: f32 output within 1e-4 of the
 largest reference magnitude, bf16 output within 2e-2 relative Frobenius
 error overall and per row, rows outside the active groups zero (or the
-existing output's bits)."""
+existing output's bits).  The same for the transposed product (tgmm): group
+counts, offsets, K and N on and off the tile multiples, f32 or bf16 output,
+the grid (the single-queue and per-XCD schedules) and the allocation-free
+entry point."""
 import numpy as np
 import pytest
 import torch
@@ -162,3 +165,62 @@ def test_random_problem_matches_the_oracle(trial):
     else:
         assert torch.equal(outside, torch.cat([existing[:lo], existing[hi:]])), \
             "rows outside the active groups do not keep the existing output"
+
+
+# The transposed product (the weight gradient): bf16 operands, f32 or bf16
+# out [Ga,K,N]; group counts past 16 with grids that are multiples of 8
+# reach the per-XCD schedules, other grids the single queue.
+TG_TRIALS = 48
+
+
+def _draw_tgmm(trial):
+    rng = np.random.default_rng(8200 + trial)
+    gen = torch.Generator().manual_seed(8200 + trial)
+    G = int(rng.integers(1, 41))
+    s = int(rng.integers(0, G))
+    ga = int(rng.integers(1, G - s + 1)) if rng.random() < 0.9 else 0
+    sizes = _sizes(rng, G)
+    M = max(1, sum(sizes) + int(rng.integers(0, 20)))
+    K = 8 * int(rng.integers(1, 101))
+    N = 8 * int(rng.integers(1, 101))
+    rows = max(1, sum(sizes[s:s + ga]))
+    while rows * K * N > MAC_BUDGET and K > 8:
+        K = max(8, (K // 2) // 8 * 8)
+    lhs = torch.randn((M, K), generator=gen).to(torch.bfloat16)
+    rhs = torch.randn((M, N), generator=gen).to(torch.bfloat16)
+    out_dtype = torch.float32 if rng.random() < 0.6 else torch.bfloat16
+    grid = int(rng.choice([0, 0, 5, 8, 16, 24, 40]))
+    no_alloc = bool(rng.random() < 0.2)
+    return lhs, rhs, sizes, s, ga, out_dtype, grid, no_alloc
+
+
+@pytest.mark.parametrize("trial", range(TG_TRIALS))
+def test_random_tgmm_problem_matches_the_oracle(trial):
+    import moe_grouped_matrix_amd as m
+    lhs, rhs, sizes, s, ga, out_dtype, grid, no_alloc = _draw_tgmm(trial)
+    K, N = lhs.shape[1], rhs.shape[1]
+    print(f"tgmm sweep trial {trial}: M={lhs.shape[0]} K={K} N={N} sizes={sizes} s={s} ga={ga} "
+          f"out={out_dtype} grid={grid} no_alloc={no_alloc}", flush=True)
+    gs = torch.tensor(sizes, dtype=torch.int32)
+    m.set_grid_limit(grid)
+    try:
+        out = m.tgmm(lhs.cuda(), rhs.cuda(), gs.cuda(), num_active=ga, group_offset=s, out_dtype=out_dtype,
+                     no_alloc=no_alloc)
+        torch.cuda.synchronize()
+        assert m.device_flags() == 0
+    finally:
+        m.set_grid_limit(0)
+    assert tuple(out.shape) == (ga, K, N)
+    if ga == 0:
+        return
+    out = out.cpu()
+    ref = oracle.tgmm_reference(lhs, rhs, gs, group_offset=s, num_active=ga)
+    compare(out.reshape(ga * K, N), ref.reshape(ga * K, N), out_dtype, what=f"tgmm trial {trial}")
+    iv = torch.int16 if out_dtype == torch.bfloat16 else torch.int32
+    for h in range(ga):
+        if sizes[s + h] == 0:
+            assert int((out[h].view(iv) != 0).sum()) == 0, f"empty group {h} is not all-zero bits"
+        elif out_dtype == torch.float32:
+            scale = np.abs(ref[h]).max()
+            err = np.abs(out[h].double().numpy() - ref[h]).max()
+            assert err <= 1e-4 * max(scale, 1e-30), f"group {h}: max err {err} against {scale}"
