@@ -379,6 +379,27 @@ def test_no_active_group_writes_zeros_everywhere():
         assert int((out.view(torch.int16) != 0).sum()) == 0
 
 
+def test_zero_row_problems():
+    """M = 0: gmm returns an empty output without a launch; tgmm writes every
+    group of its output as zeros (all groups are empty) over a pre-filled
+    buffer, and no data error is flagged."""
+    import moe_grouped_matrix_amd as m
+    lhs = torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda")
+    w = torch.randn(2, 32, 64).to(torch.bfloat16).cuda()
+    gs = torch.zeros(2, dtype=torch.int32, device="cuda")
+    out = m.gmm(lhs, w, gs, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, 32)
+    rhs = torch.zeros(0, 40, dtype=torch.bfloat16, device="cuda")
+    gs3 = torch.zeros(3, dtype=torch.int32, device="cuda")
+    for od in (torch.float32, torch.bfloat16):
+        dw = torch.full((3, 64, 40), 7.0, dtype=od, device="cuda")
+        m.tgmm(lhs, rhs, gs3, out=dw)
+        torch.cuda.synchronize()
+        assert int((dw.view(torch.int16) != 0).sum()) == 0
+    assert m.device_flags() == 0
+
+
 def test_single_group_is_dense_matmul():
     g = torch.Generator().manual_seed(5)
     lhs = torch.randn(300, 256, generator=g).to(torch.bfloat16)
