@@ -59,7 +59,7 @@ def test_library_exports_every_declared_symbol(lib_path):
 def test_library_has_no_undefined_internal_symbols(lib_path):
     """Every kernel launched from the host has its launch stub in the library
     (a kernel the host compiler silently failed to instantiate would show up
-    here as an undefined symbol and only fail at load time on a GPU machine)."""
+    here as an undefined symbol and only fail at load time on a machine with a GPU)."""
     syms = subprocess.run(["nm", "-D", "--undefined-only", lib_path], capture_output=True, text=True).stdout
     assert "gmmk" not in syms, [l for l in syms.splitlines() if "gmmk" in l]
 
