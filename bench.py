@@ -488,7 +488,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path).", file=sys.stderr)
+              "(the library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
 
     clock = ClockSampler()  # before the first GPU call: it starts a child process
