@@ -118,7 +118,7 @@ hipError_t by_size(const Params& p, const KernelChoice& kc, int cu, hipStream_t 
       return bias ? launch_big<BigCfg<NN, false, true>>(p, cu, cap, st) : launch_big<BigCfg<NN, false, false>>(p, cu, cap, st);
     }
   }
-  if constexpr (OP == Op::BF16 && BF8 && !NN && (FMT >> 3) < 3) {  // one-byte weights
+  if constexpr (OP == Op::BF16 && BF8 && !NN && (FMT >> 3) < 6) {  // one-byte and four-bit weights
     if (sz == SizeClass::Small && stream_fits(p)) return launch_stream(p, FMT >> 3, cu, cap, st);
   }
   // W8A8 (one-byte fp8 operands) with scale blocks of one K step

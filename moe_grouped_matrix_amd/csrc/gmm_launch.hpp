@@ -47,13 +47,14 @@ inline bool w8a8_fits(const Params& p) {
 // Queue it for lhs format fa and rhs format fb (0 e4m3fn, 1 e5m2).
 hipError_t launch_w8a8(const Params& p, int fa, int fb, int cu_count, int grid_cap, hipStream_t stream);
 
-// The weight-streaming kernel (gmm_stream.hip) takes bf16 x one-byte-weight
+// The weight-streaming kernel (gmm_stream.hip) takes bf16 x narrow-weight
 // NT problems with few rows per group: K a multiple of 128 with at least S
 // stages of 128 per tile (S: the depth of its LDS ring), no lhs scale, and
 // rhs scale blocks of exactly one stage (or no rhs scale).
 bool stream_fits(const Params& p);
 
-// Queue it for weight format fb (0 e4m3fn, 1 e5m2, 2 int8).
+// Queue it for weight format fb (0 e4m3fn, 1 e5m2, 2 int8, 3 int4, 4 uint4,
+// 5 fp4 e2m1).
 hipError_t launch_stream(const Params& p, int fb, int cu_count, int grid_cap, hipStream_t stream);
 
 // Queue the transposed grouped matmul (out [Ga,K,N]); grid_cap > 0 limits

@@ -39,9 +39,16 @@ bool stream_fits(const Params& p) {
 }
 
 hipError_t launch_stream(const Params& p, int fb, int cu, int cap, hipStream_t st) {
-  if (!stream_fits(p) || fb < 0 || fb > 2) return hipErrorInvalidValue;
-  if (fb == 0) return launch_out<0>(p, cu, cap, st);
-  return fb == 1 ? launch_out<1>(p, cu, cap, st) : launch_out<2>(p, cu, cap, st);
+  if (!stream_fits(p)) return hipErrorInvalidValue;
+  switch (fb) {
+    case 0: return launch_out<0>(p, cu, cap, st);
+    case 1: return launch_out<1>(p, cu, cap, st);
+    case 2: return launch_out<2>(p, cu, cap, st);
+    case 3: return launch_out<3>(p, cu, cap, st);
+    case 4: return launch_out<4>(p, cu, cap, st);
+    case 5: return launch_out<5>(p, cu, cap, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace gmmk

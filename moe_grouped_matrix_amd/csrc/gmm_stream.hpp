@@ -1,8 +1,9 @@
 // gmm_stream.hpp -- the weight-streaming kernel of the gfx950 grouped matmul:
-// bf16 lhs x one-byte weight [G,N,K] (e4m3fn, e5m2 or int8, widened exactly
-// to bf16) with per-block rhs_scale and an optional bias, for problems with
-// few rows per group (decode), where the run time is the time to read every
-// active group's weight once from HBM.
+// bf16 lhs x narrow weight [G,N,K] (e4m3fn, e5m2 or int8, or packed int4,
+// uint4 or fp4 e2m1, widened exactly to bf16) with per-block rhs_scale and
+// an optional bias, for problems with few rows per group (decode), where
+// the run time is the time to read every active group's weight once from
+// HBM.
 //
 // Output tiles are 64 rows (group-aligned) x 256 columns; a tile reads its
 // group's 256 x K weight slab once, so a group of up to 64 rows reads its
@@ -42,14 +43,18 @@
 
 namespace gmmk {
 
-// FB_: the weight's one-byte format (0 e4m3fn, 1 e5m2, 2 int8).
+// FB_: the weight's format: one byte (0 e4m3fn, 1 e5m2, 2 int8) or four
+// bits, two to a byte with the even element in the low nibble (3 int4,
+// 4 uint4, 5 fp4 e2m1).
 template <bool OUT_F32_, int FB_ = 0>
 struct StreamCfg {
   static constexpr bool OUT_F32 = OUT_F32_;
   static constexpr int FB = FB_;
   static constexpr int BM = 64, BN = 256, BKS = 128;  // tile rows, tile columns, K per stage
   static constexpr int NWAVES = 8, T = 64 * NWAVES;
-  static constexpr int W_ROW = BKS, A_ROW = BKS * 2;  // bytes per weight / lhs row in a stage
+  static constexpr bool NIB = FB >= 3;  // four-bit weights
+  static constexpr int W_ROW = NIB ? BKS / 2 : BKS, A_ROW = BKS * 2;  // bytes per weight / lhs row in a stage
+  static constexpr int W_CHUNKS = W_ROW / 16;  // 16-byte chunks per weight row (8, or 4 for four bits)
   static constexpr int W_BYTES = BN * W_ROW, A_BYTES = BM * A_ROW;
   // the block's scales (256 f32) and the tile's bias (256 values): one
   // 16-byte-per-lane load each, whose 64 lanes all write the slot
@@ -66,15 +71,18 @@ struct StreamCfg {
   static constexpr int WCOLS = 32 * FN;  // columns per wave
   static constexpr int es_out = OUT_F32 ? 4 : 2;
   static constexpr int E = FM * FN * (OUT_F32 ? 4 : 2);  // 16-byte stores per wave and tile
-  static_assert(W_OPS * NWAVES == 32 && A_OPS * NWAVES == 16, "load split");
+  static_assert(W_OPS * NWAVES * 1024 == W_BYTES && A_OPS * NWAVES == 16, "load split");
   static_assert(WCOLS * NWAVES == BN, "the waves cover the tile's columns");
 };
 
-// 128-byte weight rows: chunk c of row n at c ^ swz_w(n); 256-byte lhs rows:
-// chunk c of row r at c ^ (r & 15).  Eight consecutive weight rows, or
-// sixteen consecutive lhs rows, read at one logical chunk then land in
-// distinct bank groups.
+// 128-byte weight rows: chunk c of row n at c ^ swz_w(n); 64-byte (four-bit)
+// weight rows: at c ^ swz_w4(n); 256-byte lhs rows: chunk c of row r at
+// c ^ (r & 15).  Sixteen consecutive weight or lhs rows read at one logical
+// chunk then land in distinct 16-byte bank groups.
 __device__ __forceinline__ int swz_w(int n) { return (n & 7) ^ ((n >> 3) & 1); }
+__device__ __forceinline__ int swz_w4(int n) { return (n >> 2) & 3; }
+template <class C>
+__device__ __forceinline__ int swz_row(int n) { return C::NIB ? swz_w4(n) : swz_w(n); }
 __device__ __forceinline__ int swz_a(int r) { return r & 15; }
 
 struct StreamItem {
@@ -109,9 +117,10 @@ __device__ __forceinline__ StreamSrc stream_src(const Params& p, const StreamIte
   const int K = p.K, N = p.N;
   StreamSrc s;
   const char* a = reinterpret_cast<const char*>(p.lhs) + (long long)it.row0 * K * 2;
-  const char* w = reinterpret_cast<const char*>(p.rhs) + ((long long)it.h * N + it.n0) * K;
+  const int wrow = C::NIB ? K / 2 : K;  // weight bytes per row
+  const char* w = reinterpret_cast<const char*>(p.rhs) + ((long long)it.h * N + it.n0) * wrow;
   s.ra = uniform_rsrc(a, live ? it.rows * K * 2 : 0);
-  s.rw = uniform_rsrc(w, live ? it.ncols * K : 0);
+  s.rw = uniform_rsrc(w, live ? it.ncols * wrow : 0);
   if (p.rhs_scale) {
     const char* sc = reinterpret_cast<const char*>(p.rhs_scale) + ((long long)it.h * p.nb * N + it.n0) * 4;
     s.rs = uniform_rsrc(sc, live ? p.nb * N * 4 - it.n0 * 4 : 0);
@@ -130,8 +139,9 @@ __device__ __forceinline__ StreamSrc stream_src(const Params& p, const StreamIte
 }
 
 // Per-lane offsets of this wave's loads.  Its weight load i is load
-// j = 4 i + w of the stage: rows 8 j + lane/8, chunk lane%8.  Its lhs load
-// i is load j = 4 i + w: rows 4 j + lane/16, chunk lane%16.  Wave 0 also
+// j = 8 i + w of the stage: rows 8 j + lane/8, chunk lane%8 (four-bit
+// weights: rows 16 j + lane/4, chunk lane%4).  Its lhs load i is load
+// j = 8 i + w: rows 4 j + lane/16, chunk lane%16.  Wave 0 also
 // loads the block's scales (lane: columns 4 lane .. +4) and wave 1 the bias
 // (lane: columns 8 lane .. +8 for bf16, lanes < 32; 4 lane .. +4 for f32).
 // The column test is made per tile (stream_stage).
@@ -144,8 +154,13 @@ __device__ __forceinline__ StreamOff stream_offsets(int K, int w, int lane, bool
   StreamOff o;
 #pragma unroll
   for (int i = 0; i < C::W_OPS; ++i) {
-    const int n = 8 * (C::NWAVES * i + w) + (lane >> 3);
-    o.w[i] = n * K + (((lane & 7) ^ swz_w(n)) << 4);
+    if constexpr (C::NIB) {
+      const int n = 16 * (C::NWAVES * i + w) + (lane >> 2);
+      o.w[i] = n * (K / 2) + (((lane & 3) ^ swz_w4(n)) << 4);
+    } else {
+      const int n = 8 * (C::NWAVES * i + w) + (lane >> 3);
+      o.w[i] = n * K + (((lane & 7) ^ swz_w(n)) << 4);
+    }
   }
 #pragma unroll
   for (int i = 0; i < C::A_OPS; ++i) {
@@ -245,14 +260,16 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
     // lane parts of the fragment addresses (stage-relative).  32x32x16 K
     // step j of a stage (j = 0..7), lane half kh: K elements 64 kh + 8 j +
     // [0, 8) of the stage -- weight bytes 8 j .. of the lane's 64-byte run
-    // (16-byte chunks 4 kh .. 4 kh + 3 of its column's 128-byte row), lhs
-    // chunk 8 kh + j of its row's 256-byte row.
-    int w_off[C::FN][4];
+    // (16-byte chunks 4 kh .. 4 kh + 3 of its column's 128-byte row; four-bit
+    // weights: bytes 4 j .. of a 32-byte run, chunks 2 kh, 2 kh + 1 of a
+    // 64-byte row), lhs chunk 8 kh + j of its row's 256-byte row.
+    constexpr int WC = C::W_CHUNKS / 2;  // 16-byte weight chunks per lane and stage
+    int w_off[C::FN][WC];
 #pragma unroll
     for (int fb = 0; fb < C::FN; ++fb) {
       const int wn = C::WCOLS * w + 32 * fb + r32;  // weight row = tile column
 #pragma unroll
-      for (int c = 0; c < 4; ++c) w_off[fb][c] = wn * C::W_ROW + (((4 * kh + c) ^ swz_w(wn)) << 4);
+      for (int c = 0; c < WC; ++c) w_off[fb][c] = wn * C::W_ROW + (((WC * kh + c) ^ swz_row<C>(wn)) << 4);
     }
     // lhs rows 32 fm + r32 (fm = 0, 1), the same swizzle
     const int a_base = C::W_BYTES + r32 * C::A_ROW;
@@ -263,13 +280,13 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
     // a stage's fragments: the weight runs (64 one-byte values per column
     // block), the lhs rows (eight 16-byte chunks per row block), the
     // block's scales of the lane's columns
-    i32x4 fw[C::FN][4], fa[C::FM][8];
+    i32x4 fw[C::FN][WC], fa[C::FM][8];
     f32x4 fsc[C::FN][4];
     auto read_frags = [&](const char* st) __attribute__((always_inline)) {
 #pragma unroll
       for (int fb = 0; fb < C::FN; ++fb)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) fw[fb][c] = *reinterpret_cast<const i32x4*>(st + w_off[fb][c]);
+        for (int c = 0; c < WC; ++c) fw[fb][c] = *reinterpret_cast<const i32x4*>(st + w_off[fb][c]);
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
@@ -316,18 +333,31 @@ __global__ __launch_bounds__(C::T) void gmm_stream_kernel(Params p) {
         for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[fm][i] = 0.f;
+        if constexpr (C::NIB) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          // weight bytes 16 c .. 16 c + 15 of the run: K steps 2 c, 2 c + 1,
-          // widened once for both row blocks
-          const i32x4 bw0 = fp8x8_to_bf16x8<C::FB>(i32x2{fw[fb][c][0], fw[fb][c][1]});
-          const i32x4 bw1 = fp8x8_to_bf16x8<C::FB>(i32x2{fw[fb][c][2], fw[fb][c][3]});
+          for (int j = 0; j < 8; ++j) {
+            // word j % 4 of chunk j / 4 of the run: K step j's eight
+            // nibbles, widened once for both row blocks
+            const i32x4 bw = nib8_to_bf16x8<C::FB>((unsigned)fw[fb][j >> 2][j & 3]);
 #pragma unroll
-          for (int fm = 0; fm < C::FM; ++fm) {
-            acc[fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, bw0), __builtin_bit_cast(bf16x8, fa[fm][2 * c]), acc[fm], 0, 0, 0);
-            acc[fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, bw1), __builtin_bit_cast(bf16x8, fa[fm][2 * c + 1]), acc[fm], 0, 0, 0);
+            for (int fm = 0; fm < C::FM; ++fm)
+              acc[fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, bw), __builtin_bit_cast(bf16x8, fa[fm][j]), acc[fm], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            // weight bytes 16 c .. 16 c + 15 of the run: K steps 2 c, 2 c + 1,
+            // widened once for both row blocks
+            const i32x4 bw0 = fp8x8_to_bf16x8<C::FB>(i32x2{fw[fb][c][0], fw[fb][c][1]});
+            const i32x4 bw1 = fp8x8_to_bf16x8<C::FB>(i32x2{fw[fb][c][2], fw[fb][c][3]});
+#pragma unroll
+            for (int fm = 0; fm < C::FM; ++fm) {
+              acc[fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, bw0), __builtin_bit_cast(bf16x8, fa[fm][2 * c]), acc[fm], 0, 0, 0);
+              acc[fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, bw1), __builtin_bit_cast(bf16x8, fa[fm][2 * c + 1]), acc[fm], 0, 0, 0);
+            }
           }
         }
         // register 4 g + i holds column 8 g + 4 kh + i of the block for the lane's row

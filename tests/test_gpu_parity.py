@@ -480,6 +480,42 @@ def test_weight_streaming_kernel_other_weight_formats(wdtype, out_dtype):
     assert m.device_flags() == 0
 
 
+@pytest.mark.parametrize("fmt", ["int4", "uint4", "fp4_e2m1"])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_weight_streaming_kernel_four_bit_weights_bit_exact(fmt, out_dtype):
+    """The weight-streaming kernel with packed four-bit weights (two to a
+    byte, the even element in the low nibble; every nibble value), on the
+    decode recipe's group sizes and offset: small-integer activations,
+    power-of-two block scales and an integer bias keep every product, block
+    sum and fold exact, so the outputs equal the oracle's bit for bit -- on
+    the full grid and on five workgroups (several tiles each)."""
+    import moe_grouped_matrix_amd as m
+    g = torch.Generator().manual_seed(11)
+    base = workloads.decode_fp8_weight(tokens=48, experts=24, K=768, N=328, forced_empty=8,
+                                       group_offset=4, num_active=14)
+    sizes, s, Ga = base.group_sizes, base.group_offset, base.num_active
+    M, K, N = base.M, 768, 328
+    lhs = torch.randint(-3, 4, (M, K), generator=g).to(torch.bfloat16)
+    packed = torch.randint(0, 256, (Ga, N, K // 2), generator=g).to(torch.uint8)
+    rs = 2.0 ** torch.randint(-3, 4, (Ga, K // 128, 1, N), generator=g).to(torch.float32)
+    bias = torch.randint(-8, 9, (Ga, 1, N), generator=g).to(torch.bfloat16)
+    want = oracle.round_to(oracle.gmm_reference(lhs, packed, sizes, rhs_format=fmt, rhs_scale=rs, rhs_bias=bias,
+                                                group_offset=s), out_dtype)
+    iv = torch.int16 if out_dtype == torch.bfloat16 else torch.int32
+    m.set_tile_policy(0)
+    for grid in (0, 5):
+        print(f"stream four-bit {fmt} out={out_dtype} grid={grid}", flush=True)
+        m.set_grid_limit(grid)
+        try:
+            out = m.gmm(lhs.cuda(), packed.cuda(), sizes.cuda(), rhs_format=fmt, out_dtype=out_dtype,
+                        rhs_scale=rs.cuda(), rhs_bias=bias.cuda(), group_offset=s)
+            torch.cuda.synchronize()
+        finally:
+            m.set_grid_limit(0)
+        assert torch.equal(out.cpu().view(iv), want.view(iv)), (fmt, out_dtype, grid)
+    assert m.device_flags() == 0
+
+
 def test_weight_streaming_kernel_mostly_inactive_rows():
     """An expert shard of a decode batch: 2 of 24 experts active, so almost
     all of the 2048 output rows lie outside the active groups and are zeroed

@@ -91,7 +91,7 @@ def test_stream_kernel_keeps_every_counted_operation(stream_asm):
     """The weight-streaming kernel's waits count 8 direct-to-LDS loads per
     stage in the code (4 weight and 2 lhs per wave, the scale load of wave 0
     and the bias load of wave 1: two stages in the prologue and one in each
-    of the K loop's four variants) and E = 4 (bf16 output) or 8 (f32) stores
+    of the K loop's four variants; four-bit weights: 2 weight loads, so 6) and E = 4 (bf16 output) or 8 (f32) stores
     per wave and tile: the prologue's E range-dropped stores and the
     epilogue of each of the three loop variants that can end a tile.  Where
     a stage is a tile's stage 0, wave 0's scale load and wave 1's bias load
@@ -100,13 +100,15 @@ def test_stream_kernel_keeps_every_counted_operation(stream_asm):
     up to two loads fewer appear in the code."""
     seen = 0
     for name, lines in _functions(stream_asm, r"_ZN4gmmk17gmm_stream_kernel"):
-        out_f32 = re.search(r"StreamCfgILb([01])E", name).group(1) == "1"
+        m = re.search(r"StreamCfgILb([01])ELi([0-9])E", name)
+        out_f32, fb = m.group(1) == "1", int(m.group(2))
+        per_stage = 6 if fb >= 3 else 8
         loads = sum(1 for ln in lines if ln.startswith("buffer_load") and ln.endswith(" lds"))
         stores = sum(1 for ln in lines if ln.startswith("buffer_store"))
-        assert 6 * 8 - 2 <= loads <= 6 * 8, (name, loads)
+        assert 6 * per_stage - 2 <= loads <= 6 * per_stage, (name, loads)
         assert stores == 4 * (8 if out_f32 else 4), (name, stores)
         seen += 1
-    assert seen == 6  # e4m3fn / e5m2 / int8 weights x bf16 / f32 output
+    assert seen == 12  # e4m3fn / e5m2 / int8 / int4 / uint4 / fp4 weights x bf16 / f32 output
 
 
 def test_loop_kernels_do_not_spill(kernel_asm, w8a8_asm, stream_asm):
@@ -118,7 +120,7 @@ def test_loop_kernels_do_not_spill(kernel_asm, w8a8_asm, stream_asm):
         for name, lines in _functions(asm, pattern):
             assert not any(ln.startswith("scratch_") for ln in lines), name
             seen += 1
-    assert seen == 2 + 6 + 8
+    assert seen == 2 + 12 + 8
 
 
 def test_w8a8_kernel_keeps_every_counted_operation(w8a8_asm):

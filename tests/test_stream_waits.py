@@ -15,7 +15,8 @@ the epilogue's E stores in a tile's last stage, and the wait before the
 next stage's fragments are read, with the kernel's constants: (S-2) stages
 of loads, plus E where the wait is WITH_E (a tile's stage 0 and its last
 stage).  It checks that every wait is exact, for waves 0-1 (one load per
-stage more: the scales, the bias) and the others, bf16 and f32 output
+stage more: the scales, the bias) and the others, with one-byte weights (6
+and 7 loads per stage) and four-bit ones (4 and 5), bf16 and f32 output
 (E = 4, 8), and tiles of 3 to 11 stages."""
 import pytest
 
@@ -55,7 +56,7 @@ def _kernel_rule(kt, KT):
 
 
 @pytest.mark.parametrize("KT", [3, 4, 5, 8, 11])
-@pytest.mark.parametrize("ops", [6, 7])
+@pytest.mark.parametrize("ops", [4, 5, 6, 7])
 @pytest.mark.parametrize("E", [4, 8])
 def test_every_stream_wait_is_exact(KT, ops, E):
     waits = _replay(KT, tiles=4, ops=ops, E=E, with_e_rule=_kernel_rule)
